@@ -1,0 +1,308 @@
+"""Throughput of the scaled low-precision GEMM path on one MI355X.
+
+One step = one pass of the path over one batch of synthetic input: quantize
+the bf16 activations on the GPU (row-wise E4M3, per-tensor E4M3 or NVFP4,
+per the workload), then one gemm_scaled launch with its fused epilogue.
+Weights are quantized once, before timing (they are pre-quantized in
+inference, as in AstrAI's "NT pre-quantized" benchmark).  Three input/weight
+buffer sets rotate from step to step so the working set exceeds the 256 MB
+last-level cache.
+
+Prints ONE JSON line: whole-step TFLOP/s (value), the GEMM kernel's roofline
+position (its launch durations measured with events on the launch stream
+inside the timed region), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synthetic import WORKLOADS  # noqa: E402
+
+METRIC = "TFLOP/s and % of dense FP8 MFMA peak, scaled GEMM at T=4096 (and T=1024)"
+DEFAULT_WORKLOAD = "fp8_row_swiglu_t4096"
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"fp8": 5000.0, "f16": 2500.0}
+HBM_GBS = 8000.0
+
+GEMM_SOURCES = {
+    "e4m3_row": ["spg_gemm_fp8.hip", "spg_gemm_common.h"],
+    "e4m3_tensor": ["spg_gemm_fp8.hip", "spg_gemm_common.h"],
+    "nvfp4": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h"],
+}
+
+
+def kernel_source_hash(fmt: str) -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES[fmt]:
+        with open(os.path.join(ROOT, "scaled_precision_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def gemm_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one GEMM launch: read A and W codes (and the
+    NVFP4 scale planes), read the residual, write the bf16 output once."""
+    b = wl.batch
+    if wl.fmt == "nvfp4":
+        ab = wl.M * wl.K // 2 + wl.M * wl.K // 16
+        wb = wl.N * wl.K // 2 + wl.N * wl.K // 16
+    else:
+        ab = wl.M * wl.K
+        wb = wl.N * wl.K
+    out = 2 * wl.M * wl.n_out
+    res = 2 * wl.M * wl.n_out if wl.epilogue == "add" else 0
+    return b * (ab + wb + out + res)
+
+
+def operator_bytes(M, N, K, n_out, residual: bool, fmt: str) -> int:
+    """Bytes of the quantize + GEMM operator as ninfer PR #160's operator
+    table counts them: bf16 activations in, weight codes and scales, bf16
+    output, bf16 residual."""
+    if fmt == "nvfp4":
+        w = N * K // 2 + N * K // 16
+    else:
+        w = N * K + 4 * N
+    return 2 * M * K + w + 2 * M * n_out + (2 * M * n_out if residual else 0)
+
+
+def traffic_from_profiles(wl, name):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    only when it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(name)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(wl.fmt):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def to_dev(x16, torch):
+    return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(wl, A16, W16, R16, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same step:
+    quantize `rows` activation rows and compute their whole output rows
+    (weights quantized beforehand, outside the timed part, as on the GPU)."""
+    import oracle
+    if wl.batch > 1:
+        A16, W16 = A16[0], W16[0]
+    if wl.fmt == "e4m3_row":
+        Wq, sw = oracle.quantize_rowwise(W16)
+    elif wl.fmt == "e4m3_tensor":
+        Wq, sw = oracle.quantize_tensor(W16)
+        sw = sw[0]
+        sa_t = oracle.amax(A16) / np.float32(448.0)
+    else:
+        tw = oracle.nvfp4_tensor_scale(W16)
+        Wq, Ws = oracle.quantize_block16_rows(W16, tw)
+        ta = oracle.nvfp4_tensor_scale(A16)
+
+    def step(rows):
+        a = np.ascontiguousarray(A16[:rows])
+        r = np.ascontiguousarray(R16[:rows]) if R16 is not None else None
+        if wl.fmt == "e4m3_row":
+            qa, sa = oracle.quantize_rowwise(a)
+            D, Da = oracle.gemm_e4m3_sums(qa, Wq)
+            oracle.epilogue(wl.epilogue, D, Da, sa, sw, r)
+        elif wl.fmt == "e4m3_tensor":
+            qa = oracle.quantize_rows_with_scale(a, sa_t)
+            D, Da = oracle.gemm_e4m3_sums(qa, Wq)
+            oracle.epilogue(wl.epilogue, D, Da, sa_t, sw, r)
+        else:
+            qa, sa = oracle.quantize_block16_rows(a, ta)
+            D, Da = oracle.gemm_nvfp4_sums(qa, sa, Wq, Ws)
+            oracle.epilogue(wl.epilogue, D, Da, ta, tw, r)
+
+    t0 = time.perf_counter()
+    step(1)
+    one = max(time.perf_counter() - t0, 1e-4)
+    rows = int(max(1, min(wl.M, budget_s / one)))
+    t0 = time.perf_counter()
+    step(rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * wl.N * wl.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{rows} of {wl.M} token rows of one product: quantize + all {wl.n_out} outputs "
+                  f"({wl.epilogue}), fp64, {dt:.1f} s",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=3, help="rotating input/weight buffer sets")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU sharding or collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import scaled_precision_gemm_amd as spg
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    A16, W16, R16 = wl.inputs()
+    sets = max(1, args.sets)
+
+    # ---- device buffers: `sets` rotated activation / weight sets ------------
+    A0, W0 = to_dev(A16, torch), to_dev(W16, torch)
+    R = to_dev(R16, torch) if R16 is not None else None
+    acts, weights = [], []
+    for s in range(sets):
+        shift = 977 * s
+        A = A0 if s == 0 else torch.roll(A0, shifts=shift, dims=-2).contiguous()
+        W = W0 if s == 0 else torch.roll(W0, shifts=shift, dims=-2).contiguous()
+        if wl.fmt == "e4m3_row":
+            wq = spg.quantize_rowwise(W)
+        elif wl.fmt == "e4m3_tensor":
+            wq = spg.quantize_tensor(W)
+        else:
+            wq = spg.quantize_block16(W)
+        acts.append(A)
+        weights.append(wq)
+        del W
+    del A0, W0
+    torch.cuda.synchronize()
+
+    # activation-side buffers, reused every step
+    if wl.fmt == "e4m3_row":
+        qa = torch.empty(wl.a_shape(), dtype=torch.uint8, device="cuda")
+        sa = torch.empty((wl.M,), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.batch, wl.M, wl.n_out) if wl.batch > 1 else (wl.M, wl.n_out),
+                      dtype=torch.bfloat16, device="cuda")
+    ws = None
+
+    def step(i):
+        nonlocal ws
+        A = acts[i % sets]
+        w = weights[i % sets]
+        if wl.fmt == "e4m3_row":
+            spg.quantize_rowwise(A, out=qa, scale=sa)
+            ev[i][1].record()
+            spg.gemm_scaled(qa, sa, w[0], w[1], wl.epilogue, residual=R, out=out, workspace=ws)
+        elif wl.fmt == "e4m3_tensor":
+            q, s = spg.quantize_tensor(A)
+            ev[i][1].record()
+            spg.gemm_scaled(q, s, w[0], w[1], wl.epilogue, fmt="e4m3_tensor", out=out, workspace=ws)
+        else:
+            q, bs, t = spg.quantize_block16(A)
+            ev[i][1].record()
+            spg.gemm_scaled(q, bs, w[0], w[1], wl.epilogue, residual=R, fmt="nvfp4", out=out,
+                            tscale_a=t, tscale_w=w[2], workspace=ws)
+
+    # workspace sized once by the library's own query, reused every step
+    plan = spg.gemm_plan(wl.M, wl.N, wl.K, wl.fmt, wl.epilogue, batch=wl.batch)
+    a_codes = qa if wl.fmt == "e4m3_row" else None
+    if a_codes is None:
+        a_codes = torch.empty(wl.a_shape() if wl.fmt != "nvfp4" else (wl.M, wl.K // 2), dtype=torch.uint8,
+                              device="cuda")
+    ws = spg.gemm_workspace(a_codes, weights[0][0], wl.fmt, wl.epilogue, out=out, residual=R)
+
+    stream = torch.cuda.current_stream()
+    n_ev = max(args.warmup, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+
+    for i in range(args.warmup):
+        ev[i][0].record()
+        step(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][2].record()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    gemm_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    quant_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+
+    ms_per_step = total_ms / args.steps
+    flops = wl.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_avg = float(np.mean(gemm_ms))
+    achieved = flops / (gemm_avg * 1e-3) / 1e12
+    peak_key = "f16" if wl.fmt == "nvfp4" else "fp8"
+    peak = PEAK_TFLOPS[peak_key]
+    roofline = {
+        "bound": "mfma",
+        "kernel": "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel",
+        "achieved": round(achieved, 1),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic_from_profiles(wl, args.workload),
+        "algorithmic_bytes": gemm_bytes(wl),
+        "flops_per_launch": flops,
+        "launch_ms_avg": round(gemm_avg, 4),
+        "launch_ms_p10_p90": [round(float(np.percentile(gemm_ms, 10)), 4),
+                              round(float(np.percentile(gemm_ms, 90)), 4)],
+    }
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.fmt == "nvfp4" else "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "format": wl.fmt, "epilogue": wl.epilogue,
+            "M": wl.M, "N": wl.N, "K": wl.K, "batch": wl.batch,
+            "step": "activation quantize + gemm_scaled (weights pre-quantized)",
+            "buffer_sets": sets, "plan": plan,
+        },
+        "pct_fp8_peak": round(100.0 * value / PEAK_TFLOPS["fp8"], 2),
+        "quantize_ms_avg": round(float(np.mean(quant_ms)), 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, A16, W16, R16, args.cpu_budget)
+        line["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * spg.h - C ABI of the scaled low-precision GEMM path for MI355X (gfx950).
+ *
+ * The path computes the linear layers of LLM prefill in two primitives, the
+ * quantizer and the GEMM, the split AstrAI's commit log calls its
+ * "two-primitive API" (quantize + mm_fp8):
+ *
+ *   1. quantize bf16 activations per token row to FP8 E4M3 (ninfer PR #167,
+ *      "The fp8 A8 GEMM stages its operands through TMA", opening summary and
+ *      "Measured": row-scaled A8, FP8_E4M3FN weights with row scales), per
+ *      matrix (AstrAI, "Benchmark: ... E4M3, NT pre-quantized"), or per 16
+ *      K-elements to NVFP4 (ninfer PR #160, "The NVFP4 TMA route reads
+ *      activation scales as one tile": E2M1 codes, E4M3 scales over
+ *      "[BlockM tokens, 16 groups]" tiles);
+ *   2. multiply by pre-quantized weights with fp32 accumulation and apply the
+ *      scales after accumulation, then one fused bf16 epilogue: plain store
+ *      (linear), residual add (linear_add) or paired SwiGLU (linear_swiglu)
+ *      (PR #167 opening summary and the maintainer review's note on "explicit
+ *      paired SwiGLU handling").  The output is always bf16 (AstrAI: "GEMM
+ *      output is always bf16").
+ *
+ * Conventions for every entry point
+ *  - All matrices are row-major.  A is [M, K] (tokens x reduction), W is
+ *    [N, K] (weight rows x reduction): both K-contiguous, C = A W^T (the "NT"
+ *    layout).
+ *  - bf16 tensors are passed as const void* to 16-bit values.
+ *  - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *    allocates nothing and keeps no mutable global state.  Work is enqueued
+ *    on `stream` (a hipStream_t; NULL = the default stream) and is
+ *    asynchronous: device faults surface at the caller's next synchronisation.
+ *  - Return value: SPG_OK, or an error code.  On any validation error nothing
+ *    is enqueued and outputs are untouched.  No C++ exception crosses the ABI.
+ *  - Alignment: code and bf16-input pointers and their row strides in bytes
+ *    must be multiples of 16 (the kernels load 16-byte vectors); bf16 GEMM
+ *    outputs and residuals need only 2-byte alignment, any row stride; fp32
+ *    scale pointers 4 bytes.  K must be a multiple of 16 (FP8) or 32 (NVFP4).
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef SPG_H
+#define SPG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+    SPG_OK = 0,
+    SPG_EINVAL = 1,        /* bad argument (null, enum, shape, alignment)   */
+    SPG_EUNSUPPORTED = 2,  /* valid request outside what this build runs    */
+    SPG_EWORKSPACE = 3,    /* workspace null or smaller than required       */
+    SPG_EHIP = 4           /* a HIP call or kernel launch reported an error */
+};
+
+/* ---- operand formats (AstrAI: "validate the fmt enum") ----------------- */
+enum {
+    SPG_FMT_E4M3_ROW = 0,    /* E4M3 codes; fp32 scale per row of A and of W  */
+    SPG_FMT_E4M3_TENSOR = 1, /* E4M3 codes; one fp32 scale per matrix         */
+    SPG_FMT_NVFP4 = 2        /* E2M1 codes 2/byte + E4M3 scale per 16 + fp32  */
+};
+
+/* ---- fused epilogues (ninfer: linear, linear_add, linear_swiglu) -------- */
+enum {
+    SPG_EPI_STORE = 0,   /* out = bf16(v)                                    */
+    SPG_EPI_ADD = 1,     /* out = bf16(v + residual)                         */
+    SPG_EPI_SWIGLU = 2   /* out[:, j] = bf16(silu(v[:, j]) * v[:, j + N/2])  */
+};
+
+const char *spg_status_string(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Quantizers                                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * quantize_rowwise - FP8 E4M3 with one fp32 scale per row (PR #167's
+ * row-scaled A8 activations and its row-scaled E4M3FN weights).
+ *   For each row r: s_r = fl32(max_k |x_rk| / 448);
+ *   q_rk = E4M3 nearest-even of fl32(x_rk / s_r), saturating at +-448, sign of
+ *   zero kept; s_r = 0 gives signed-zero codes.
+ *   x     : bf16 [rows, K], row stride ldx elements
+ *   q     : uint8 codes [rows, K], row stride ldq bytes
+ *   scale : fp32 [rows]
+ *   K % 16 == 0, ldx >= K, ldq >= K, ldx % 8 == 0, ldq % 16 == 0.
+ *   rows == 0 is a no-op; rows > 0 with K == 0 is invalid (no scale exists).
+ */
+int quantize_rowwise(const void *x, int64_t rows, int64_t K, int64_t ldx,
+                     uint8_t *q, int64_t ldq, float *scale, void *stream);
+
+/*
+ * quantize_tensor - FP8 E4M3 with one fp32 scale per matrix (AstrAI's
+ * per-tensor NT benchmark; a batch of matrices gets one scale each).
+ *   x     : bf16, `batch` matrices [rows, K] (row stride K) at x + b*bstride
+ *   q     : uint8 codes, matrix b at q + b*rows*K
+ *   scale : fp32 [batch], s_b = fl32(amax_b / 448)
+ *   ws    : device workspace of at least quantize_tensor_workspace_bytes()
+ *   K % 16 == 0, bstride % 8 == 0, bstride >= rows*K.
+ */
+size_t quantize_tensor_workspace_bytes(int64_t batch, int64_t rows, int64_t K);
+int quantize_tensor(const void *x, int64_t batch, int64_t rows, int64_t K, int64_t bstride,
+                    uint8_t *q, float *scale, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * quantize_block16 - NVFP4 (PR #160): E2M1 codes, one E4M3 scale per 16
+ * consecutive K-elements of a row, one fp32 scale for the tensor.
+ *   t     = fl32(amax / 2688)                      (2688 = 448 * 6)
+ *   b_g   = E4M3 nearest-even of fl32(amax_g / fl32(6 t)), saturating
+ *   e_g   = fl32(dec(b_g) * t)
+ *   code  = E2M1 nearest-even of fl32(x / e_g), saturating at +-6; e_g == 0
+ *           gives signed zeros
+ *   x      : bf16 [rows, K], row stride K
+ *   q      : uint8 [rows, K/2]; element k in the low nibble when k is even
+ *   bscale : uint8 E4M3 codes [rows, K/16], row-major
+ *   tscale : fp32 [1], device
+ *   ws     : device workspace of at least quantize_block16_workspace_bytes()
+ *   K % 32 == 0.
+ */
+size_t quantize_block16_workspace_bytes(int64_t rows, int64_t K);
+int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale,
+                     float *tscale, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* GEMM                                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Shape and layout of one gemm_scaled call.  Initialise with
+ * spg_gemm_desc_init() so unused fields are zero and optional pointers NULL
+ * (AstrAI: default-initialised parameter structs never carry garbage).
+ *   M, N, K  : A [M, K], W [N, K]; out [M, N], or [M, N/2] for SWIGLU
+ *   batch    : number of independent products (>= 1)
+ *   lda, ldw : row strides of A and W in bytes of codes (NVFP4: bytes of
+ *              packed codes, >= K/2)
+ *   ldo, ldr : row strides of out and residual in bf16 elements
+ *   stride_* : batch strides (bytes for A/W codes, elements for out and
+ *              residual); 0 broadcasts one matrix to every batch entry
+ *              (AstrAI: "size-1 batches broadcast (stride 0)")
+ *   format   : SPG_FMT_*
+ *   tscale_a, tscale_w : NVFP4 only, device fp32 [1] tensor scales
+ */
+typedef struct spg_gemm_desc {
+    int64_t M, N, K, batch;
+    int64_t lda, ldw, ldo, ldr;
+    int64_t stride_a, stride_w, stride_o, stride_r;
+    int32_t format;
+    int32_t reserved;
+    const float *tscale_a;
+    const float *tscale_w;
+} spg_gemm_desc;
+
+/* Zero every field, set batch = 1 and the dense strides for M, N, K. */
+void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32_t format);
+
+/*
+ * gemm_scaled - out = epilogue(scale * (A W^T)), fp32 accumulation.
+ *   out      : bf16 [M, N] (STORE, ADD) or [M, N/2] (SWIGLU)
+ *   A, W     : codes as described by d->format
+ *   sa, sw   : E4M3_ROW: fp32 [M] and fp32 [N] (per batch entry: + b*M, b*N
+ *              unless that operand's batch stride is 0);
+ *              E4M3_TENSOR: fp32 [batch] each (index 0 when broadcast);
+ *              NVFP4: E4M3 block-scale planes [M, K/16] and [N, K/16],
+ *              row-major (NVFP4 requires batch == 1)
+ *   residual : bf16 [M, N], required for SPG_EPI_ADD, NULL otherwise; it may
+ *              be the same buffer as out when ldr == ldo and strides match
+ *   epilogue : SPG_EPI_*; SWIGLU pairs W rows j (gate) and j + N/2 (up) and
+ *              needs N even
+ *   ws       : device workspace of at least gemm_scaled_workspace_bytes(d, epilogue)
+ *              (may be NULL when that is 0)
+ * Results: each element within 2^-8 |y| + 2^-12 S of the exact value y,
+ * where S is the scaled sum of |products| (fp32 accumulation order is free).
+ */
+size_t gemm_scaled_workspace_bytes(const spg_gemm_desc *d, int epilogue);
+int gemm_scaled(void *out, const void *A, const void *sa, const void *W, const void *sw,
+                const void *residual, int epilogue, const spg_gemm_desc *d,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Tile / route selection (host only, no device access)                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The route model of PR #167 ("Routing"): compare quantised costs, "waves
+ * needed times the work one SM carries through a wave", one empirical factor
+ * per route.  A candidate is a tile of bm x bn outputs of which per_unit run
+ * concurrently on one compute unit, with a cost factor; its cost for an
+ * M x N output over `batch` products is
+ *     factor * ceil(tiles / (units * per_unit)) * per_unit * bm * bn,
+ * tiles = batch * ceil(M/bm) * ceil(N/bn).  spg_route_select returns the
+ * index of the cheapest candidate (the first on ties).
+ */
+typedef struct spg_route_candidate {
+    int32_t bm, bn, per_unit;
+    double factor;
+} spg_route_candidate;
+
+double spg_route_cost(const spg_route_candidate *c, int64_t M, int64_t N, int64_t batch, int32_t units);
+int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t N, int64_t batch,
+                     int32_t units);
+
+/*
+ * The plan gemm_scaled would launch for `d` on a device with `units` compute
+ * units: tile shape, K-split and the number of workgroups.  Returns SPG_OK or
+ * the validation error gemm_scaled would return.
+ */
+typedef struct spg_plan {
+    int32_t bm, bn, bk;      /* workgroup tile (output rows, weight rows, K)  */
+    int32_t split_k;         /* K partitions reduced through the workspace    */
+    int64_t tiles;           /* output tiles over the whole batch             */
+    int64_t workgroups;      /* tiles * split_k                               */
+    int32_t kernel;          /* internal kernel id                            */
+} spg_plan;
+
+int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units, spg_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPG_H */

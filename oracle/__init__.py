@@ -43,6 +43,7 @@ def _load():
     c_i64, c_f, c_d, c_u32, c_p = (ctypes.c_int64, ctypes.c_float, ctypes.c_double,
                                    ctypes.c_uint32, ctypes.c_void_p)
     sig = {
+        "spo_threads": (ctypes.c_int, []),
         "spo_bf16_to_f32": (c_f, [ctypes.c_uint16]),
         "spo_bf16_from_f64": (ctypes.c_uint16, [c_d]),
         "spo_e4m3_value": (c_d, [c_u32]),
@@ -69,6 +70,11 @@ def _load():
 
 
 _lib = _load()
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_lib.spo_threads())
 
 
 def _p(a: np.ndarray):

@@ -42,10 +42,14 @@
  * integer dot products, power-of-two cases and naive triple loops.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
 #define EXPORT __attribute__((visibility("default")))
+
+/* Threads an OpenMP region of this library uses. */
+EXPORT int spo_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------- */
 /* bf16 and fp32 bit helpers                                                 */

@@ -1,0 +1,260 @@
+"""Python binding of the gfx950 scaled low-precision GEMM library.
+
+Argument marshalling only: each function checks dtypes and shapes, allocates
+outputs with torch on the input's device (torch is the memory and stream
+provider), and calls the C ABI of ``libspg.so`` (declared in
+``include/spg.h``) on torch's current stream.  Every step of the path runs in
+the library's HIP kernels; there is no fallback.  Importing this package
+fails loudly when the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "quantize_rowwise", "quantize_tensor", "quantize_block16", "gemm_scaled",
+    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "lib", "LIB_PATH",
+    "FMT_E4M3_ROW", "FMT_E4M3_TENSOR", "FMT_NVFP4", "EPI_STORE", "EPI_ADD", "EPI_SWIGLU",
+    "SpgError",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspg.so")
+
+FMT_E4M3_ROW, FMT_E4M3_TENSOR, FMT_NVFP4 = 0, 1, 2
+EPI_STORE, EPI_ADD, EPI_SWIGLU = 0, 1, 2
+_EPI = {"store": EPI_STORE, "add": EPI_ADD, "swiglu": EPI_SWIGLU}
+_FMT = {"e4m3_row": FMT_E4M3_ROW, "e4m3_tensor": FMT_E4M3_TENSOR, "nvfp4": FMT_NVFP4}
+
+
+class SpgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {lib.spg_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+class GemmDesc(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("batch", ctypes.c_int64),
+        ("lda", ctypes.c_int64), ("ldw", ctypes.c_int64), ("ldo", ctypes.c_int64), ("ldr", ctypes.c_int64),
+        ("stride_a", ctypes.c_int64), ("stride_w", ctypes.c_int64),
+        ("stride_o", ctypes.c_int64), ("stride_r", ctypes.c_int64),
+        ("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("tscale_a", ctypes.c_void_p), ("tscale_w", ctypes.c_void_p),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32), ("split_k", ctypes.c_int32),
+        ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("kernel", ctypes.c_int32),
+    ]
+
+
+class RouteCandidate(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("per_unit", ctypes.c_int32),
+                ("factor", ctypes.c_double)]
+
+
+# Exported symbols and their signatures (mirrors include/spg.h).
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SIGNATURES = {
+    "spg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "quantize_rowwise": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
+    "quantize_tensor_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "quantize_tensor": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "quantize_block16_workspace_bytes": (_SZ, [_I64, _I64]),
+    "quantize_block16": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "spg_gemm_desc_init": (None, [ctypes.POINTER(GemmDesc), _I64, _I64, _I64, _I32]),
+    "gemm_scaled_workspace_bytes": (_SZ, [ctypes.POINTER(GemmDesc), ctypes.c_int]),
+    "gemm_scaled": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(GemmDesc), _P, _SZ, _P]),
+    "spg_route_cost": (ctypes.c_double, [ctypes.POINTER(RouteCandidate), _I64, _I64, _I64, _I32]),
+    "spg_route_select": (ctypes.c_int, [ctypes.POINTER(RouteCandidate), _I32, _I64, _I64, _I64, _I32]),
+    "spg_gemm_plan": (ctypes.c_int, [ctypes.POINTER(GemmDesc), ctypes.c_int, _I32, ctypes.POINTER(Plan)]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run scaled_precision_gemm_amd/build.py (hipcc, gfx950)")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise SpgError(status, what)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+# ---------------------------------------------------------------------------
+# quantizers
+# ---------------------------------------------------------------------------
+
+def quantize_rowwise(x: torch.Tensor, out: torch.Tensor | None = None, scale: torch.Tensor | None = None):
+    """Per-row E4M3: x bf16 [R, K] -> (codes uint8 [R, K], scales fp32 [R])."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_cuda, "x must be a 2-D bf16 CUDA tensor")
+    _need(x.stride(1) == 1, "x rows must be contiguous")
+    R, K = x.shape
+    q = out if out is not None else torch.empty((R, K), dtype=torch.uint8, device=x.device)
+    s = scale if scale is not None else torch.empty((R,), dtype=torch.float32, device=x.device)
+    _check(lib.quantize_rowwise(_ptr(x), R, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), _stream(x)),
+           "quantize_rowwise")
+    return q, s
+
+
+def quantize_tensor(x: torch.Tensor):
+    """Per-matrix E4M3: x bf16 [R, K] or [B, R, K] -> (codes, scales fp32 [B])."""
+    _need(x.dtype == torch.bfloat16 and x.dim() in (2, 3) and x.is_cuda and x.is_contiguous(),
+          "x must be a contiguous 2-D or 3-D bf16 CUDA tensor")
+    xb = x.unsqueeze(0) if x.dim() == 2 else x
+    B, R, K = xb.shape
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty((B,), dtype=torch.float32, device=x.device)
+    nws = lib.quantize_tensor_workspace_bytes(B, R, K)
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device)
+    _check(lib.quantize_tensor(_ptr(xb), B, R, K, R * K, _ptr(q), _ptr(s), _ptr(ws), ws.numel(), _stream(x)),
+           "quantize_tensor")
+    return q, s
+
+
+def quantize_block16(x: torch.Tensor):
+    """NVFP4: x bf16 [R, K] -> (codes uint8 [R, K/2], block scales uint8
+    [R, K/16] (E4M3), tensor scale fp32 [1])."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_cuda and x.is_contiguous(),
+          "x must be a contiguous 2-D bf16 CUDA tensor")
+    R, K = x.shape
+    q = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    bs = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
+    t = torch.empty((1,), dtype=torch.float32, device=x.device)
+    nws = lib.quantize_block16_workspace_bytes(R, K)
+    ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device)
+    _check(lib.quantize_block16(_ptr(x), R, K, _ptr(q), _ptr(bs), _ptr(t), _ptr(ws), ws.numel(), _stream(x)),
+           "quantize_block16")
+    return q, bs, t
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def _desc(fmt: int, M: int, N: int, K: int) -> GemmDesc:
+    d = GemmDesc()
+    lib.spg_gemm_desc_init(ctypes.byref(d), M, N, K, fmt)
+    return d
+
+
+def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residual=None,
+              tscale_a=None, tscale_w=None) -> tuple[GemmDesc, int, int]:
+    fmt = _FMT.get(fmt, fmt)
+    epi = _EPI.get(epilogue, epilogue)
+    _need(A.dtype == torch.uint8 and W.dtype == torch.uint8, "A and W must be uint8 code tensors")
+    batched = A.dim() == 3 or W.dim() == 3
+    A3 = A if A.dim() == 3 else A.unsqueeze(0)
+    W3 = W if W.dim() == 3 else W.unsqueeze(0)
+    _need(A3.stride(2) == 1 and W3.stride(2) == 1, "rows must be contiguous")
+    batch = max(A3.shape[0], W3.shape[0])
+    _need(A3.shape[0] in (1, batch) and W3.shape[0] in (1, batch), "batch sizes must match or be 1")
+    M, Kc = A3.shape[1:]
+    N = W3.shape[1]
+    K = 2 * Kc if fmt == FMT_NVFP4 else Kc
+    _need(W3.shape[2] == Kc, "A and W disagree on K")
+    d = _desc(fmt, M, N, K)
+    d.batch = batch
+    d.lda, d.ldw = A3.stride(1), W3.stride(1)
+    d.stride_a = A3.stride(0) if A3.shape[0] > 1 else 0
+    d.stride_w = W3.stride(0) if W3.shape[0] > 1 else 0
+    n_out = N // 2 if epi == EPI_SWIGLU else N
+    if out is not None:
+        o3 = out if out.dim() == 3 else out.unsqueeze(0)
+        d.ldo = o3.stride(1)
+        d.stride_o = o3.stride(0) if batch > 1 else 0
+    else:
+        d.ldo = n_out
+        d.stride_o = M * n_out if batch > 1 else 0
+    if residual is not None:
+        r3 = residual if residual.dim() == 3 else residual.unsqueeze(0)
+        d.ldr = r3.stride(1)
+        d.stride_r = r3.stride(0) if r3.shape[0] > 1 else 0
+    if fmt == FMT_NVFP4:
+        d.tscale_a = tscale_a.data_ptr() if tscale_a is not None else None
+        d.tscale_w = tscale_w.data_ptr() if tscale_w is not None else None
+    return d, epi, batched
+
+
+def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
+                out=None, tscale_a=None, tscale_w=None, workspace=None):
+    """out = epilogue(scale * A W^T) in bf16.
+
+    e4m3_row: A uint8 [M,K], sa fp32 [M]; W uint8 [N,K], sw fp32 [N]
+    e4m3_tensor: A [B,M,K] or [M,K], sa fp32 [B]; W likewise, sw fp32 [B]
+    nvfp4: A uint8 [M,K/2], sa uint8 [M,K/16]; W [N,K/2], sw [N,K/16];
+           tscale_a, tscale_w fp32 [1]
+    """
+    d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w)
+    n_out = d.N // 2 if epi == EPI_SWIGLU else d.N
+    if out is None:
+        shape = (d.batch, d.M, n_out) if batched else (d.M, n_out)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=A.device)
+    _need(out.dtype == torch.bfloat16, "out must be bf16")
+    if residual is not None:
+        _need(residual.dtype == torch.bfloat16, "residual must be bf16")
+    nws = lib.gemm_scaled_workspace_bytes(ctypes.byref(d), epi)
+    if nws > 0 and (workspace is None or workspace.numel() < nws):
+        workspace = torch.empty((nws,), dtype=torch.uint8, device=A.device)
+    _check(lib.gemm_scaled(_ptr(out), _ptr(A), _ptr(sa), _ptr(W), _ptr(sw), _ptr(residual), epi,
+                           ctypes.byref(d), _ptr(workspace) if nws > 0 else None,
+                           workspace.numel() if (workspace is not None and nws > 0) else 0, _stream(A)),
+           "gemm_scaled")
+    return out
+
+
+def gemm_workspace(A, W, fmt="e4m3_row", epilogue="store", out=None, residual=None):
+    """A device workspace large enough for gemm_scaled on these operands, or
+    None when the plan needs none."""
+    d, epi, _ = make_desc(A, W, fmt, epilogue, out, residual)
+    nws = lib.gemm_scaled_workspace_bytes(ctypes.byref(d), epi)
+    return torch.empty((nws,), dtype=torch.uint8, device=A.device) if nws > 0 else None
+
+
+def gemm_plan(M, N, K, fmt="e4m3_row", epilogue="store", batch=1, units=256) -> dict:
+    fmt = _FMT.get(fmt, fmt)
+    epi = _EPI.get(epilogue, epilogue)
+    d = _desc(fmt, M, N, K)
+    d.batch = batch
+    if batch > 1:
+        d.stride_a, d.stride_w = M * d.lda, N * d.ldw
+    p = Plan()
+    _check(lib.spg_gemm_plan(ctypes.byref(d), epi, units, ctypes.byref(p)), "spg_gemm_plan")
+    return {f: getattr(p, f) for f, _ in Plan._fields_}
+
+
+def route_cost(bm, bn, per_unit, factor, M, N, batch, units) -> float:
+    c = RouteCandidate(bm, bn, per_unit, factor)
+    return lib.spg_route_cost(ctypes.byref(c), M, N, batch, units)
+
+
+def route_select(cands, M, N, batch, units) -> int:
+    arr = (RouteCandidate * len(cands))(*[RouteCandidate(*c) for c in cands])
+    return lib.spg_route_select(arr, len(cands), M, N, batch, units)

@@ -1,0 +1,298 @@
+// Exported C ABI (include/spg.h): argument validation, the tile / split-K
+// selector and kernel launches.  No allocation, no global mutable state.
+#include <math.h>
+#include <string.h>
+
+#include "spg_common.h"
+
+using namespace spg;
+
+namespace {
+
+constexpr int64_t kTile = 256;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+bool aligned2(const void *p) { return ((uintptr_t)p & 1u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int device_units()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+int64_t n_out_of(const spg_gemm_desc *d, int epi) { return epi == SPG_EPI_SWIGLU ? d->N / 2 : d->N; }
+
+// Checks that do not need the data pointers.
+int validate_desc(const spg_gemm_desc *d, int epi)
+{
+    if (!d) return SPG_EINVAL;
+    if (d->format != SPG_FMT_E4M3_ROW && d->format != SPG_FMT_E4M3_TENSOR && d->format != SPG_FMT_NVFP4)
+        return SPG_EINVAL;
+    if (epi != SPG_EPI_STORE && epi != SPG_EPI_ADD && epi != SPG_EPI_SWIGLU) return SPG_EINVAL;
+    if (d->M < 0 || d->N < 0 || d->K < 0 || d->batch < 1) return SPG_EINVAL;
+    if (d->stride_a < 0 || d->stride_w < 0 || d->stride_o < 0 || d->stride_r < 0) return SPG_EINVAL;
+    if (epi == SPG_EPI_SWIGLU && (d->N & 1)) return SPG_EINVAL;
+    const int64_t nout = n_out_of(d, epi);
+    if (d->format == SPG_FMT_NVFP4) {
+        if (d->K % 32) return SPG_EINVAL;
+        if (d->lda < d->K / 2 || d->ldw < d->K / 2) return SPG_EINVAL;
+        if (d->batch != 1) return SPG_EUNSUPPORTED;
+    } else {
+        if (d->K % 16) return SPG_EINVAL;
+        if (d->lda < d->K || d->ldw < d->K) return SPG_EINVAL;
+    }
+    if ((d->lda & 15) || (d->ldw & 15)) return SPG_EINVAL;
+    if ((d->stride_a & 15) || (d->stride_w & 15)) return SPG_EINVAL;
+    if (d->ldo < nout) return SPG_EINVAL;
+    if (epi == SPG_EPI_ADD && d->ldr < nout) return SPG_EINVAL;
+    return SPG_OK;
+}
+
+// The split-K factor: only when the output tiles fill less than half of
+// the compute units, pick the split s <= 8 (K / s >= 1024) that minimises
+// waves(tiles * s) / s, i.e. the wave-quantised time of the K-split work.
+int choose_split(int64_t tiles, int64_t K, int units, int bk)
+{
+    if (tiles * 2 > units) return 1;
+    int best = 1;
+    double best_cost = 1.0;
+    for (int s = 2; s <= 8; ++s) {
+        if (K / s < 1024) break;
+        const double waves = (double)cdiv(tiles * s, units);
+        const double cost = waves / s;
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = s;
+        }
+    }
+    (void)bk;
+    return best;
+}
+
+void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
+{
+    memset(p, 0, sizeof(*p));
+    const int64_t nout = n_out_of(d, epi);
+    p->bm = (int32_t)kTile;
+    p->bn = (int32_t)kTile;   // weight rows per tile (SWIGLU: 128 gate + 128 up)
+    p->bk = d->format == SPG_FMT_NVFP4 ? 64 : 128;
+    const int64_t tiles_m = cdiv(d->M, kTile);
+    const int64_t tiles_n = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
+    p->tiles = tiles_m * tiles_n * d->batch;
+    p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->K, units, p->bk) : 1;
+    p->workgroups = p->tiles * p->split_k;
+    p->kernel = d->format == SPG_FMT_NVFP4 ? 1 : 0;
+}
+
+size_t plan_workspace(const spg_plan *p)
+{
+    if (p->split_k <= 1) return 0;
+    const size_t partial = (size_t)p->tiles * p->split_k * kTile * kTile * sizeof(float);
+    const size_t counters = (((size_t)p->tiles * sizeof(uint32_t)) + 255) & ~(size_t)255;
+    return partial + counters;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+
+SPG_EXPORT const char *spg_status_string(int status)
+{
+    switch (status) {
+    case SPG_OK: return "success";
+    case SPG_EINVAL: return "invalid argument";
+    case SPG_EUNSUPPORTED: return "unsupported request";
+    case SPG_EWORKSPACE: return "workspace missing or too small";
+    case SPG_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+SPG_EXPORT void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32_t format)
+{
+    if (!d) return;
+    memset(d, 0, sizeof(*d));
+    d->M = M;
+    d->N = N;
+    d->K = K;
+    d->batch = 1;
+    d->format = format;
+    d->lda = d->ldw = format == SPG_FMT_NVFP4 ? K / 2 : K;
+    d->ldo = N;
+    d->ldr = N;
+}
+
+SPG_EXPORT double spg_route_cost(const spg_route_candidate *c, int64_t M, int64_t N, int64_t batch, int32_t units)
+{
+    if (!c || c->bm <= 0 || c->bn <= 0 || c->per_unit <= 0 || units <= 0) return INFINITY;
+    const int64_t tiles = batch * cdiv(M, c->bm) * cdiv(N, c->bn);
+    const int64_t slots = (int64_t)units * c->per_unit;
+    const int64_t waves = cdiv(tiles, slots);
+    return c->factor * (double)waves * (double)c->per_unit * (double)c->bm * (double)c->bn;
+}
+
+SPG_EXPORT int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t N, int64_t batch,
+                                int32_t units)
+{
+    if (!c || n <= 0) return -1;
+    int best = 0;
+    double best_cost = spg_route_cost(&c[0], M, N, batch, units);
+    for (int i = 1; i < n; ++i) {
+        const double cost = spg_route_cost(&c[i], M, N, batch, units);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = i;
+        }
+    }
+    return best;
+}
+
+SPG_EXPORT int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units, spg_plan *plan)
+{
+    if (!plan) return SPG_EINVAL;
+    const int v = validate_desc(d, epilogue);
+    if (v != SPG_OK) return v;
+    make_plan(d, epilogue, units > 0 ? units : 256, plan);
+    return SPG_OK;
+}
+
+SPG_EXPORT size_t gemm_scaled_workspace_bytes(const spg_gemm_desc *d, int epilogue)
+{
+    if (validate_desc(d, epilogue) != SPG_OK) return 0;
+    spg_plan p;
+    make_plan(d, epilogue, device_units(), &p);
+    return plan_workspace(&p);
+}
+
+SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void *W, const void *sw,
+                           const void *residual, int epilogue, const spg_gemm_desc *d, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    int v = validate_desc(d, epilogue);
+    if (v != SPG_OK) return v;
+    const int64_t nout = n_out_of(d, epilogue);
+    if (d->M == 0 || nout == 0) return SPG_OK;
+    if (!out || !A || !W || !sa || !sw) return SPG_EINVAL;
+    if (!aligned2(out) || !aligned16(A) || !aligned16(W)) return SPG_EINVAL;
+    if (epilogue == SPG_EPI_ADD) {
+        if (!residual || !aligned2(residual)) return SPG_EINVAL;
+    } else if (residual) {
+        return SPG_EINVAL;
+    }
+    if (d->format == SPG_FMT_NVFP4) {
+        if (!d->tscale_a || !d->tscale_w || !aligned4(d->tscale_a) || !aligned4(d->tscale_w)) return SPG_EINVAL;
+    } else if (!aligned4(sa) || !aligned4(sw)) {
+        return SPG_EINVAL;
+    }
+
+    spg_plan p;
+    make_plan(d, epilogue, device_units(), &p);
+    const size_t need = plan_workspace(&p);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return SPG_EWORKSPACE;
+
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.out = out;
+    g.A = (const uint8_t *)A;
+    g.W = (const uint8_t *)W;
+    g.sa = sa;
+    g.sw = sw;
+    g.residual = (const uint16_t *)residual;
+    g.M = d->M;
+    g.N = d->N;
+    g.K = d->K;
+    g.batch = d->batch;
+    g.lda = d->lda;
+    g.ldw = d->ldw;
+    g.ldo = d->ldo;
+    g.ldr = d->ldr;
+    g.stride_a = d->stride_a;
+    g.stride_w = d->stride_w;
+    g.stride_o = d->stride_o;
+    g.stride_r = d->stride_r;
+    g.sa_bstride = d->M;
+    g.sw_bstride = d->N;
+    g.format = d->format;
+    g.epilogue = epilogue;
+    g.tscale_a = d->tscale_a;
+    g.tscale_w = d->tscale_w;
+    g.split_k = p.split_k;
+    const int64_t unit_k = p.bk;
+    g.k_chunk = p.split_k > 1 ? cdiv(cdiv(d->K, p.split_k), unit_k) * unit_k : (d->K > 0 ? d->K : 1);
+    g.tiles_m = cdiv(d->M, kTile);
+    g.tiles_n = epilogue == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
+    if (p.split_k > 1) {
+        g.partials = (float *)ws;
+        const size_t partial = (size_t)p.tiles * p.split_k * kTile * kTile * sizeof(float);
+        g.counters = (uint32_t *)((char *)ws + partial);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = d->format == SPG_FMT_NVFP4 ? launch_gemm_nvfp4(g, p, s) : launch_gemm_fp8(g, p, s);
+    return e == hipSuccess ? SPG_OK : SPG_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// quantizers
+// ---------------------------------------------------------------------------
+
+SPG_EXPORT int quantize_rowwise(const void *x, int64_t rows, int64_t K, int64_t ldx, uint8_t *q, int64_t ldq,
+                                float *scale, void *stream)
+{
+    if (rows < 0 || K < 0 || (K % 16)) return SPG_EINVAL;
+    if (rows == 0 || K == 0) {
+        if (rows > 0 && K == 0) return SPG_EINVAL;   // a scale of an empty row is undefined
+        return SPG_OK;
+    }
+    if (!x || !q || !scale) return SPG_EINVAL;
+    if (ldx < K || ldq < K || (ldx & 7) || (ldq & 15)) return SPG_EINVAL;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(scale)) return SPG_EINVAL;
+    hipError_t e = launch_quantize_rowwise((const uint16_t *)x, rows, K, ldx, q, ldq, scale, (hipStream_t)stream);
+    return e == hipSuccess ? SPG_OK : SPG_EHIP;
+}
+
+SPG_EXPORT size_t quantize_tensor_workspace_bytes(int64_t batch, int64_t rows, int64_t K)
+{
+    if (batch < 1 || rows < 0 || K < 0) return 0;
+    return (size_t)batch * (size_t)amax_parts(rows * K) * sizeof(uint32_t);
+}
+
+SPG_EXPORT int quantize_tensor(const void *x, int64_t batch, int64_t rows, int64_t K, int64_t bstride, uint8_t *q,
+                               float *scale, void *ws, size_t ws_bytes, void *stream)
+{
+    if (batch < 1 || rows < 0 || K < 0 || (K % 16)) return SPG_EINVAL;
+    if (rows == 0 || K == 0) return SPG_EINVAL;
+    if (!x || !q || !scale) return SPG_EINVAL;
+    if (bstride < rows * K || (bstride & 7)) return SPG_EINVAL;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(scale)) return SPG_EINVAL;
+    const size_t need = quantize_tensor_workspace_bytes(batch, rows, K);
+    if (!ws || ws_bytes < need || !aligned4(ws)) return SPG_EWORKSPACE;
+    hipError_t e = launch_quantize_tensor((const uint16_t *)x, batch, rows, K, bstride, q, scale, (uint32_t *)ws,
+                                          amax_parts(rows * K), (hipStream_t)stream);
+    return e == hipSuccess ? SPG_OK : SPG_EHIP;
+}
+
+SPG_EXPORT size_t quantize_block16_workspace_bytes(int64_t rows, int64_t K)
+{
+    if (rows < 0 || K < 0) return 0;
+    return (size_t)amax_parts(rows * K) * sizeof(uint32_t);
+}
+
+SPG_EXPORT int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale, float *tscale,
+                                void *ws, size_t ws_bytes, void *stream)
+{
+    if (rows < 0 || K < 0 || (K % 32)) return SPG_EINVAL;
+    if (rows == 0 || K == 0) return SPG_EINVAL;
+    if (!x || !q || !bscale || !tscale) return SPG_EINVAL;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(tscale)) return SPG_EINVAL;
+    const size_t need = quantize_block16_workspace_bytes(rows, K);
+    if (!ws || ws_bytes < need || !aligned4(ws)) return SPG_EWORKSPACE;
+    hipError_t e = launch_quantize_block16((const uint16_t *)x, rows, K, q, bscale, tscale, (uint32_t *)ws,
+                                           amax_parts(rows * K), (hipStream_t)stream);
+    return e == hipSuccess ? SPG_OK : SPG_EHIP;
+}

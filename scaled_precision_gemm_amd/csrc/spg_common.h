@@ -1,0 +1,134 @@
+// Internal declarations and device helpers of the gfx950 library.
+// Not part of the public ABI (include/spg.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spg.h"
+
+#define SPG_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace spg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Number formats
+// ---------------------------------------------------------------------------
+
+// binary32 -> E4M3FN code: round to nearest even, saturate at +-448, keep
+// the sign of zero.  Integer rounding on the binary32 bit pattern: the three
+// kept mantissa bits are rounded with the usual (half - 1 + lsb) increment;
+// below the smallest normal (2^-6) the value is a multiple of 2^-9 and
+// rint(|v| * 2^9) (exact scaling, round-half-even) gives the code directly.
+__device__ __forceinline__ uint32_t encode_e4m3(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {                 // |v| >= 448
+        code = 0x7Eu;
+    } else if (a < 0x3C800000u) {           // |v| < 2^-6
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    } else {
+        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (r >> 20) - ((127u - 7u) << 3);
+    }
+    return sign | code;
+}
+
+// binary32 -> E2M1 code (4 bits): nearest even, saturate at +-6, sign kept.
+__device__ __forceinline__ uint32_t encode_e2m1(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 28) & 0x8u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x40C00000u) {                 // |v| >= 6
+        code = 7u;
+    } else if (a < 0x3F800000u) {           // |v| < 1: multiples of 1/2
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
+    } else {
+        uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+        code = (r >> 22) - ((127u - 1u) << 1);
+    }
+    return sign | code;
+}
+
+// E4M3FN code -> binary32 (exact).  Codes 0x7F/0xFF (NaN) are never produced
+// by the quantizers and are not decoded specially.
+__device__ __forceinline__ float decode_e4m3(uint32_t c)
+{
+    uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// binary32 -> bf16 bits, round to nearest even (finite inputs; NaN kept NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront (64 lanes) reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers shared between translation units
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+    void *out;
+    const uint8_t *A;
+    const uint8_t *W;
+    const void *sa;
+    const void *sw;
+    const uint16_t *residual;
+    int64_t M, N, K, batch;
+    int64_t lda, ldw, ldo, ldr;
+    int64_t stride_a, stride_w, stride_o, stride_r;
+    int64_t sa_bstride, sw_bstride;   // batch stride of the scale arrays (elements)
+    int32_t format, epilogue;
+    const float *tscale_a, *tscale_w;
+    float *partials;                  // split-K fp32 partial tiles (workspace)
+    uint32_t *counters;               // split-K arrival counters (workspace)
+    int32_t split_k;
+    int64_t k_chunk;                  // K per split (multiple of the tile K)
+    int64_t tiles_m, tiles_n;         // output tiles per product
+};
+
+hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s);
+hipError_t launch_gemm_nvfp4(const GemmArgs &g, const spg_plan &p, hipStream_t s);
+hipError_t launch_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t K, int64_t ldx,
+                                   uint8_t *q, int64_t ldq, float *scale, hipStream_t s);
+hipError_t launch_quantize_tensor(const uint16_t *x, int64_t batch, int64_t rows, int64_t K,
+                                  int64_t bstride, uint8_t *q, float *scale, uint32_t *ws,
+                                  int64_t parts, hipStream_t s);
+hipError_t launch_quantize_block16(const uint16_t *x, int64_t rows, int64_t K, uint8_t *q,
+                                   uint8_t *bscale, float *tscale, uint32_t *ws, int64_t parts,
+                                   hipStream_t s);
+
+// Partial-maximum blocks used by the per-tensor amax pass.
+int64_t amax_parts(int64_t elems);
+
+}  // namespace spg

@@ -1,0 +1,284 @@
+// Quantizer kernels for gfx950: per-row and per-tensor FP8 E4M3, and the
+// NVFP4 block-16 format.
+//
+// Row-scaled FP8 follows ninfer PR #167 ("The fp8 A8 GEMM stages its operands
+// through TMA", opening summary: row-scaled A8; "Measured": E4M3FN weights
+// with row scales).  Per-tensor FP8 follows AstrAI's per-tensor NT benchmark,
+// whose quantizer reduces an amax before encoding.  NVFP4 follows ninfer PR
+// #160 (E2M1 codes, an E4M3 scale per 16 K-elements, an fp32 tensor scale).
+//
+// All three are HBM-bound streams (2 bytes in, 1 or 0.56 bytes out per
+// element).  Loads are 16-byte vectors of 8 bf16; amax is taken on the bf16
+// bit patterns with the sign cleared (for non-negative floats the unsigned
+// integer order is the numeric order), reduced across the wavefront with
+// lane shuffles, then across waves through LDS.  Scales and ratios use IEEE
+// binary32 division (no fast-math), so the codes are bit-identical to a
+// correctly rounded reference.
+#include "spg_common.h"
+
+namespace spg {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// max(|bf16|) over the 8 values of a 16-byte vector, as a bit pattern.
+__device__ __forceinline__ uint32_t amax8(const uint4 &v)
+{
+    uint32_t m = 0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+        m = max(m, max(lo, hi));
+    }
+    return m;
+}
+
+// Encode 8 bf16 values (one 16-byte vector) to 8 E4M3 codes under scale s.
+__device__ __forceinline__ uint2 encode8_e4m3(const uint4 &v, float s)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t c0, c1, c2, c3;
+        if (s > 0.0f) {
+            c0 = encode_e4m3(bf16_lo(w[2 * h]) / s);
+            c1 = encode_e4m3(bf16_hi(w[2 * h]) / s);
+            c2 = encode_e4m3(bf16_lo(w[2 * h + 1]) / s);
+            c3 = encode_e4m3(bf16_hi(w[2 * h + 1]) / s);
+        } else {   // zero scale: signed zeros
+            c0 = (w[2 * h] >> 8) & 0x80u;
+            c1 = (w[2 * h] >> 24) & 0x80u;
+            c2 = (w[2 * h + 1] >> 8) & 0x80u;
+            c3 = (w[2 * h + 1] >> 24) & 0x80u;
+        }
+        out[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    return make_uint2(out[0], out[1]);
+}
+
+// Block-wide max of a per-thread value (256 threads = 4 waves).
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *lds4)
+{
+    v = wave_max_u32(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds4[wave] = v;
+    __syncthreads();
+    uint32_t r = max(max(lds4[0], lds4[1]), max(lds4[2], lds4[3]));
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// ---------------------------------------------------------------------------
+// Row-wise FP8.  TPR threads cooperate on one row (TPR = 64: one wave per
+// row, 4 rows per block; TPR = 256: one row per block).  Each thread keeps up
+// to CACHE 16-byte vectors of its row in registers between the amax pass and
+// the encode pass; CACHE = 0 re-reads the row (served from L2) instead.
+// ---------------------------------------------------------------------------
+template <int TPR, int CACHE>
+__global__ __launch_bounds__(kThreads) void quant_rowwise_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t K, int64_t ldx,
+    uint8_t *__restrict__ q, int64_t ldq, float *__restrict__ scale)
+{
+    __shared__ uint32_t lds4[4];
+    constexpr int RPB = kThreads / TPR;
+    const int lane = threadIdx.x % TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const bool live = row < rows;
+    const uint16_t *xr = x + (live ? row : 0) * ldx;
+    const int64_t nvec = K / 8;
+
+    uint32_t m = 0;
+    uint4 cache[CACHE > 0 ? CACHE : 1];
+    if (CACHE > 0) {
+#pragma unroll
+        for (int c = 0; c < CACHE; ++c) {
+            int64_t v = lane + (int64_t)c * TPR;
+            if (live && v < nvec) {
+                cache[c] = ld16(xr + v * 8);
+                m = max(m, amax8(cache[c]));
+            }
+        }
+    } else {
+        for (int64_t v = lane; live && v < nvec; v += TPR) m = max(m, amax8(ld16(xr + v * 8)));
+    }
+
+    if (TPR == kThreads) {
+        m = block_max_u32(m, lds4);
+    } else {
+#pragma unroll
+        for (int off = TPR / 2; off >= 1; off >>= 1) {
+            uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+            m = max(m, o);
+        }
+    }
+    if (!live) return;
+    const float s = __uint_as_float(m << 16) / 448.0f;
+    if (lane == 0) scale[row] = s;
+    uint8_t *qr = q + row * ldq;
+    if (CACHE > 0) {
+#pragma unroll
+        for (int c = 0; c < CACHE; ++c) {
+            int64_t v = lane + (int64_t)c * TPR;
+            if (v < nvec) *reinterpret_cast<uint2 *>(qr + v * 8) = encode8_e4m3(cache[c], s);
+        }
+    } else {
+        for (int64_t v = lane; v < nvec; v += TPR)
+            *reinterpret_cast<uint2 *>(qr + v * 8) = encode8_e4m3(ld16(xr + v * 8), s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor amax: `parts` blocks per matrix each write the max of their
+// slice; the encode kernels fold the partial maxima.  No atomics and no
+// zero-initialised scratch, so the result is deterministic.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(
+    const uint16_t *__restrict__ x, int64_t elems, int64_t bstride, int64_t parts,
+    uint32_t *__restrict__ partial)
+{
+    __shared__ uint32_t lds4[4];
+    const int64_t b = blockIdx.y;
+    const uint16_t *xb = x + b * bstride;
+    const int64_t nvec = elems / 8;
+    const int64_t per = (nvec + parts - 1) / parts;
+    const int64_t v0 = blockIdx.x * per, v1 = min(nvec, v0 + per);
+    uint32_t m = 0;
+    for (int64_t v = v0 + threadIdx.x; v < v1; v += kThreads) m = max(m, amax8(ld16(xb + v * 8)));
+    m = block_max_u32(m, lds4);
+    if (threadIdx.x == 0) partial[b * parts + blockIdx.x] = m;
+}
+
+__device__ __forceinline__ uint32_t fold_partials(const uint32_t *p, int64_t parts, uint32_t *lds4)
+{
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < parts; i += kThreads) m = max(m, p[i]);
+    return block_max_u32(m, lds4);
+}
+
+__global__ __launch_bounds__(kThreads) void quant_tensor_encode_kernel(
+    const uint16_t *__restrict__ x, int64_t elems, int64_t bstride, const uint32_t *__restrict__ partial,
+    int64_t parts, uint8_t *__restrict__ q, float *__restrict__ scale)
+{
+    __shared__ uint32_t lds4[4];
+    const int64_t b = blockIdx.y;
+    const uint32_t m = fold_partials(partial + b * parts, parts, lds4);
+    const float s = __uint_as_float(m << 16) / 448.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) scale[b] = s;
+    const uint16_t *xb = x + b * bstride;
+    uint8_t *qb = q + b * elems;
+    const int64_t nvec = elems / 8;
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads)
+        *reinterpret_cast<uint2 *>(qb + v * 8) = encode8_e4m3(ld16(xb + v * 8), s);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 encode: one thread per 16-element group (two 16-byte loads, one
+// 8-byte code store, one scale byte).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void quant_block16_encode_kernel(
+    const uint16_t *__restrict__ x, int64_t groups, const uint32_t *__restrict__ partial, int64_t parts,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ bscale, float *__restrict__ tscale)
+{
+    __shared__ uint32_t lds4[4];
+    const uint32_t m = fold_partials(partial, parts, lds4);
+    const float t = __uint_as_float(m << 16) / 2688.0f;
+    const float six_t = 6.0f * t;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = t;
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * kThreads) {
+        const uint4 v0 = ld16(x + g * 16), v1 = ld16(x + g * 16 + 8);
+        const uint32_t gm = max(amax8(v0), amax8(v1));
+        uint32_t b = 0;
+        if (t > 0.0f) b = encode_e4m3(__uint_as_float(gm << 16) / six_t);
+        const float e = decode_e4m3(b) * t;
+        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t c0, c1;
+            if (e > 0.0f) {
+                c0 = encode_e2m1(bf16_lo(w[i]) / e);
+                c1 = encode_e2m1(bf16_hi(w[i]) / e);
+            } else {
+                c0 = (w[i] >> 12) & 0x8u;
+                c1 = (w[i] >> 28) & 0x8u;
+            }
+            packed[i >> 2] |= (c0 | (c1 << 4)) << (8 * (i & 3));
+        }
+        *reinterpret_cast<uint2 *>(q + g * 8) = make_uint2(packed[0], packed[1]);
+        bscale[g] = (uint8_t)b;
+    }
+}
+
+int64_t grid_for(int64_t items, int64_t per_block, int64_t cap)
+{
+    int64_t g = (items + per_block - 1) / per_block;
+    return g < 1 ? 1 : (g > cap ? cap : g);
+}
+
+}  // namespace
+
+int64_t amax_parts(int64_t elems)
+{
+    // one partial per 16K elements, at most 1024 per matrix
+    int64_t p = (elems + 16383) / 16384;
+    return p < 1 ? 1 : (p > 1024 ? 1024 : p);
+}
+
+hipError_t launch_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t K, int64_t ldx,
+                                   uint8_t *q, int64_t ldq, float *scale, hipStream_t s)
+{
+    const int64_t nvec = K / 8;
+    if (nvec <= 64 * 2) {
+        dim3 grid((unsigned)((rows + 3) / 4));
+        quant_rowwise_kernel<64, 2><<<grid, kThreads, 0, s>>>(x, rows, K, ldx, q, ldq, scale);
+    } else {
+        dim3 grid((unsigned)rows);
+        if (nvec <= 256 * 1)
+            quant_rowwise_kernel<256, 1><<<grid, kThreads, 0, s>>>(x, rows, K, ldx, q, ldq, scale);
+        else if (nvec <= 256 * 2)
+            quant_rowwise_kernel<256, 2><<<grid, kThreads, 0, s>>>(x, rows, K, ldx, q, ldq, scale);
+        else if (nvec <= 256 * 4)
+            quant_rowwise_kernel<256, 4><<<grid, kThreads, 0, s>>>(x, rows, K, ldx, q, ldq, scale);
+        else if (nvec <= 256 * 8)
+            quant_rowwise_kernel<256, 8><<<grid, kThreads, 0, s>>>(x, rows, K, ldx, q, ldq, scale);
+        else
+            quant_rowwise_kernel<256, 0><<<grid, kThreads, 0, s>>>(x, rows, K, ldx, q, ldq, scale);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_tensor(const uint16_t *x, int64_t batch, int64_t rows, int64_t K,
+                                  int64_t bstride, uint8_t *q, float *scale, uint32_t *ws,
+                                  int64_t parts, hipStream_t s)
+{
+    const int64_t elems = rows * K;
+    amax_partial_kernel<<<dim3((unsigned)parts, (unsigned)batch), kThreads, 0, s>>>(x, elems, bstride, parts, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t g = grid_for(elems / 8, kThreads * 4, 2048);
+    quant_tensor_encode_kernel<<<dim3((unsigned)g, (unsigned)batch), kThreads, 0, s>>>(x, elems, bstride, ws,
+                                                                                      parts, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_block16(const uint16_t *x, int64_t rows, int64_t K, uint8_t *q,
+                                   uint8_t *bscale, float *tscale, uint32_t *ws, int64_t parts,
+                                   hipStream_t s)
+{
+    const int64_t elems = rows * K;
+    amax_partial_kernel<<<dim3((unsigned)parts, 1), kThreads, 0, s>>>(x, elems, elems, parts, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t groups = elems / 16;
+    const int64_t g = grid_for(groups, kThreads * 2, 4096);
+    quant_block16_encode_kernel<<<dim3((unsigned)g), kThreads, 0, s>>>(x, groups, ws, parts, q, bscale, tscale);
+    return hipGetLastError();
+}
+
+}  // namespace spg

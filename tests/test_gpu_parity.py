@@ -1,0 +1,389 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Quantizers must match bit for bit (codes and fp32 scales).  GEMM outputs must
+satisfy, per element, |gpu - y| <= 2^-8 |y| + 2^-12 S, with y the oracle's
+exact fp64 result and S the scaled sum of |products|.  The oracle quantizes
+the bf16 inputs itself: no oracle input comes from the GPU.  Full-size
+workloads are checked on sampled rows x columns (tile edges included).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic import WORKLOADS, bf16_normal, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import scaled_precision_gemm_amd as m
+    return m
+
+
+def dev(x16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_close(gpu_bits, y, S, what):
+    ok, excess = oracle.within_tolerance(gpu_bits, y, S)
+    exact = np.mean(gpu_bits == np.vectorize(oracle.bf16_from_f64, otypes=[np.uint16])(y)) if y.size < 300000 else None
+    bad = np.argwhere(~ok)
+    assert ok.all(), (f"{what}: {len(bad)} of {ok.size} outside the bound; worst excess {excess.max():.3g} "
+                      f"at {bad[:5].tolist()}")
+    return exact
+
+
+# ---------------------------------------------------------------------------
+# quantize_rowwise
+# ---------------------------------------------------------------------------
+ROW_SHAPES = [(1, 16), (17, 48), (321, 512), (5, 1024), (3, 1040), (9, 2048), (4, 4096), (6, 8192),
+              (2, 16384), (7, 17408), (3, 40000)]
+
+
+@pytest.mark.parametrize("shape", ROW_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_quantize_rowwise_bitexact(spg, shape):
+    x = bf16_normal(shape, 1.0, 1000 + shape[1])
+    q, s = spg.quantize_rowwise(dev(x))
+    qo, so = oracle.quantize_rowwise(x)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("name", ["fp8_row_tiny", "fp8_row_add_t1024", "fp8_row_swiglu_t4096"])
+def test_quantize_rowwise_bitexact_workloads(spg, name):
+    wl = WORKLOADS[name]
+    A, W, _ = wl.inputs()
+    for x in (A, W):
+        q, s = spg.quantize_rowwise(dev(x))
+        qo, so = oracle.quantize_rowwise(x)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(q.cpu().numpy(), qo)
+        del q, s
+
+
+def test_quantize_rowwise_every_bf16_value_with_unit_and_pow2_scales(spg):
+    # rows led by 448 * 2^k have scale exactly 2^k, so every bf16 value of
+    # magnitude <= 448 * 2^k is encoded directly: all roundings and ties
+    u = np.arange(65536, dtype=np.uint32)
+    f = (u << 16).view(np.float32)
+    for k in (0, -7, 5):
+        top = np.float32(448.0 * 2.0 ** k)
+        vals = f[np.isfinite(f) & (np.abs(f) <= top)]
+        K = 4096
+        n = (len(vals) + K - 2) // (K - 1)
+        body = np.resize(vals, n * (K - 1)).reshape(n, K - 1)
+        x = np.concatenate([np.full((n, 1), top, np.float32), body], axis=1)
+        x16 = f32_to_bf16_bits(x)
+        q, s = spg.quantize_rowwise(dev(x16))
+        qo, so = oracle.quantize_rowwise(x16)
+        assert np.all(so == np.float32(2.0 ** k))
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quantize_rowwise_zero_and_signed_zero_rows(spg):
+    x = np.zeros((3, 64), np.uint16)
+    x[1, ::3] = 0x8000
+    x[2] = bf16_normal((64,), 1.0, 5)
+    q, s = spg.quantize_rowwise(dev(x))
+    qo, so = oracle.quantize_rowwise(x)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quantize_rowwise_strided_rows(spg):
+    x = bf16_normal((40, 160), 1.0, 6)
+    xt = dev(x)[:, :128]                       # row stride 160, K 128
+    q = torch.full((40, 144), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.empty(40, dtype=torch.float32, device="cuda")
+    spg.quantize_rowwise(xt, out=q[:, :128], scale=s)
+    qo, so = oracle.quantize_rowwise(np.ascontiguousarray(x[:, :128]))
+    qh = q.cpu().numpy()
+    assert np.array_equal(qh[:, :128], qo) and np.all(qh[:, 128:] == 0xAB)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# quantize_tensor / quantize_block16
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(1, 5, 32), (3, 17, 48), (64, 512, 512), (1, 8192, 8192)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_quantize_tensor_bitexact(spg, shape):
+    x = bf16_normal(shape, 1.0, 2000 + shape[0])
+    q, s = spg.quantize_tensor(dev(x))
+    qo, so = oracle.quantize_tensor(x)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("shape,std", [((1, 32), 1.0), ((7, 64), 1.0), ((33, 96), 0.02), ((4096, 6144), 1.0),
+                                       ((5120, 6144), 0.02)], ids=lambda v: str(v))
+def test_quantize_block16_bitexact(spg, shape, std):
+    x = bf16_normal(shape, std, 3000 + shape[0])
+    q, bs, t = spg.quantize_block16(dev(x))
+    qo, bso, to = oracle.quantize_block16(x)
+    assert t.cpu().numpy().view(np.uint32)[0] == np.float32(to).view(np.uint32)
+    assert np.array_equal(bs.cpu().numpy(), bso)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quantize_block16_every_bf16_value_in_unit_groups(spg):
+    # tensor amax 2688 gives t = 1; a group led by 6 gets scale code 1.0,
+    # so its other 15 values are encoded directly to E2M1
+    u = np.arange(65536, dtype=np.uint32)
+    f = (u << 16).view(np.float32)
+    vals = f[np.isfinite(f) & (np.abs(f) <= 6.0)]
+    n = (len(vals) + 14) // 15
+    body = np.resize(vals, n * 15).reshape(n, 15)
+    groups = np.concatenate([np.full((n, 1), 6.0, np.float32), body], axis=1)
+    K = 256
+    rows = (n + K // 16 - 1) // (K // 16)
+    pad = rows * (K // 16) - n
+    groups = np.concatenate([groups, np.tile(groups[:1], (pad, 1))])
+    x = groups.reshape(rows, K)
+    x[0, 0] = 2688.0
+    x16 = f32_to_bf16_bits(x)
+    q, bs, t = spg.quantize_block16(dev(x16))
+    qo, bso, to = oracle.quantize_block16(x16)
+    assert to == 1.0
+    assert np.array_equal(bs.cpu().numpy(), bso)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quantize_block16_wide_scale_range_and_zero(spg):
+    # group magnitudes from 2^-20 to 1 relative to the tensor maximum:
+    # subnormal and zero block-scale codes
+    x = bf16_normal((16, 512), 1.0, 7).astype(np.uint32)
+    xf = (x << 16).view(np.float32).reshape(16, 32, 16)
+    xf *= (2.0 ** -np.linspace(0, 20, 32, dtype=np.float32))[None, :, None]
+    xf[3] = 0.0
+    x16 = f32_to_bf16_bits(xf.reshape(16, 512))
+    q, bs, t = spg.quantize_block16(dev(x16))
+    qo, bso, to = oracle.quantize_block16(x16)
+    assert np.array_equal(bs.cpu().numpy(), bso) and np.any(bso < 8) and np.any(bso == 0)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+# ---------------------------------------------------------------------------
+# GEMM, whole outputs (small and ragged shapes)
+# ---------------------------------------------------------------------------
+
+def run_fp8(spg, A16, W16, epi, fmt, R16=None):
+    A, W = dev(A16), dev(W16)
+    if fmt == "e4m3_row":
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+    else:
+        qa, sa = spg.quantize_tensor(A)
+        qw, sw = spg.quantize_tensor(W)
+    out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=dev(R16) if R16 is not None else None, fmt=fmt)
+    return host_u16(out)
+
+
+def oracle_fp8(A16, W16, epi, fmt, R16=None):
+    if fmt == "e4m3_row":
+        return oracle.linear_e4m3_rowwise(A16, W16, epi, R16)
+    qa, sa = oracle.quantize_tensor(A16)
+    qw, sw = oracle.quantize_tensor(W16)
+    D, Da = oracle.gemm_e4m3_sums(qa, qw)
+    y, S, out = oracle.epilogue(epi, D, Da, sa[0], sw[0], R16)
+    return dict(y=y, S=S, out=out)
+
+
+SMALL = [(128, 256, 512), (1, 2, 16), (17, 34, 48), (257, 300, 160), (300, 258, 1040), (64, 512, 384)]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3_row", "e4m3_tensor"])
+@pytest.mark.parametrize("epi", ["store", "add", "swiglu"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_fp8_small_shapes(spg, shape, epi, fmt):
+    M, N, K = shape
+    A16 = bf16_normal((M, K), 1.0, M * 7 + K)
+    W16 = bf16_normal((N, K), 0.02, N * 11 + K)
+    R16 = bf16_normal((M, N), 1.0, M + N) if epi == "add" else None
+    gpu = run_fp8(spg, A16, W16, epi, fmt, R16)
+    ref = oracle_fp8(A16, W16, epi, fmt, R16)
+    assert gpu.shape == ref["out"].shape
+    check_close(gpu, ref["y"], ref["S"], f"{shape} {epi} {fmt}")
+
+
+def test_gemm_zero_weight_add_returns_residual_bitwise(spg):
+    A16 = bf16_normal((300, 256), 1.0, 1)
+    W16 = np.zeros((260, 256), np.uint16)
+    R16 = bf16_normal((300, 260), 1.0, 2)
+    gpu = run_fp8(spg, A16, W16, "add", "e4m3_row", R16)
+    assert np.array_equal(gpu, R16)
+
+
+def test_gemm_power_of_two_case_is_bitwise(spg):
+    # codes from a narrow exponent band with power-of-two scales: every partial
+    # sum is exact in fp32 whatever the order, so the GPU output must equal
+    # the oracle's single rounding bit for bit
+    rng = np.random.default_rng(3)
+    M, N, K = 96, 160, 64
+    vals = np.array([1.0, 1.125, 1.25, 1.5, 1.75, 2.0, -1.0, -1.5, -2.0, 0.0], np.float32)
+    A = rng.choice(vals, (M, K)).astype(np.float32)
+    W = rng.choice(vals, (N, K)).astype(np.float32) * np.float32(2.0 ** -3)
+    A[:, 0] = 448.0 * 2.0 ** -4
+    W[:, 0] = 448.0 * 2.0 ** -9
+    A16, W16 = f32_to_bf16_bits(A), f32_to_bf16_bits(W)
+    gpu = run_fp8(spg, A16, W16, "store", "e4m3_row")
+    ref = oracle.linear_e4m3_rowwise(A16, W16, "store")
+    assert np.all(ref["sa"] == np.float32(2.0 ** -4)) and np.all(ref["sw"] == np.float32(2.0 ** -9))
+    assert np.array_equal(gpu, ref["out"])
+
+
+def test_gemm_batched_tensor_scale_with_broadcast_weight(spg):
+    B, M, N, K = 3, 100, 72, 96
+    A16 = bf16_normal((B, M, K), 1.0, 9)
+    W16 = bf16_normal((N, K), 1.0, 10)
+    qa, sa = spg.quantize_tensor(dev(A16))
+    qw, sw = spg.quantize_tensor(dev(W16))
+    out = host_u16(spg.gemm_scaled(qa, sa, qw, sw, "store", fmt="e4m3_tensor"))
+    qwo, swo = oracle.quantize_tensor(W16)
+    for b in range(B):
+        qao, sao = oracle.quantize_tensor(A16[b])
+        D, Da = oracle.gemm_e4m3_sums(qao, qwo)
+        y, S, _ = oracle.epilogue("store", D, Da, sao[0], swo[0])
+        check_close(out[b], y, S, f"batch {b}")
+
+
+def test_gemm_add_in_place(spg):
+    M, N, K = 130, 260, 128
+    A16 = bf16_normal((M, K), 1.0, 21)
+    W16 = bf16_normal((N, K), 0.02, 22)
+    R16 = bf16_normal((M, N), 1.0, 23)
+    qa, sa = spg.quantize_rowwise(dev(A16))
+    qw, sw = spg.quantize_rowwise(dev(W16))
+    r = dev(R16)
+    spg.gemm_scaled(qa, sa, qw, sw, "add", residual=r, out=r)
+    ref = oracle.linear_e4m3_rowwise(A16, W16, "add", R16)
+    check_close(host_u16(r), ref["y"], ref["S"], "in-place add")
+
+
+def test_gemm_is_deterministic(spg):
+    A16 = bf16_normal((1024, 2048), 1.0, 31)
+    W16 = bf16_normal((512, 2048), 0.02, 32)
+    R16 = bf16_normal((1024, 512), 1.0, 33)
+    a = run_fp8(spg, A16, W16, "add", "e4m3_row", R16)
+    b = run_fp8(spg, A16, W16, "add", "e4m3_row", R16)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# NVFP4
+# ---------------------------------------------------------------------------
+
+def run_nvfp4(spg, A16, W16, epi, R16=None):
+    qa, bsa, ta = spg.quantize_block16(dev(A16))
+    qw, bsw, tw = spg.quantize_block16(dev(W16))
+    out = spg.gemm_scaled(qa, bsa, qw, bsw, epi, residual=dev(R16) if R16 is not None else None,
+                          fmt="nvfp4", tscale_a=ta, tscale_w=tw)
+    return host_u16(out)
+
+
+def oracle_nvfp4(A16, W16, epi, R16=None):
+    qa, bsa, ta = oracle.quantize_block16(A16)
+    qw, bsw, tw = oracle.quantize_block16(W16)
+    D, Da = oracle.gemm_nvfp4_sums(qa, bsa, qw, bsw)
+    y, S, out = oracle.epilogue(epi, D, Da, ta, tw, R16)
+    return dict(y=y, S=S, out=out)
+
+
+@pytest.mark.parametrize("epi", ["store", "add", "swiglu"])
+@pytest.mark.parametrize("shape", [(64, 64, 64), (17, 40, 96), (257, 300, 320), (128, 512, 1056)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_nvfp4_small_shapes(spg, shape, epi):
+    M, N, K = shape
+    A16 = bf16_normal((M, K), 1.0, 40 + M)
+    W16 = bf16_normal((N, K), 0.02, 41 + N)
+    R16 = bf16_normal((M, N), 1.0, 42) if epi == "add" else None
+    gpu = run_nvfp4(spg, A16, W16, epi, R16)
+    ref = oracle_nvfp4(A16, W16, epi, R16)
+    check_close(gpu, ref["y"], ref["S"], f"nvfp4 {shape} {epi}")
+
+
+def test_gemm_nvfp4_wide_scale_range(spg):
+    # block scales spanning subnormal E4M3 codes exercise every decode path
+    M, N, K = 96, 64, 512
+    x = bf16_normal((M, K), 1.0, 50).astype(np.uint32)
+    xf = (x << 16).view(np.float32).reshape(M, K // 16, 16)
+    xf *= (2.0 ** -np.linspace(0, 18, K // 16, dtype=np.float32))[None, :, None]
+    A16 = f32_to_bf16_bits(xf.reshape(M, K))
+    W16 = bf16_normal((N, K), 0.02, 51)
+    gpu = run_nvfp4(spg, A16, W16, "store")
+    ref = oracle_nvfp4(A16, W16, "store")
+    check_close(gpu, ref["y"], ref["S"], "nvfp4 wide scales")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled outputs
+# ---------------------------------------------------------------------------
+
+def sample(n, count, rng, tile=256):
+    edges = [0, n - 1] + [v for t in range(tile, n, tile) for v in (t - 1, t)][:12]
+    rest = rng.choice(n, size=max(0, count - len(edges)), replace=False)
+    return np.unique(np.clip(np.concatenate([edges, rest]), 0, n - 1))
+
+
+@pytest.mark.parametrize("name", ["fp8_row_add_t1024", "fp8_row_swiglu_t4096", "fp8_tensor_square_8192",
+                                  "fp8_tensor_bmm64_512", "nvfp4_add_t4096"])
+def test_workload_full_size_sampled(spg, name):
+    wl = WORKLOADS[name]
+    rng = np.random.default_rng(99)
+    A16, W16, R16 = wl.inputs()
+    A, W = dev(A16), dev(W16)
+    R = dev(R16) if R16 is not None else None
+    if wl.fmt == "e4m3_row":
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue, residual=R)
+    elif wl.fmt == "e4m3_tensor":
+        qa, sa = spg.quantize_tensor(A)
+        qw, sw = spg.quantize_tensor(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue, fmt="e4m3_tensor")
+    else:
+        qa, sa, ta = spg.quantize_block16(A)
+        qw, sw, tw = spg.quantize_block16(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue, residual=R, fmt="nvfp4", tscale_a=ta, tscale_w=tw)
+    torch.cuda.synchronize()
+    gpu = host_u16(out)
+    del A, W, R, qa, qw, out
+    torch.cuda.empty_cache()
+
+    batches = [0, wl.batch // 2, wl.batch - 1] if wl.batch > 1 else [None]
+    for b in batches:
+        Ab = A16[b] if b is not None else A16
+        Wb = W16[b] if b is not None else W16
+        g = gpu[b] if b is not None else gpu
+        rows = sample(wl.M, 40, rng)
+        cols = sample(wl.n_out, 40, rng, tile=128 if wl.epilogue == "swiglu" else 256)
+        wrows = np.concatenate([cols, cols + wl.N // 2]) if wl.epilogue == "swiglu" else cols
+        Rs = np.ascontiguousarray(R16[np.ix_(rows, cols)]) if R16 is not None else None
+        if wl.fmt == "e4m3_row":
+            qa_o, sa_o = oracle.quantize_rowwise(np.ascontiguousarray(Ab[rows]))
+            qw_o, sw_o = oracle.quantize_rowwise(np.ascontiguousarray(Wb[wrows]))
+            D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+        elif wl.fmt == "e4m3_tensor":
+            sa_o = oracle.amax(Ab) / np.float32(448.0)
+            sw_o = oracle.amax(Wb) / np.float32(448.0)
+            qa_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(Ab[rows]), sa_o)
+            qw_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(Wb[wrows]), sw_o)
+            D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+        else:
+            ta_o = oracle.nvfp4_tensor_scale(Ab)
+            tw_o = oracle.nvfp4_tensor_scale(Wb)
+            qa_o, bsa_o = oracle.quantize_block16_rows(np.ascontiguousarray(Ab[rows]), ta_o)
+            qw_o, bsw_o = oracle.quantize_block16_rows(np.ascontiguousarray(Wb[wrows]), tw_o)
+            D, Da = oracle.gemm_nvfp4_sums(qa_o, bsa_o, qw_o, bsw_o)
+            sa_o, sw_o = ta_o, tw_o
+        y, S, _ = oracle.epilogue(wl.epilogue, D, Da, sa_o, sw_o, Rs)
+        check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"{name} batch {b}")
