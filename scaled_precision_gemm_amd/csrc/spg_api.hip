@@ -48,6 +48,8 @@ int validate_desc(const spg_gemm_desc *d, int epi)
         if (d->lda < d->K || d->ldw < d->K) return SPG_EINVAL;
     }
     if ((d->lda & 15) || (d->ldw & 15)) return SPG_EINVAL;
+    // a 256-row tile of codes must fit the 31-bit range of a buffer resource
+    if (d->lda > (INT64_C(1) << 23) || d->ldw > (INT64_C(1) << 23)) return SPG_EUNSUPPORTED;
     if ((d->stride_a & 15) || (d->stride_w & 15)) return SPG_EINVAL;
     if (d->ldo < nout) return SPG_EINVAL;
     if (epi == SPG_EPI_ADD && d->ldr < nout) return SPG_EINVAL;
@@ -81,7 +83,7 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     const int64_t nout = n_out_of(d, epi);
     p->bm = (int32_t)kTile;
     p->bn = (int32_t)kTile;   // weight rows per tile (SWIGLU: 128 gate + 128 up)
-    p->bk = d->format == SPG_FMT_NVFP4 ? 64 : 128;
+    p->bk = 64;   // K elements per pipeline stage (both kernels)
     const int64_t tiles_m = cdiv(d->M, kTile);
     const int64_t tiles_n = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
     p->tiles = tiles_m * tiles_n * d->batch;

@@ -61,7 +61,10 @@ __device__ __forceinline__ h2 scale_h2(uint32_t code)
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs g)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_ab[2][2][kStageBytes];
+    constexpr int kLdsBytes = kEpiBytes > 4 * kStageBytes ? kEpiBytes : 4 * kStageBytes;
+    __shared__ __attribute__((aligned(2048))) uint8_t lds[kLdsBytes];
+    // [stage][operand] views of the flat array
+    auto lds_ab = [&](int st, int op) -> uint8_t * { return &lds[(st * 2 + op) * kStageBytes]; };
     __shared__ float lds_sa[kBM];
     __shared__ float lds_sw[kBN];
     __shared__ uint32_t lds_flag;
@@ -116,8 +119,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
             const uint32_t wa = (c & 3) == 0 ? va.x : (c & 3) == 1 ? va.y : (c & 3) == 2 ? va.z : va.w;
             const uint32_t ww = (c & 3) == 0 ? vw.x : (c & 3) == 1 ? vw.y : (c & 3) == 2 ? vw.z : vw.w;
             const int q = c >> 1;
-            *reinterpret_cast<uint4 *>(&lds_ab[st][0][swz(tid, c)]) = decode8_f16(wa, scale_h2((sa4 >> (8 * q)) & 0xFFu));
-            *reinterpret_cast<uint4 *>(&lds_ab[st][1][swz(tid, c)]) = decode8_f16(ww, scale_h2((sw4 >> (8 * q)) & 0xFFu));
+            *reinterpret_cast<uint4 *>(lds_ab(st, 0) + swz(tid, c)) = decode8_f16(wa, scale_h2((sa4 >> (8 * q)) & 0xFFu));
+            *reinterpret_cast<uint4 *>(lds_ab(st, 1) + swz(tid, c)) = decode8_f16(ww, scale_h2((sw4 >> (8 * q)) & 0xFFu));
         }
     };
 
@@ -136,10 +139,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
             v8h af[4], bf[4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
-                af[mi] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4 *>(&lds_ab[st][0][swz(wm * 128 + mi * 32 + l32, c)]));
+                af[mi] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4 *>(lds_ab(st, 0) + swz(wm * 128 + mi * 32 + l32, c)));
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-                bf[ni] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4 *>(&lds_ab[st][1][swz(brow(ni), c)]));
+                bf[ni] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4 *>(lds_ab(st, 1) + swz(brow(ni), c)));
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     }
 
     if (g.split_k > 1 && !splitk_fixup(g, T, acc, &lds_flag)) return;
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw);
+    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds);
 }
 
 __global__ void zero_u32_kernel_fp4(uint32_t *p, int64_t n)

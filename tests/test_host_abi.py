@@ -182,7 +182,7 @@ def test_quantizer_validation_errors(spg):
 
 def test_plans_for_the_workloads(spg):
     p = spg.gemm_plan(1024, 5120, 17408, "e4m3_row", "add")
-    assert (p["bm"], p["bn"], p["tiles"], p["split_k"]) == (256, 256, 80, 3)
+    assert (p["bm"], p["bn"], p["bk"], p["tiles"], p["split_k"]) == (256, 256, 64, 80, 3)
     p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu")
     assert (p["tiles"], p["split_k"]) == (16 * 136, 1)
     p = spg.gemm_plan(128, 256, 512, "e4m3_row", "store")
