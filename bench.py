@@ -91,6 +91,84 @@ def traffic_from_profiles(wl, name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _read_csv(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command=""):
+    """Write profiles/<kernel>_<workload>.md (rocprofv3 kernel statistics and
+    HBM traffic per launch) and the traffic record bench.py reports.
+
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM are scaled by what
+    the same counters read for the plain copy dispatch of known size that
+    --copy-probe-mib runs in the same process."""
+    wl = WORKLOADS[name]
+    kname = "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel"
+    stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
+    lines = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    gemm_avg_us = None
+    for r in stats:
+        short = r["Name"].replace("void ", "").replace("spg::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+        if kname in r["Name"]:
+            gemm_avg_us = float(r["AverageNs"]) / 1e3
+
+    def per_dispatch(d, counter):
+        rows = _read_csv(_find(d, "counter_collection.csv"))
+        gemm = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and kname in r["Kernel_Name"]]
+        copy = [(float(r["Counter_Value"]), int(r["Grid_Size"])) for r in rows
+                if r["Counter_Name"] == counter and "copy" in r["Kernel_Name"].lower()]
+        return gemm, copy
+
+    g_fetch, c_fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    g_write, c_write = per_dispatch(write_dir, "WRITE_SIZE")
+    copy_bytes = None
+    for i, a in enumerate(command.split()):
+        if a == "--copy-probe-mib":
+            copy_bytes = int(command.split()[i + 1]) << 20
+    f_read = (max(v for v, _ in c_fetch) * 1024 / copy_bytes) if (c_fetch and copy_bytes) else 1.0
+    f_write = (max(v for v, _ in c_write) * 1024 / copy_bytes) if (c_write and copy_bytes) else 1.0
+    rd = float(np.median(g_fetch)) * 1024 / f_read
+    wr = float(np.median(g_write)) * 1024 / f_write
+    rec = {
+        "kernel": kname, "workload": name, "kernel_source_hash": kernel_source_hash(wl.fmt),
+        "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+        "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": gemm_bytes(wl),
+        "fetch_scale": f_read, "write_scale": f_write, "rocprof_avg_launch_us": gemm_avg_us,
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    allrec = json.load(open(tpath)) if os.path.exists(tpath) else {}
+    allrec[name] = rec
+    with open(tpath, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+    md = os.path.join(ROOT, "profiles", f"{kname}_{name}.md")
+    with open(md, "w") as fh:
+        fh.write(f"# {kname} on {name} (M={wl.M}, N={wl.N}, K={wl.K}, batch={wl.batch}, {wl.fmt}, {wl.epilogue})\n\n")
+        fh.write(f"Kernel statistics, `rocprofv3 --kernel-trace --stats` (one MI355X):\n\n")
+        fh.write("\n".join(lines) + "\n\n")
+        fh.write(f"HBM traffic of one {kname} launch (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, "
+                 f"median over launches), scaled by the counters' reading for a plain copy of "
+                 f"{(copy_bytes or 0) >> 20} MiB (read scale {f_read:.4f}, write scale {f_write:.4f}):\n\n")
+        fh.write(f"- read  {rd / 1e6:.1f} MB, write {wr / 1e6:.1f} MB, total {(rd + wr) / 1e6:.1f} MB\n")
+        fh.write(f"- algorithmic (A and W codes once, residual once, output once): {gemm_bytes(wl) / 1e6:.1f} MB\n")
+        fh.write(f"- kernel source hash {rec['kernel_source_hash']}\n\n")
+        fh.write("Commands (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):\n\n")
+        fh.write("```\n" + command.strip() + "\n```\n")
+    print(f"wrote {md} and {tpath}")
+
+
 def to_dev(x16, torch):
     return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -129,10 +207,13 @@ def cpu_baseline(wl, A16, W16, R16, budget_s: float):
             D, Da = oracle.gemm_nvfp4_sums(qa, sa, Wq, Ws)
             oracle.epilogue(wl.epilogue, D, Da, ta, tw, r)
 
+    # the oracle parallelizes over rows: calibrate on one row per thread,
+    # then time a whole number of such rounds filling the budget
+    per = oracle.threads()
     t0 = time.perf_counter()
-    step(1)
+    step(per)
     one = max(time.perf_counter() - t0, 1e-4)
-    rows = int(max(1, min(wl.M, budget_s / one)))
+    rows = int(min(wl.M, per * max(1, round(budget_s / one))))
     t0 = time.perf_counter()
     step(rows)
     dt = time.perf_counter() - t0
@@ -157,7 +238,17 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating input/weight buffer sets")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, run one plain bf16->f16 copy of this many MiB (the reference "
+                         "dispatch for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn rocprofv3 output of this workload into profiles/ summaries")
+    ap.add_argument("--command", default="", help="with --summarize: the command line that produced the runs")
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize_profiles(args.workload, *args.summarize, command=args.command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -225,6 +316,14 @@ def main():
         a_codes = torch.empty(wl.a_shape() if wl.fmt != "nvfp4" else (wl.M, wl.K // 2), dtype=torch.uint8,
                               device="cuda")
     ws = spg.gemm_workspace(a_codes, weights[0][0], wl.fmt, wl.epilogue, out=out, residual=R)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty(n // 2, dtype=torch.float16, device="cuda")
+        dst.copy_(src)                        # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.current_stream()
     n_ev = max(args.warmup, args.steps)
