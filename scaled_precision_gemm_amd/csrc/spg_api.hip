@@ -95,9 +95,7 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
 size_t plan_workspace(const spg_plan *p)
 {
     if (p->split_k <= 1) return 0;
-    const size_t partial = (size_t)p->tiles * p->split_k * kTile * kTile * sizeof(float);
-    const size_t counters = (((size_t)p->tiles * sizeof(uint32_t)) + 255) & ~(size_t)255;
-    return partial + counters;
+    return (size_t)p->tiles * p->split_k * kTile * kTile * sizeof(float);
 }
 
 }  // namespace
@@ -229,11 +227,7 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.k_chunk = p.split_k > 1 ? cdiv(cdiv(d->K, p.split_k), unit_k) * unit_k : (d->K > 0 ? d->K : 1);
     g.tiles_m = cdiv(d->M, kTile);
     g.tiles_n = epilogue == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
-    if (p.split_k > 1) {
-        g.partials = (float *)ws;
-        const size_t partial = (size_t)p.tiles * p.split_k * kTile * kTile * sizeof(float);
-        g.counters = (uint32_t *)((char *)ws + partial);
-    }
+    if (p.split_k > 1) g.partials = (float *)ws;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = d->format == SPG_FMT_NVFP4 ? launch_gemm_nvfp4(g, p, s) : launch_gemm_fp8(g, p, s);
     return e == hipSuccess ? SPG_OK : SPG_EHIP;

@@ -111,7 +111,6 @@ struct GemmArgs {
     int32_t format, epilogue;
     const float *tscale_a, *tscale_w;
     float *partials;                  // split-K fp32 partial tiles (workspace)
-    uint32_t *counters;               // split-K arrival counters (workspace)
     int32_t split_k;
     int64_t k_chunk;                  // K per split (multiple of the tile K)
     int64_t tiles_m, tiles_n;         // output tiles per product
@@ -119,6 +118,7 @@ struct GemmArgs {
 
 hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s);
 hipError_t launch_gemm_nvfp4(const GemmArgs &g, const spg_plan &p, hipStream_t s);
+hipError_t launch_splitk_reduce(const GemmArgs &g, int64_t tiles, hipStream_t s);
 hipError_t launch_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t K, int64_t ldx,
                                    uint8_t *q, int64_t ldq, float *scale, hipStream_t s);
 hipError_t launch_quantize_tensor(const uint16_t *x, int64_t batch, int64_t rows, int64_t K,

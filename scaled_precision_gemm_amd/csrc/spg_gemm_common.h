@@ -55,10 +55,9 @@ struct Tile {
 // column-major inside a group, so neighbouring tile ids share A panels
 // (same rows) and W panels (same columns) through the L2 of their XCD.
 template <int EPI>
-__device__ __forceinline__ Tile tile_of(const GemmArgs &g)
+__device__ __forceinline__ Tile tile_from_id(const GemmArgs &g, int64_t t)
 {
     Tile T;
-    int64_t t = xcd_remap(blockIdx.x, gridDim.x);
     T.global = t;
     const int64_t per = g.tiles_m * g.tiles_n;
     T.b = t / per;
@@ -72,6 +71,12 @@ __device__ __forceinline__ Tile tile_of(const GemmArgs &g)
     T.n0 = EPI == SPG_EPI_SWIGLU ? T.tn * (kBN / 2) : T.tn * kBN;
     T.c0 = T.n0;
     return T;
+}
+
+template <int EPI>
+__device__ __forceinline__ Tile tile_of(const GemmArgs &g)
+{
+    return tile_from_id<EPI>(g, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // W row of tile row r (0..255) and whether it exists.  SWIGLU: rows 0..127
@@ -101,48 +106,24 @@ __device__ __forceinline__ void zero_acc(Acc &acc)
             for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.0f;
 }
 
-// Split-K: every K slice stores its fp32 partial tile (register order, so
-// each store instruction writes 1 KiB contiguous per wave); the slice that
-// arrives last (device-scope counter, zeroed before the launch) sums all
-// partials in slice order - independent of which slice arrives last, so the
-// result is deterministic - and goes on to the epilogue.  Returns false for
-// the slices that stop here.
-__device__ __forceinline__ bool splitk_fixup(const GemmArgs &g, const Tile &T, Acc &acc, uint32_t *flag)
+// Split-K, part 1: every K slice stores its fp32 partial tile and stops; a
+// second kernel (splitk_reduce_kernel) sums the slices once all have
+// finished - the kernel boundary orders the stores before the loads, so no
+// device-scope fence or counter is needed.  A lane's 16 accumulators of one
+// 32x32 block are stored contiguously (four 16-byte stores; a wave writes
+// 4 KiB contiguous per block): slice s of tile t, block b, thread x starts at
+// ((t * S + s) * 16 + b) * 4096 + x * 16 floats.
+__device__ __forceinline__ void splitk_store(const GemmArgs &g, const Tile &T, const Acc &acc)
 {
-    const int tid = threadIdx.x;
-    const int split = blockIdx.y;
-    constexpr int64_t kTileElems = (int64_t)kBM * kBN;
-    float *mine = g.partials + (T.global * g.split_k + split) * kTileElems;
+    float *base = g.partials + (T.global * g.split_k + blockIdx.y) * (int64_t)(kBM * kBN) + threadIdx.x * 16;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int blk = 0; blk < 16; ++blk) {
+        v4f *dst = reinterpret_cast<v4f *>(base + blk * (kThreads * 16));
+        const v16f &a = acc[blk >> 2][blk & 3];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mine[((mi * 4 + ni) * 16 + e) * kThreads + tid] = acc[mi][ni][e];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&g.counters[T.global], 1u);
-        *flag = (prev == (uint32_t)g.split_k - 1) ? 1u : 0u;
+        for (int q = 0; q < 4; ++q)
+            __builtin_nontemporal_store(v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, dst + q);
     }
-    __syncthreads();
-    if (!*flag) return false;
-    __threadfence();
-    const float *all = g.partials + T.global * g.split_k * kTileElems;
-    // one slice at a time, all 256 loads of a slice in flight together
-    for (int sp = 0; sp < g.split_k; ++sp) {
-        const float *p = all + sp * kTileElems + tid;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float v = __builtin_nontemporal_load(&p[((mi * 4 + ni) * 16 + e) * kThreads]);
-                    acc[mi][ni][e] = sp == 0 ? v : acc[mi][ni][e] + v;
-                }
-    }
-    return true;
 }
 
 // LDS-staged fused epilogue.

@@ -94,7 +94,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     __shared__ __attribute__((aligned(2048))) uint8_t lds[kLdsBytes];
     __shared__ float lds_sa[kBM];
     __shared__ float lds_sw[kBN];
-    __shared__ uint32_t lds_flag;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -265,28 +264,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     }
     __syncthreads();
 
-    if (g.split_k > 1 && !splitk_fixup(g, T, acc, &lds_flag)) return;
+    if (g.split_k > 1) {
+        splitk_store(g, T, acc);      // the slices are summed by splitk_reduce_kernel
+        return;
+    }
     epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds);
-}
-
-__global__ void zero_u32_kernel(uint32_t *p, int64_t n)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 {
-    if (g.split_k > 1) {
-        zero_u32_kernel<<<dim3((unsigned)((p.tiles + 255) / 256)), 256, 0, s>>>(g.counters, p.tiles);
-    }
     dim3 grid((unsigned)p.tiles, (unsigned)g.split_k, 1);
     if (g.format == SPG_FMT_E4M3_ROW)
         gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW><<<grid, kThreads, 0, s>>>(g);
     else
         gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR><<<grid, kThreads, 0, s>>>(g);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && g.split_k > 1) e = launch_splitk_reduce(g, p.tiles, s);
+    return e;
 }
 
 }  // namespace

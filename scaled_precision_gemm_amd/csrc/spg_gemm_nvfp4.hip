@@ -67,7 +67,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     auto lds_ab = [&](int st, int op) -> uint8_t * { return &lds[(st * 2 + op) * kStageBytes]; };
     __shared__ float lds_sa[kBM];
     __shared__ float lds_sw[kBN];
-    __shared__ uint32_t lds_flag;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -164,24 +163,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
         __syncthreads();
     }
 
-    if (g.split_k > 1 && !splitk_fixup(g, T, acc, &lds_flag)) return;
+    if (g.split_k > 1) {
+        splitk_store(g, T, acc);      // the slices are summed by splitk_reduce_kernel
+        return;
+    }
     epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds);
-}
-
-__global__ void zero_u32_kernel_fp4(uint32_t *p, int64_t n)
-{
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 {
-    if (g.split_k > 1)
-        zero_u32_kernel_fp4<<<dim3((unsigned)((p.tiles + 255) / 256)), 256, 0, s>>>(g.counters, p.tiles);
     dim3 grid((unsigned)p.tiles, (unsigned)g.split_k, 1);
     gemm_nvfp4_kernel<EPI><<<grid, kThreads, 0, s>>>(g);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && g.split_k > 1) e = launch_splitk_reduce(g, p.tiles, s);
+    return e;
 }
 
 }  // namespace
