@@ -29,7 +29,8 @@
 //    those MFMAs run).  A copy thus has about 1.4 stages to land.
 //  * SWIGLU pairs weight rows inside one 256-row W tile (128 gate + 128 up).
 //  * XCD-aware tile order; optional split-K through the workspace;
-//    LDS-staged epilogue with 16-byte stores.
+//    epilogue straight from registers with 8-byte stores (W fragments are the
+//    first MFMA operand, so a lane holds four adjacent output columns).
 #include "spg_gemm_common.h"
 
 namespace spg {
@@ -41,7 +42,7 @@ constexpr int kBK = 128;                      // K bytes (E4M3 elements) per sta
 constexpr int kOp = kBM * kBK;                // one operand, one stage: 32 KiB
 constexpr int kSlot = 2 * kOp;                // A + W of one stage: 64 KiB
 constexpr uint32_t kOOB = 0x80000000u;        // buffer offset past any range
-constexpr int kLdsBytes = kEpiBytes > 2 * kSlot ? kEpiBytes : 2 * kSlot;
+constexpr int kLdsBytes = 2 * kSlot;
 
 // Raw buffer resource: base, no stride, `bytes` in range, dword format bits.
 __device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
@@ -92,8 +93,8 @@ template <int EPI, int SMODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 {
     __shared__ __attribute__((aligned(2048))) uint8_t lds[kLdsBytes];
-    __shared__ float lds_sa[kBM];
-    __shared__ float lds_sw[kBN];
+    __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
+    __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -109,21 +110,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     const int nk = (int)((k_end - k_begin + kBK - 1) / kBK);
     const int64_t Nh = g.N / 2;
 
-    // ---- scales into LDS (read by the epilogue after the main loop) ---------
-    {
-        bool wok;
-        const int64_t wr = w_row<EPI>(g, T, tid, wok);
-        const int64_t r = T.m0 + tid;
-        if (SMODE == SPG_FMT_E4M3_ROW) {
-            const float *sa = (const float *)g.sa + (g.stride_a ? T.b * g.sa_bstride : 0);
-            const float *sw = (const float *)g.sw + (g.stride_w ? T.b * g.sw_bstride : 0);
-            lds_sa[tid] = r < g.M ? sa[r] : 0.0f;
-            lds_sw[tid] = wok ? sw[wr] : 0.0f;
-        } else {
-            lds_sa[tid] = ((const float *)g.sa)[g.stride_a ? T.b : 0];
-            lds_sw[tid] = ((const float *)g.sw)[g.stride_w ? T.b : 0];
-        }
-    }
+    // scales into LDS (read by the epilogue after the main loop's barriers)
+    stage_scales<EPI, SMODE>(g, T, lds_sa, lds_sw);
 
     // ---- copy setup -----------------------------------------------------------
     // Wave w fills tile rows [64 w, 64 w + 64) of A and of W: eight 8-row
@@ -197,10 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             foff[ks][h] = (uint32_t)l32 * kBK + ((((uint32_t)(ks * 4 + khalf * 2 + h)) ^ fx) << 4);
-    auto brow0 = [&](int ni) -> uint32_t {
-        if (EPI == SPG_EPI_SWIGLU) return ni < 2 ? wn * 64 + ni * 32 : 128 + wn * 64 + (ni - 2) * 32;
-        return wn * 128 + ni * 32;
-    };
+    auto brow0 = [&](int ni) -> uint32_t { return (uint32_t)wtile_row0<EPI>(wn, ni); };
     // Fragment half-reads r0 .. r1-1 of sub-step ks of stage kt: index 0..7
     // are the B fragments (ni = r / 2, half r % 2), 8..15 the A fragments.
     auto read_frags = [&](int kt, int ks, Frags &F, int r0, int r1) {
@@ -244,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
             for (int j = 0; j < 32; ++j) {
                 const int mi = (j & 15) >> 2, ni = j & 3;
                 const Frags &F = j < 16 ? F0 : F1;
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(F.a[mi]), op(F.b[ni]), acc[mi][ni],
+                acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(F.b[ni]), op(F.a[mi]), acc[ni][mi],
                                                                               0, 0, 0, 0, 0, 0);
                 if (j <= 5) read_frags(kt, 1, F1, j * 3, j == 5 ? 16 : j * 3 + 3);
                 if (j == 7) {
@@ -268,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         splitk_store(g, T, acc);      // the slices are summed by splitk_reduce_kernel
         return;
     }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds);
+    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 32768]);   // after the barrier above
 }
 
 template <int EPI>

@@ -61,12 +61,12 @@ __device__ __forceinline__ h2 scale_h2(uint32_t code)
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs g)
 {
-    constexpr int kLdsBytes = kEpiBytes > 4 * kStageBytes ? kEpiBytes : 4 * kStageBytes;
+    constexpr int kLdsBytes = 4 * kStageBytes;
     __shared__ __attribute__((aligned(2048))) uint8_t lds[kLdsBytes];
     // [stage][operand] views of the flat array
     auto lds_ab = [&](int st, int op) -> uint8_t * { return &lds[(st * 2 + op) * kStageBytes]; };
-    __shared__ float lds_sa[kBM];
-    __shared__ float lds_sw[kBN];
+    __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
+    __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -77,9 +77,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     const int64_t k_end = min(g.K, k_begin + g.k_chunk);
     const int nk = (int)((k_end - k_begin + kBK - 1) / kBK);
 
-    // 2^14 undoes the two 2^-7 operand offsets of the f16 decode.
-    lds_sa[tid] = 16384.0f * *g.tscale_a * *g.tscale_w;
-    lds_sw[tid] = 1.0f;
+    stage_scales<EPI, SPG_FMT_NVFP4>(g, T, lds_sa, lds_sw);
 
     // ---- this thread stages row tid of the A tile and row tid of the W tile
     const int64_t G = g.K / 16;
@@ -126,10 +124,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     Acc acc;
     zero_acc(acc);
     const int l32 = lane & 31, khalf = lane >> 5;
-    auto brow = [&](int ni) -> uint32_t {
-        if (EPI == SPG_EPI_SWIGLU) return (ni < 2 ? wn * 64 + ni * 32 : 128 + wn * 64 + (ni - 2) * 32) + l32;
-        return wn * 128 + ni * 32 + l32;
-    };
+    auto brow = [&](int ni) -> uint32_t { return (uint32_t)wtile_row0<EPI>(wn, ni) + l32; };
     auto compute = [&](int st) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -146,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+                    acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[ni], af[mi], acc[ni][mi], 0, 0, 0);
         }
     };
 
@@ -167,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
         splitk_store(g, T, acc);      // the slices are summed by splitk_reduce_kernel
         return;
     }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds);
+    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 32768]);   // after the barrier above
 }
 
 template <int EPI>
