@@ -209,7 +209,9 @@ typedef struct spg_plan {
     int32_t bm, bn, bk;      /* workgroup tile (output rows, weight rows, K)  */
     int32_t split_k;         /* K partitions reduced through the workspace    */
     int64_t tiles;           /* output tiles over the whole batch             */
-    int64_t workgroups;      /* tiles * split_k                               */
+    int64_t workgroups;      /* workgroups launched: tiles * split_k, or at  */
+                             /* most one per compute unit when the FP8 kernel */
+                             /* runs an unsplit product persistently         */
     int32_t kernel;          /* internal kernel id                            */
 } spg_plan;
 

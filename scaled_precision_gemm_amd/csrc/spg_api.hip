@@ -83,13 +83,18 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     const int64_t nout = n_out_of(d, epi);
     p->bm = (int32_t)kTile;
     p->bn = (int32_t)kTile;   // weight rows per tile (SWIGLU: 128 gate + 128 up)
-    p->bk = 64;   // K elements per pipeline stage (both kernels)
+    p->bk = d->format == SPG_FMT_NVFP4 ? 64 : 128;   // K elements per pipeline stage
     const int64_t tiles_m = cdiv(d->M, kTile);
     const int64_t tiles_n = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
     p->tiles = tiles_m * tiles_n * d->batch;
     p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->K, units, p->bk) : 1;
-    p->workgroups = p->tiles * p->split_k;
     p->kernel = d->format == SPG_FMT_NVFP4 ? 1 : 0;
+    // The FP8 kernel runs unsplit products with two or more K stages
+    // persistently: one workgroup per compute unit walking its tiles.
+    if (p->kernel == 0 && p->split_k == 1 && cdiv(d->K, p->bk) >= 2)
+        p->workgroups = p->tiles < units ? p->tiles : units;
+    else
+        p->workgroups = p->tiles * p->split_k;
 }
 
 size_t plan_workspace(const spg_plan *p)

@@ -278,112 +278,131 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
 // the output leaves in whole rows.  Stores cost about one cycle per distinct
 // cache line an instruction touches: in the accumulator layout one store
 // instruction covers 32 token rows (32 lines), after the transpose it covers
-// 4 whole 256-byte row segments (measured on 8192 x 8192 bf16: 3.3 TB/s for
+// 8 whole 128-byte row segments (measured on 8192 x 8192 bf16: 3.3 TB/s for
 // the former pattern, 6.5 TB/s for whole rows).
 //
-// Each wave stages only its own 128 x 128 quadrant (SWIGLU: 128 x 64 outputs)
-// in a private 32 KiB region, so no workgroup barrier is involved.  Row r of
-// the region holds the wave's outputs of token row wm * 128 + r; its 16-byte
-// chunks are XOR-swizzled so that both the fragment-order writes (one row per
-// lane) and the row-order reads spread over all 64 banks:
-//   256-byte rows: chunk c at c ^ (r & 15);  128-byte rows: c ^ ((r >> 1) & 7)
-//  1. ADD: the residual quadrant is copied into the region row by row;
+// Each wave works through its 128 x 128 quadrant (SWIGLU: 128 x 64 outputs)
+// in passes of 32 token rows x 64 columns, staged in a private 4 KiB region,
+// so no workgroup barrier is involved.  Row r of the region holds 128 bytes
+// of token row (pass base + r); its 16-byte chunks are XOR-swizzled (chunk c
+// at c ^ ((r >> 1) & 7)) so that both the fragment-order writes (one row per
+// lane) and the row-order reads spread over all 64 banks.  Per pass:
+//  1. ADD: the residual block is copied into the region row by row;
 //  2. every lane forms v = acc * lds_sa * lds_sw (+ residual read back from
 //     the region in fp32, one rounding; SWIGLU silu(gate) * up) and writes the
 //     bf16 results in place (8 bytes per register group);
-//  3. the region leaves as 16-byte chunks of whole rows.
-// `region` must be 32 KiB, 16-byte aligned, and free of other use; the
-// caller's LDS stage buffers are reused after the main loop.
+//  3. the region leaves as 16-byte chunks of whole 128-byte row segments.
+// `region` is this wave's 4 KiB, 16-byte aligned, used by nothing else.
+constexpr int kEpiRegionBytes = 4 * 4096;   // per workgroup
+
 template <int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
                                          const float *lds_sw, uint8_t *region)
 {
     constexpr bool SW = EPI == SPG_EPI_SWIGLU;
-    constexpr int RB = SW ? 128 : 256;        // region row bytes
-    constexpr int NCH = RB / 16;              // chunks per row
-    constexpr int NX = SW ? 2 : 4;            // W blocks producing outputs
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NP = SW ? 1 : 2;            // 64-column passes per 32-row block
+    int lane = threadIdx.x & 63;
+    // Opaque to the optimizer: lane-derived offsets are recomputed per call
+    // instead of being hoisted (and spilled) across a persistent tile loop.
+    asm volatile("" : "+v"(lane));
+    const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
     const EpiOut o = epi_out<EPI>(g, T);
-    const int64_t row0 = T.m0 + wm * 128;                       // first token row of the quadrant
-    const int64_t col0 = T.c0 + (SW ? wn * 64 : wn * 128);      // first output column
-    const int64_t rows_valid = min((int64_t)128, g.M - row0);
-    const int64_t cols_valid = min((int64_t)(RB / 2), o.nvalid - col0);
-    auto phys = [](int r, int c) -> int { return SW ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
     const bool vec16 = ((((uintptr_t)o.out) & 15) == 0) && ((g.ldo & 7) == 0);
+    const bool rvec = EPI == SPG_EPI_ADD && ((((uintptr_t)o.res) & 15) == 0) && ((g.ldr & 7) == 0);
+    auto phys = [](int r, int c) -> int { return c ^ ((r >> 1) & 7); };
+    const int rr = lane >> 3, rc = lane & 7;  // row-order lane position: 8 rows x 8 chunks
+    // 32-bit element offsets inside a 32-row block (ldo, ldr < 2^26)
+    const uint32_t ldo = (uint32_t)g.ldo, ldr = (uint32_t)g.ldr;
 
-    // 1. residual quadrant -> region
-    if (EPI == SPG_EPI_ADD) {
-        const bool rvec = ((((uintptr_t)o.res) & 15) == 0) && ((g.ldr & 7) == 0);
-#pragma unroll 4
-        for (int it = 0; it < 128 * NCH / 64; ++it) {
-            const int r = it * (64 / NCH) + lane / NCH, c = lane % NCH;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (r < rows_valid && c * 8 < cols_valid) {
-                const uint16_t *src = o.res + (row0 + r) * g.ldr + col0 + c * 8;
-                if (rvec && c * 8 + 8 <= cols_valid) {
-                    v = *reinterpret_cast<const uint4 *>(src);
-                } else {
-                    uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                    for (int j = 0; j < 8; ++j)
-                        if (c * 8 + j < cols_valid) h[j] = src[j];
-                    v = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
-                }
-            }
-            *reinterpret_cast<uint4 *>(region + r * RB + phys(r, c) * 16) = v;
-        }
-    }
-
-    // 2. accumulators -> bf16 in the region (fragment order)
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
-        const int r = y * 32 + l32;
-        const float sa = lds_sa[wm * 128 + r];
+        const int64_t row0 = T.m0 + wm * 128 + y * 32;
+        const int rows_valid = (int)min((int64_t)32, g.M - row0);
+        if (rows_valid <= 0) break;                                 // uniform per wave
+        const float sa = lds_sa[wm * 128 + y * 32 + l32];
 #pragma unroll
-        for (int x = 0; x < NX; ++x) {
-            const int w0 = wtile_row0<EPI>(wn, x);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int wl = w0 + q * 8 + khalf * 4;
-                const v4f sw = *reinterpret_cast<const v4f *>(lds_sw + wl);
-                const v4f swu = SW ? *reinterpret_cast<const v4f *>(lds_sw + 128 + wl) : v4f{};
-                uint2 *dst = reinterpret_cast<uint2 *>(region + r * RB + phys(r, x * 4 + q) * 16 + khalf * 8);
-                float v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int e = q * 4 + j;
-                    if (SW) {
-                        const float vg = acc[x][y][e] * sa * sw[j];
-                        const float vu = acc[x + 2][y][e] * sa * swu[j];
-                        v[j] = silu_f32(vg) * vu;
-                    } else {
-                        v[j] = acc[x][y][e] * sa * sw[j];
-                    }
-                }
-                if (EPI == SPG_EPI_ADD) {
-                    const uint2 rv = *dst;
-                    v[0] += bf16_lo(rv.x);
-                    v[1] += bf16_hi(rv.x);
-                    v[2] += bf16_lo(rv.y);
-                    v[3] += bf16_hi(rv.y);
-                }
-                *dst = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
-        }
-    }
+        for (int p = 0; p < NP; ++p) {
+            const int64_t col0 = T.c0 + (SW ? wn * 64 : wn * 128 + p * 64);
+            const int cols_valid = (int)min((int64_t)64, o.nvalid - col0);
+            if (cols_valid <= 0) break;                             // uniform per wave
+            // keep each pass's loads inside the pass (hoisting them all would
+            // need more registers than the accumulators leave)
+            __builtin_amdgcn_sched_barrier(0);
+            uint16_t *const obase = o.out + row0 * g.ldo + col0;   // uniform
 
-    // 3. region -> global, 16-byte chunks of whole rows
-#pragma unroll 4
-    for (int it = 0; it < 128 * NCH / 64; ++it) {
-        const int r = it * (64 / NCH) + lane / NCH, c = lane % NCH;
-        if (r >= rows_valid || c * 8 >= cols_valid) continue;
-        const uint4 v = *reinterpret_cast<const uint4 *>(region + r * RB + phys(r, c) * 16);
-        uint16_t *dst = o.out + (row0 + r) * g.ldo + col0 + c * 8;
-        if (vec16 && c * 8 + 8 <= cols_valid) {
-            *reinterpret_cast<uint4 *>(dst) = v;
-        } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int j = 0; j < 8 && c * 8 + j < cols_valid; ++j) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+            // 1. residual block -> region
+            if (EPI == SPG_EPI_ADD) {
+                const uint16_t *const rbase = o.res + row0 * g.ldr + col0;
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int r = it * 8 + rr;
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (r < rows_valid && rc * 8 < cols_valid) {
+                        const uint16_t *src = rbase + (uint32_t)(r * ldr + rc * 8);
+                        if (rvec && rc * 8 + 8 <= cols_valid) {
+                            v = *reinterpret_cast<const uint4 *>(src);
+                        } else {
+                            uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                            for (int j = 0; j < 8; ++j)
+                                if (rc * 8 + j < cols_valid) h[j] = src[j];
+                            v = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
+                                           h[6] | h[7] << 16);
+                        }
+                    }
+                    *reinterpret_cast<uint4 *>(region + r * 128 + phys(r, rc) * 16) = v;
+                }
+            }
+
+            // 2. accumulators -> bf16 in the region (fragment order)
+#pragma unroll
+            for (int xx = 0; xx < 2; ++xx) {
+                const int x = SW ? xx : p * 2 + xx;
+                const int w0 = wtile_row0<EPI>(wn, x);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int wl = w0 + q * 8 + khalf * 4;
+                    const v4f sw = *reinterpret_cast<const v4f *>(lds_sw + wl);
+                    const v4f swu = SW ? *reinterpret_cast<const v4f *>(lds_sw + 128 + wl) : v4f{};
+                    uint2 *dst = reinterpret_cast<uint2 *>(region + l32 * 128 + phys(l32, xx * 4 + q) * 16 + khalf * 8);
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e = q * 4 + j;
+                        if (SW) {
+                            const float vg = acc[x][y][e] * sa * sw[j];
+                            const float vu = acc[x + 2][y][e] * sa * swu[j];
+                            v[j] = silu_f32(vg) * vu;
+                        } else {
+                            v[j] = acc[x][y][e] * sa * sw[j];
+                        }
+                    }
+                    if (EPI == SPG_EPI_ADD) {
+                        const uint2 rv = *dst;
+                        v[0] += bf16_lo(rv.x);
+                        v[1] += bf16_hi(rv.x);
+                        v[2] += bf16_lo(rv.y);
+                        v[3] += bf16_hi(rv.y);
+                    }
+                    *dst = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+
+            // 3. region -> global, 16-byte chunks of whole row segments
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int r = it * 8 + rr;
+                if (r >= rows_valid || rc * 8 >= cols_valid) continue;
+                const uint4 v = *reinterpret_cast<const uint4 *>(region + r * 128 + phys(r, rc) * 16);
+                uint16_t *dst = obase + (uint32_t)(r * ldo + rc * 8);
+                if (vec16 && rc * 8 + 8 <= cols_valid) {
+                    *reinterpret_cast<uint4 *>(dst) = v;
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                    for (int j = 0; j < 8 && rc * 8 + j < cols_valid; ++j)
+                        dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+                }
+            }
         }
     }
 }

@@ -33,6 +33,8 @@
 //    first MFMA operand, so a lane holds four adjacent output columns).
 #include "spg_gemm_common.h"
 
+#include <type_traits>
+
 namespace spg {
 
 namespace {
@@ -42,7 +44,6 @@ constexpr int kBK = 128;                      // K bytes (E4M3 elements) per sta
 constexpr int kOp = kBM * kBK;                // one operand, one stage: 32 KiB
 constexpr int kSlot = 2 * kOp;                // A + W of one stage: 64 KiB
 constexpr uint32_t kOOB = 0x80000000u;        // buffer offset past any range
-constexpr int kLdsBytes = 2 * kSlot;
 
 // Raw buffer resource: base, no stride, `bytes` in range, dword format bits.
 __device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
@@ -89,20 +90,30 @@ __device__ __forceinline__ v8i op(const uint4 (&h)[2])
     return v8i{(int)h[0].x, (int)h[0].y, (int)h[0].z, (int)h[0].w, (int)h[1].x, (int)h[1].y, (int)h[1].z, (int)h[1].w};
 }
 
-template <int EPI, int SMODE>
+// Copy sources of one tile: buffer resources over its A rows and its two
+// 128-row W halves (each wave copies 64 rows of A and 64 rows of one W half).
+struct CopySrc {
+    v4i a, w;
+};
+
+template <int EPI, int SMODE, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 {
-    __shared__ __attribute__((aligned(2048))) uint8_t lds[kLdsBytes];
-    __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
-    __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+    __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlot + kEpiRegionBytes];
+    __shared__ __attribute__((aligned(16))) float lds_scale[2][2][kBM];   // [tile parity][a / w][row]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int wm = wave >> 1, wn = wave & 1;
-    const Tile T = tile_of<EPI>(g);
 
-    const uint8_t *A = g.A + (g.stride_a ? T.b * g.stride_a : 0);
-    const uint8_t *W = g.W + (g.stride_w ? T.b * g.stride_w : 0);
+    // Tiles of this workgroup: virtual workgroup ids blockIdx.x + i * gridDim.x
+    // (a persistent grid of one workgroup per compute unit walks the same
+    // XCD-aware order a one-tile-per-workgroup launch would).
+    const int64_t total = g.batch * g.tiles_m * g.tiles_n;
+    const int ntile = (int)((total - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x);
+    auto tile_i = [&](int i) -> Tile {
+        return tile_from_id<EPI>(g, xcd_remap((int64_t)blockIdx.x + (int64_t)i * gridDim.x, total));
+    };
 
     const int split = blockIdx.y;
     const int64_t k_begin = (int64_t)split * g.k_chunk;
@@ -110,160 +121,241 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     const int nk = (int)((k_end - k_begin + kBK - 1) / kBK);
     const int64_t Nh = g.N / 2;
 
-    // scales into LDS (read by the epilogue after the main loop's barriers)
-    stage_scales<EPI, SMODE>(g, T, lds_sa, lds_sw);
-
     // ---- copy setup -----------------------------------------------------------
     // Wave w fills tile rows [64 w, 64 w + 64) of A and of W: eight 8-row
     // blocks each, one 1 KiB copy instruction per block.  In a block lane L
     // owns LDS slot L: row L / 8, physical chunk L % 8, so it fetches logical
     // chunk (L % 8) ^ ((row >> 1) & 7); for 8-row blocks at row 64 w + 8 i
     // that XOR term is 4 (i & 1) + L / 16 (mod 8), so two offsets per operand
-    // serve all eight blocks, the row step going into the scalar offset.
-    const uint32_t rib = lane >> 3, pchunk = lane & 7;
-    const uint32_t c_even = pchunk ^ ((lane >> 4) & 7u);
-    const uint32_t c_odd = pchunk ^ ((4u + (lane >> 4)) & 7u);
-    const int64_t a_rows = min((int64_t)kBM, g.M - T.m0);
-    const v4i rs_a = make_rsrc(A + T.m0 * g.lda, (uint32_t)(a_rows * g.lda));
-    // W: waves 0,1 the first 128 tile rows, waves 2,3 the second 128 (SWIGLU:
-    // gate rows n0.., up rows N/2 + n0..)
-    int64_t w_first, w_rows;
-    if (EPI == SPG_EPI_SWIGLU) {
-        w_rows = min((int64_t)128, Nh - T.n0);
-        w_first = (wave < 2 ? T.n0 : Nh + T.n0);
-    } else {
-        const int64_t half0 = T.n0 + (wave < 2 ? 0 : 128);
-        w_rows = min((int64_t)128, g.N - half0);
-        w_first = half0;
-    }
-    w_rows = max(w_rows, (int64_t)0);
-    const v4i rs_w = make_rsrc(W + w_first * g.ldw, (uint32_t)(w_rows * g.ldw));
-    const uint32_t ra0 = (uint32_t)(wave * 64) + rib;            // A tile row of block 0
-    const uint32_t rw0 = (uint32_t)((wave & 1) * 64) + rib;      // row within the W half
-    const uint32_t va_e = ra0 * (uint32_t)g.lda + c_even * 16u, va_o = ra0 * (uint32_t)g.lda + c_odd * 16u;
-    const uint32_t vw_e = rw0 * (uint32_t)g.ldw + c_even * 16u, vw_o = rw0 * (uint32_t)g.ldw + c_odd * 16u;
+    // serve all eight blocks.
+    auto make_src = [&](const Tile &T) -> CopySrc {
+        const uint8_t *A = g.A + (g.stride_a ? T.b * g.stride_a : 0);
+        const uint8_t *W = g.W + (g.stride_w ? T.b * g.stride_w : 0);
+        const int64_t a_rows = min((int64_t)kBM, g.M - T.m0);
+        // W: waves 0,1 the first 128 tile rows, waves 2,3 the second 128
+        // (SWIGLU: gate rows n0.., up rows N/2 + n0..)
+        int64_t w_first, w_rows;
+        if (EPI == SPG_EPI_SWIGLU) {
+            w_rows = min((int64_t)128, Nh - T.n0);
+            w_first = (wave < 2 ? T.n0 : Nh + T.n0);
+        } else {
+            const int64_t half0 = T.n0 + (wave < 2 ? 0 : 128);
+            w_rows = min((int64_t)128, g.N - half0);
+            w_first = half0;
+        }
+        w_rows = max(w_rows, (int64_t)0);
+        return CopySrc{make_rsrc(A + T.m0 * g.lda, (uint32_t)(a_rows * g.lda)),
+                       make_rsrc(W + w_first * g.ldw, (uint32_t)(w_rows * g.ldw))};
+    };
+    // Lane-dependent copy and fragment offsets.  They are recomputed for every
+    // tile from an opaque copy of the lane id, so that they are dead (not
+    // kept in registers, nor spilled) while a tile's epilogue runs.
+    struct LaneCtx {
+        uint32_t c_even, c_odd, va_e, va_o, vw_e, vw_o;
+        uint32_t foff[2][2];
+    };
+    auto lane_ctx = [&]() -> LaneCtx {
+        int ln = tid & 63;
+        asm volatile("" : "+v"(ln));
+        LaneCtx c;
+        const uint32_t rib = (uint32_t)ln >> 3, pchunk = (uint32_t)ln & 7;
+        c.c_even = pchunk ^ (((uint32_t)ln >> 4) & 7u);
+        c.c_odd = pchunk ^ ((4u + ((uint32_t)ln >> 4)) & 7u);
+        const uint32_t ra0 = (uint32_t)(wave * 64) + rib;        // A tile row of block 0
+        const uint32_t rw0 = (uint32_t)((wave & 1) * 64) + rib;  // row within the W half
+        c.va_e = ra0 * (uint32_t)g.lda + c.c_even * 16u;
+        c.va_o = ra0 * (uint32_t)g.lda + c.c_odd * 16u;
+        c.vw_e = rw0 * (uint32_t)g.ldw + c.c_even * 16u;
+        c.vw_o = rw0 * (uint32_t)g.ldw + c.c_odd * 16u;
+        // Fragment rows are 32-row aligned, so (row >> 1) & 7 depends on the
+        // lane only: every fragment of a lane uses the same chunk offsets.
+        const uint32_t l32 = (uint32_t)ln & 31, khalf = (uint32_t)ln >> 5;
+        const uint32_t fx = (l32 >> 1) & 7u;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                c.foff[ks][h] = l32 * kBK + ((((uint32_t)ks * 4 + khalf * 2 + (uint32_t)h) ^ fx) << 4);
+        return c;
+    };
+    LaneCtx L = lane_ctx();
     const uint32_t lds_base =
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&lds[0];
 
-    // Copy instruction idx (0..15) of stage kt: 8-row block idx >> 1 of A
-    // (idx even) or of W (idx odd).
-    auto issue_one = [&](int kt, int idx) {
-        const int i = idx >> 1;
+    // Per-stage copy plan: source tile, scalar K offset and the per-lane base
+    // offsets of the even / odd 8-row blocks (kOOB where a lane's 16 bytes lie
+    // past K, or for a stage that does not exist: such copies read zeros into
+    // a slot nobody reads again, which keeps every wait count uniform).
+    struct StageCopy {
+        v4i ra, rw;
+        uint32_t soff, a_e, a_o, w_e, w_o;
+    };
+    auto plan_stage = [&](const CopySrc &src, int kt, bool exists) -> StageCopy {
         const int64_t k0 = k_begin + (int64_t)kt * kBK;
         const bool full = k0 + kBK <= k_end;
-        const bool odd = i & 1;
-        const bool in = full || (k0 + (int64_t)(odd ? c_odd : c_even) * 16 < k_end);
-        const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
-            (int)(lds_base + (uint32_t)((kt & 1) * kSlot) + (uint32_t)(wave * 64 * kBK)));
+        const bool in_e = exists && (full || k0 + (int64_t)L.c_even * 16 < k_end);
+        const bool in_o = exists && (full || k0 + (int64_t)L.c_odd * 16 < k_end);
         // The range check of a raw buffer access covers the VGPR offset only,
         // so the row step stays in the VGPR offset (rows past the valid range
         // then read as zero) and only k0, which never crosses a row, goes in
         // the scalar offset.
-        const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)k0);
-        if ((idx & 1) == 0) {
-            const uint32_t va = in ? (odd ? va_o : va_e) + (uint32_t)(8 * i) * (uint32_t)g.lda : kOOB;
-            dma16(la + (uint32_t)(i * 8 * kBK), va, rs_a, soff);
-        } else {
-            const uint32_t vw = in ? (odd ? vw_o : vw_e) + (uint32_t)(8 * i) * (uint32_t)g.ldw : kOOB;
-            dma16(la + (uint32_t)kOp + (uint32_t)(i * 8 * kBK), vw, rs_w, soff);
-        }
+        StageCopy c;
+        c.ra = src.a;
+        c.rw = src.w;
+        c.soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)(exists ? k0 : 0));
+        c.a_e = in_e ? L.va_e : kOOB;
+        c.a_o = in_o ? L.va_o : kOOB;
+        c.w_e = in_e ? L.vw_e : kOOB;
+        c.w_o = in_o ? L.vw_o : kOOB;
+        return c;
     };
-    auto issue_all = [&](int kt) {
-        if (kt >= nk) return;
-#pragma unroll
-        for (int idx = 0; idx < 16; ++idx) issue_one(kt, idx);
+    // Copy instruction idx (0..15) of a stage into LDS slot `slot`: 8-row
+    // block idx >> 1 of A (idx even) or of W (idx odd).  kOOB plus the row
+    // step stays past any buffer range (ranges are at most 2^31 bytes).
+    auto issue_one = [&](const StageCopy &c, int slot, int idx) {
+        const int i = idx >> 1;
+        const bool odd = i & 1;
+        const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(lds_base + (uint32_t)(slot * kSlot) + (uint32_t)(wave * 64 * kBK)));
+        if ((idx & 1) == 0)
+            dma16(la + (uint32_t)(i * 8 * kBK), (odd ? c.a_o : c.a_e) + (uint32_t)(8 * i) * (uint32_t)g.lda, c.ra, c.soff);
+        else
+            dma16(la + (uint32_t)kOp + (uint32_t)(i * 8 * kBK), (odd ? c.w_o : c.w_e) + (uint32_t)(8 * i) * (uint32_t)g.ldw,
+                  c.rw, c.soff);
     };
 
     // ---- fragment addressing ---------------------------------------------------
-    // Fragment rows are 32-row aligned, so (row >> 1) & 7 depends on the lane
-    // only: every fragment of a lane uses the same chunk offsets.
-    const int l32 = lane & 31, khalf = lane >> 5;
-    const uint32_t fx = ((uint32_t)l32 >> 1) & 7u;
-    uint32_t foff[2][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            foff[ks][h] = (uint32_t)l32 * kBK + ((((uint32_t)(ks * 4 + khalf * 2 + h)) ^ fx) << 4);
     auto brow0 = [&](int ni) -> uint32_t { return (uint32_t)wtile_row0<EPI>(wn, ni); };
-    // Fragment half-reads r0 .. r1-1 of sub-step ks of stage kt: index 0..7
-    // are the B fragments (ni = r / 2, half r % 2), 8..15 the A fragments.
-    auto read_frags = [&](int kt, int ks, Frags &F, int r0, int r1) {
-        const uint8_t *la = &lds[(kt & 1) * kSlot];
+    // Fragment half-reads r0 .. r1-1 of sub-step ks from LDS slot `slot`:
+    // index 0..7 are the W fragments (ni = r / 2, half r % 2), 8..15 the A
+    // fragments.
+    auto read_frags = [&](int slot, int ks, Frags &F, int r0, int r1) {
+        const uint8_t *la = &lds[slot * kSlot];
         const uint8_t *lb = la + kOp;
 #pragma unroll
         for (int r = r0; r < r1; ++r) {
             const int h = r & 1;
             if (r < 8) {
                 const int ni = r >> 1;
-                F.b[ni][h] = *reinterpret_cast<const uint4 *>(lb + brow0(ni) * kBK + foff[ks][h]);
+                F.b[ni][h] = *reinterpret_cast<const uint4 *>(lb + brow0(ni) * kBK + L.foff[ks][h]);
             } else {
                 const int mi = (r - 8) >> 1;
-                F.a[mi][h] = *reinterpret_cast<const uint4 *>(la + (uint32_t)(wm * 128 + mi * 32) * kBK + foff[ks][h]);
+                F.a[mi][h] = *reinterpret_cast<const uint4 *>(la + (uint32_t)(wm * 128 + mi * 32) * kBK + L.foff[ks][h]);
             }
         }
     };
 
-    Acc acc;
-    zero_acc(acc);
+    Tile Tc = tile_i(0), Tn = Tc;
+    CopySrc sc = make_src(Tc), sn = sc;
+    bool has_next = ntile > 1;
+    if (has_next) {
+        Tn = tile_i(1);
+        sn = make_src(Tn);
+    }
+    stage_scales<EPI, SMODE>(g, Tc, lds_scale[0][0], lds_scale[0][1]);
 
     // One stage = 32 MFMAs (sub-step 0 from F0, sub-step 1 from F1) in a
     // fixed order, with the other work of the stage slotted between them so
     // that the single wave per SIMD never stalls its MFMA issue for long:
     //   after MFMA 0..5   : the 16 fragment reads of F1 (sub-step 1, this stage)
-    //   after MFMA 7      : F1 complete -> barrier: slot kt & 1 is free
-    //   after MFMA 8..23  : one copy instruction each for stage kt + 2
-    //   after MFMA 23     : own copy of stage kt + 1 landed -> barrier: published
-    //   after MFMA 24..31 : the 16 fragment reads of F0 (sub-step 0, stage kt+1)
+    //   after MFMA 7      : F1 complete -> barrier: the stage's slot is free
+    //   after MFMA 8..23  : one copy instruction each for the stage after next
+    //   after MFMA 23     : own copy of the next stage landed -> barrier: published
+    //   after MFMA 24..31 : the 16 fragment reads of F0 (sub-step 0, next stage)
+    // "Next" runs on into the following tile of the workgroup, whose first two
+    // stages are thus copied during the last two stages of the current tile
+    // and land while its epilogue runs.  Stages alternate between the two
+    // slots over the whole sequence (parity G).
     Frags F0, F1;
-    if (nk > 0) {
-        issue_all(0);
-        issue_all(1);
-        if (nk > 1) wait_vmem<16>();
-        else wait_vmem<0>();
+    {
+        // stages 0 and 1 of the sequence (stage 1 is the next tile's first
+        // when this tile has a single stage)
+        const StageCopy c0 = plan_stage(sc, 0, nk > 0);
+        const StageCopy c1 = nk > 1 ? plan_stage(sc, 1, true) : plan_stage(sn, 0, has_next);
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) issue_one(c0, 0, idx);
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) issue_one(c1, 1, idx);
+        wait_vmem<16>();
         block_barrier();                       // stage 0 published
         read_frags(0, 0, F0, 0, 16);
-        for (int kt = 0; kt < nk; ++kt) {
-            const bool next = kt + 1 < nk, next2 = kt + 2 < nk;
+    }
+    int G = 0;                                 // stage counter over all tiles (slot = G & 1)
+    // One stage; the last stage of a tile does not prefetch the next stage's
+    // F0 (it is read after the epilogue, so no fragment registers are live
+    // across it).
+    auto stage = [&](Acc &acc, int kt, auto last_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+        const int slot = G & 1;
+        // stage G + 2: this tile's kt + 2, else the next tile's kt + 2 - nk
+        const bool here = kt + 2 < nk;
+        const StageCopy c2 = plan_stage(here ? sc : sn, here ? kt + 2 : kt + 2 - nk,
+                                        here || (has_next && kt + 2 - nk < nk));
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const int mi = (j & 15) >> 2, ni = j & 3;
-                const Frags &F = j < 16 ? F0 : F1;
-                acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(F.b[ni]), op(F.a[mi]), acc[ni][mi],
-                                                                              0, 0, 0, 0, 0, 0);
-                if (j <= 5) read_frags(kt, 1, F1, j * 3, j == 5 ? 16 : j * 3 + 3);
-                if (j == 7) {
-                    wait_lds();
-                    block_barrier();
-                }
-                if (j >= 8 && j <= 23 && next2) issue_one(kt + 2, j - 8);
-                if (j == 23 && next) {
-                    if (next2) wait_vmem<16>();
-                    else wait_vmem<0>();
-                    block_barrier();
-                }
-                if (j >= 24 && next) read_frags(kt + 1, 0, F0, (j - 24) * 2, (j - 24) * 2 + 2);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 32; ++j) {
+            const int mi = (j & 15) >> 2, ni = j & 3;
+            const Frags &F = j < 16 ? F0 : F1;
+            acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(F.b[ni]), op(F.a[mi]), acc[ni][mi],
+                                                                          0, 0, 0, 0, 0, 0);
+            if (j <= 5) read_frags(slot, 1, F1, j * 3, j == 5 ? 16 : j * 3 + 3);
+            if (j == 7) {
+                wait_lds();
+                block_barrier();
             }
+            if (j >= 8 && j <= 23) issue_one(c2, slot, j - 8);
+            if (j == 23) {
+                wait_vmem<16>();               // stage G + 1 landed (stage G + 2 in flight)
+                block_barrier();
+            }
+            if (!LAST && j >= 24) read_frags(slot ^ 1, 0, F0, (j - 24) * 2, (j - 24) * 2 + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        ++G;
+    };
+    for (int i = 0; i < ntile; ++i) {
+        Acc acc;
+        zero_acc(acc);
+        for (int kt = 0; kt + 1 < nk; ++kt) stage(acc, kt, std::false_type{});
+        if (nk > 0) stage(acc, nk - 1, std::true_type{});
+
+        if (SPLIT) {
+            splitk_store(g, Tc, acc);          // the slices are summed by splitk_reduce_kernel
+        } else {
+            epilogue<EPI>(g, Tc, acc, lds_scale[i & 1][0], lds_scale[i & 1][1],
+                          &lds[2 * kSlot + wave * (kEpiRegionBytes / 4)]);
+        }
+        if (i + 1 < ntile) {
+            L = lane_ctx();
+            read_frags(G & 1, 0, F0, 0, 16);   // the next tile's stage 0, published at the last barrier
+            Tc = Tn;
+            sc = sn;
+            has_next = i + 2 < ntile;
+            if (has_next) {
+                Tn = tile_i(i + 2);
+                sn = make_src(Tn);
+            }
+            // Every wave has passed this tile's barriers, so none still reads
+            // the scales of tile i - 1 that share this buffer.
+            stage_scales<EPI, SMODE>(g, Tc, lds_scale[(i + 1) & 1][0], lds_scale[(i + 1) & 1][1]);
         }
     }
-    __syncthreads();
-
-    if (g.split_k > 1) {
-        splitk_store(g, T, acc);      // the slices are summed by splitk_reduce_kernel
-        return;
-    }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 32768]);   // after the barrier above
+    wait_vmem<0>();   // no copy into LDS may still be in flight when the workgroup ends
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 {
-    dim3 grid((unsigned)p.tiles, (unsigned)g.split_k, 1);
-    if (g.format == SPG_FMT_E4M3_ROW)
-        gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW><<<grid, kThreads, 0, s>>>(g);
-    else
-        gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR><<<grid, kThreads, 0, s>>>(g);
+    // p.workgroups: one per (tile, slice), or a persistent grid of at most
+    // one per compute unit for unsplit products with two or more K stages.
+    dim3 grid((unsigned)(p.workgroups / g.split_k), (unsigned)g.split_k, 1);
+    const bool split = g.split_k > 1;
+    if (g.format == SPG_FMT_E4M3_ROW) {
+        if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true><<<grid, kThreads, 0, s>>>(g);
+        else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false><<<grid, kThreads, 0, s>>>(g);
+    } else {
+        if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, true><<<grid, kThreads, 0, s>>>(g);
+        else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false><<<grid, kThreads, 0, s>>>(g);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && g.split_k > 1) e = launch_splitk_reduce(g, p.tiles, s);
     return e;

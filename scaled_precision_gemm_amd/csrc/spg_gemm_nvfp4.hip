@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
         splitk_store(g, T, acc);      // the slices are summed by splitk_reduce_kernel
         return;
     }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 32768]);   // after the barrier above
+    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
 }
 
 template <int EPI>

@@ -181,18 +181,28 @@ def test_quantizer_validation_errors(spg):
 # ---------------------------------------------------------------------------
 
 def test_plans_for_the_workloads(spg):
+    # 80 tiles on 256 units: a 3-way K split, one workgroup per (tile, slice)
     p = spg.gemm_plan(1024, 5120, 17408, "e4m3_row", "add")
-    assert (p["bm"], p["bn"], p["bk"], p["tiles"], p["split_k"]) == (256, 256, 64, 80, 3)
+    assert (p["bm"], p["bn"], p["bk"], p["tiles"], p["split_k"], p["workgroups"]) == (256, 256, 128, 80, 3, 240)
+    # unsplit FP8 products with two or more K stages: one persistent workgroup per unit
     p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu")
-    assert (p["tiles"], p["split_k"]) == (16 * 136, 1)
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (16 * 136, 1, 256)
+    p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu", units=304)
+    assert p["workgroups"] == 304
     p = spg.gemm_plan(128, 256, 512, "e4m3_row", "store")
-    assert (p["tiles"], p["split_k"]) == (1, 1)
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (1, 1, 1)
     p = spg.gemm_plan(512, 512, 512, "e4m3_tensor", "store", batch=64)
-    assert (p["tiles"], p["split_k"]) == (256, 1)
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (256, 1, 256)
     p = spg.gemm_plan(8192, 8192, 8192, "e4m3_tensor", "store")
-    assert (p["tiles"], p["split_k"]) == (1024, 1)
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (1024, 1, 256)
+    # a single K stage runs one workgroup per tile
+    p = spg.gemm_plan(4096, 4096, 128, "e4m3_tensor", "store")
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (256, 1, 256)
+    p = spg.gemm_plan(8192, 4096, 128, "e4m3_tensor", "store")
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (512, 1, 512)
+    # NVFP4 runs one workgroup per tile
     p = spg.gemm_plan(4096, 5120, 6144, "nvfp4", "add")
-    assert (p["tiles"], p["split_k"], p["bk"]) == (320, 1, 64)
+    assert (p["tiles"], p["split_k"], p["bk"], p["workgroups"]) == (320, 1, 64, 320)
 
 
 # ---------------------------------------------------------------------------
