@@ -133,8 +133,9 @@ int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t
  *   M, N, K  : A [M, K], W [N, K]; out [M, N], or [M, N/2] for SWIGLU
  *   batch    : number of independent products (>= 1)
  *   lda, ldw : row strides of A and W in bytes of codes (NVFP4: bytes of
- *              packed codes, >= K/2)
- *   ldo, ldr : row strides of out and residual in bf16 elements
+ *              packed codes, >= K/2); at most 2^23 (else SPG_EUNSUPPORTED)
+ *   ldo, ldr : row strides of out and residual in bf16 elements; below 2^26
+ *              (else SPG_EUNSUPPORTED)
  *   stride_* : batch strides (bytes for A/W codes, elements for out and
  *              residual); 0 broadcasts one matrix to every batch entry
  *              (AstrAI: "size-1 batches broadcast (stride 0)")

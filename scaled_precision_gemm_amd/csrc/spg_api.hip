@@ -53,6 +53,9 @@ int validate_desc(const spg_gemm_desc *d, int epi)
     if ((d->stride_a & 15) || (d->stride_w & 15)) return SPG_EINVAL;
     if (d->ldo < nout) return SPG_EINVAL;
     if (epi == SPG_EPI_ADD && d->ldr < nout) return SPG_EINVAL;
+    // the epilogue addresses a 32-row block with 32-bit byte offsets
+    if (d->ldo >= (INT64_C(1) << 26) || (epi == SPG_EPI_ADD && d->ldr >= (INT64_C(1) << 26)))
+        return SPG_EUNSUPPORTED;
     return SPG_OK;
 }
 

@@ -142,6 +142,18 @@ def test_gemm_nvfp4_batch_unsupported(spg):
     assert call_gemm(spg, d) == EUNSUP
 
 
+def test_gemm_stride_limits_unsupported(spg):
+    d = desc(spg, 64, 64, 64, 0)
+    d.lda = 1 << 24
+    assert call_gemm(spg, d) == EUNSUP
+    d = desc(spg, 64, 64, 64, 0)
+    d.ldo = 1 << 26
+    assert call_gemm(spg, d) == EUNSUP
+    d = desc(spg, 64, 64, 64, 0)
+    d.ldr = 1 << 26
+    assert call_gemm(spg, d, 1, res=FAKE2) == EUNSUP
+
+
 def test_gemm_workspace_too_small(spg):
     # T=1024 down-projection: 80 output tiles on 256 CUs -> a K split
     d = desc(spg, 1024, 5120, 17408, 0)
