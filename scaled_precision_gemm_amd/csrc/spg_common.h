@@ -28,36 +28,29 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 // rint(|v| * 2^9) (exact scaling, round-half-even) gives the code directly.
 __device__ __forceinline__ uint32_t encode_e4m3(float v)
 {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x43E00000u) {                 // |v| >= 448
-        code = 0x7Eu;
-    } else if (a < 0x3C800000u) {           // |v| < 2^-6
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    } else {
-        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        code = (r >> 20) - ((127u - 7u) << 3);
-    }
+    // All three cases are computed and one is selected: per-element branches
+    // would diverge inside a wave.
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const uint32_t normal = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+    // (clamped so the float -> integer conversion stays in range when unused)
+    const uint32_t sub = (uint32_t)__builtin_rintf(fminf(__uint_as_float(a) * 512.0f, 512.0f));   // |v| < 2^-6
+    uint32_t code = a < 0x3C800000u ? sub : normal;
+    code = a >= 0x43E00000u ? 0x7Eu : code;                                          // |v| >= 448
     return sign | code;
 }
 
 // binary32 -> E2M1 code (4 bits): nearest even, saturate at +-6, sign kept.
 __device__ __forceinline__ uint32_t encode_e2m1(float v)
 {
-    uint32_t u = __float_as_uint(v);
-    uint32_t sign = (u >> 28) & 0x8u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x40C00000u) {                 // |v| >= 6
-        code = 7u;
-    } else if (a < 0x3F800000u) {           // |v| < 1: multiples of 1/2
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
-    } else {
-        uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
-        code = (r >> 22) - ((127u - 1u) << 1);
-    }
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 28) & 0x8u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const uint32_t normal = ((a + 0x1FFFFFu + ((a >> 22) & 1u)) >> 22) - ((127u - 1u) << 1);
+    const uint32_t sub = (uint32_t)__builtin_rintf(fminf(__uint_as_float(a) * 2.0f, 16.0f));   // |v| < 1: halves
+    uint32_t code = a < 0x3F800000u ? sub : normal;
+    code = a >= 0x40C00000u ? 7u : code;                                            // |v| >= 6
     return sign | code;
 }
 

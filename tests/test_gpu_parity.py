@@ -43,7 +43,7 @@ def check_close(gpu_bits, y, S, what):
 # ---------------------------------------------------------------------------
 # quantize_rowwise
 # ---------------------------------------------------------------------------
-ROW_SHAPES = [(1, 16), (17, 48), (321, 512), (5, 1024), (3, 1040), (9, 2048), (4, 4096), (6, 8192),
+ROW_SHAPES = [(1, 16), (17, 48), (321, 512), (5, 1024), (3, 1040), (9, 2048), (4, 4096), (5, 5136), (6, 8192), (3, 12288),
               (2, 16384), (7, 17408), (3, 40000)]
 
 
@@ -86,6 +86,33 @@ def test_quantize_rowwise_every_bf16_value_with_unit_and_pow2_scales(spg):
         assert np.all(so == np.float32(2.0 ** k))
         assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
         assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_quantize_rowwise_every_amax_exponent(spg):
+    # one row per amax: every bf16 exponent (subnormal amax included), both
+    # sides of 2^-40 and the largest finite bf16; the rest of each row is
+    # random bit patterns of magnitude <= amax with random signs, so values
+    # of every size down to subnormals meet a scale of every size
+    rng = np.random.default_rng(77)
+    amax = [(e << 7) | int(rng.integers(0, 128)) for e in range(0, 255)]
+    amax += [0x0001, 0x007F, 0x0080, 0x2B7F, 0x2B80, 0x2B81, 0x7F7F]
+    K = 256
+    x = np.zeros((len(amax), K), np.uint16)
+    for i, a in enumerate(amax):
+        body = rng.integers(0, a + 1, size=K - 1).astype(np.uint16)
+        body |= (rng.integers(0, 2, size=K - 1) << 15).astype(np.uint16)
+        x[i, 0] = a
+        x[i, 1:] = body
+    q, s = spg.quantize_rowwise(dev(x))
+    qo, so = oracle.quantize_rowwise(x)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), qo)
+    # the per-tensor quantizer takes the same path with one scale per matrix
+    for i in (0, 3, 100, 200, len(amax) - 1):
+        qt, st = spg.quantize_tensor(dev(x[i:i + 1]))
+        qto, sto = oracle.quantize_tensor(x[i:i + 1])
+        assert np.array_equal(st.cpu().numpy().view(np.uint32), sto.view(np.uint32))
+        assert np.array_equal(qt.cpu().numpy(), qto)
 
 
 def test_quantize_rowwise_zero_and_signed_zero_rows(spg):
