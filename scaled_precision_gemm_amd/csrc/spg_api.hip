@@ -86,7 +86,9 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     const int64_t nout = n_out_of(d, epi);
     p->bm = (int32_t)kTile;
     p->bn = (int32_t)kTile;   // weight rows per tile (SWIGLU: 128 gate + 128 up)
-    p->bk = d->format == SPG_FMT_NVFP4 ? 64 : 128;   // K elements per pipeline stage
+    // K elements per pipeline stage: FP8 128; NVFP4 256 (copied straight into
+    // LDS) when K is a multiple of 256, else 64 (general path)
+    p->bk = d->format == SPG_FMT_NVFP4 ? (d->K % 256 == 0 ? 256 : 64) : 128;
     const int64_t tiles_m = cdiv(d->M, kTile);
     const int64_t tiles_n = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
     p->tiles = tiles_m * tiles_n * d->batch;

@@ -46,6 +46,43 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t wg, int64_t nwg)
     return base + idx;
 }
 
+// ---- direct-to-LDS copies and explicit waits (shared by the GEMM kernels) ----
+constexpr uint32_t kOOB = 0x80000000u;        // buffer offset past any range
+
+// Raw buffer resource: base, no stride, `bytes` in range, dword format bits.
+__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t b = (uint64_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from rsrc + voff + soff into LDS at lds_base + 16 * lane.
+// Issued as inline assembly so the compiler does not treat every later LDS
+// read as dependent on it; completion is awaited explicitly (vmcnt) before
+// the barrier that publishes the stage.
+__device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, v4i rsrc, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void block_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 struct Tile {

@@ -43,41 +43,6 @@ using namespace gemm;
 constexpr int kBK = 128;                      // K bytes (E4M3 elements) per stage
 constexpr int kOp = kBM * kBK;                // one operand, one stage: 32 KiB
 constexpr int kSlot = 2 * kOp;                // A + W of one stage: 64 KiB
-constexpr uint32_t kOOB = 0x80000000u;        // buffer offset past any range
-
-// Raw buffer resource: base, no stride, `bytes` in range, dword format bits.
-__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t b = (uint64_t)base;
-    v4i r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from rsrc + voff + soff into LDS at lds_base + 16 * lane.
-// Issued as inline assembly so the compiler does not treat every later LDS
-// read as dependent on it; completion is awaited explicitly (vmcnt) before
-// the barrier that publishes the stage.
-__device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, v4i rsrc, uint32_t soff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
-__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void block_barrier()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 // A lane's 32-byte MFMA operand is kept as two 16-byte halves (the two LDS
 // reads that fetch it may be issued at different points of the schedule).

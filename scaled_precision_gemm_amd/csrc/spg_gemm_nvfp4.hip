@@ -58,8 +58,10 @@ __device__ __forceinline__ h2 scale_h2(uint32_t code)
     return h2{h, h};
 }
 
+// General path (any K multiple of 32): per-thread register-staged loads, the
+// tile decoded to f16 in LDS once per stage.
 template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs g)
+__global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const GemmArgs g)
 {
     constexpr int kLdsBytes = 4 * kStageBytes;
     __shared__ __attribute__((aligned(2048))) uint8_t lds[kLdsBytes];
@@ -165,11 +167,230 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
 }
 
+// Decode for the fast path, with the hardware FP4 -> f16 conversion:
+// v_cvt_scalef32_pk_f16_fp4 multiplies by the power-of-two part of its f32
+// scale operand only, so S * 2^-7 is split as P * m with
+//   P = 2^(max(E, 1) - 14)        (exact; every e2m1 * P is a normal f16)
+//   m = (E > 0 ? 8 + M : M) / 8   (the E4M3 significand, exact in f16)
+// for a scale byte with exponent field E and mantissa field M; one packed
+// f16 multiply by m then gives e2m1 * S * 2^-7, exactly as decode8_f16.
+// Checked on the GPU against decode8_f16 for every code byte in every byte
+// position with every non-negative scale byte (the quantizer writes no
+// negative scales).
+struct BlockScale {
+    float p;
+    h2 m;
+};
+
+__device__ __forceinline__ BlockScale block_scale(uint32_t sb)
+{
+    const uint32_t E = (sb >> 3) & 15u, M = sb & 7u;
+    BlockScale b;
+    b.p = __uint_as_float(((E > 0 ? E : 1u) + 113u) << 23);
+    const _Float16 m = (_Float16)(float)((E > 0 ? 8u : 0u) + M) * (_Float16)0.125f;
+    b.m = h2{m, m};
+    return b;
+}
+
+__device__ __forceinline__ uint4 decode8_cvt(uint32_t w, const BlockScale &b)
+{
+    const h2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 0) * b.m;
+    const h2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 1) * b.m;
+    const h2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 2) * b.m;
+    const h2 r3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 3) * b.m;
+    return make_uint4(__builtin_bit_cast(uint32_t, r0), __builtin_bit_cast(uint32_t, r1),
+                      __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3));
+}
+
+// ---------------------------------------------------------------------------
+// Fast path (K a multiple of 256): the packed codes and block scales are
+// copied straight into LDS and each wave decodes its own fragments in
+// registers right before the MFMAs.
+//
+// A stage is 256 K-elements: per operand 256 rows x 128 code bytes (the same
+// 128-byte rows, XOR swizzle and copy pattern as the FP8 kernel) plus 256
+// rows x 16 scale bytes.  LDS holds two stages (2 x 72 KiB).
+//
+// K placement.  The MFMA's 16 K-slots per step are split between the lane
+// halves (8 each) and any one-to-one placement of K-elements on slots gives
+// the same dot product as long as A and W use the same one.  Lane half h of
+// k-step 2c + d (c = 16-byte chunk 0..7 of the stage row, d = 0, 1) takes the
+// codes in bytes 8h + 4d .. 8h + 4d + 3 of chunk c, i.e. K-elements
+// 32c + 16h + 8d + [0, 8): all inside NVFP4 block 2c + h, so one scale byte
+// serves a lane for both k-steps and the lane reads both k-steps' codes with
+// one 8-byte LDS read.  With the chunk swizzle, the 64 lanes of such a read
+// touch every bank twice (the minimum for 512 bytes).
+// ---------------------------------------------------------------------------
+constexpr int kBKF = 256;                       // K elements per stage
+constexpr int kCodeOp = kBM * 128;              // code bytes per operand per stage: 32 KiB
+constexpr int kScaleOp = kBM * 16;              // scale bytes per operand per stage: 4 KiB
+constexpr int kSlotF = 2 * (kCodeOp + kScaleOp);   // [A codes][W codes][A scales][W scales]
+
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs g)
+{
+    __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlotF];
+    __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
+    __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const Tile T = tile_of<EPI>(g);
+    const int64_t k_begin = (int64_t)blockIdx.y * g.k_chunk;
+    const int64_t k_end = min(g.K, k_begin + g.k_chunk);
+    const int nk = (int)((k_end - k_begin) / kBKF);       // whole stages (K, k_chunk multiples of 256)
+    const int64_t Nh = g.N / 2, G = g.K / 16;            // scale bytes per row
+
+    stage_scales<EPI, SPG_FMT_NVFP4>(g, T, lds_sa, lds_sw);
+
+    // ---- copy setup: codes exactly as the FP8 kernel (128-byte rows) ----------
+    const uint32_t rib = lane >> 3, pchunk = lane & 7;
+    const uint32_t c_even = pchunk ^ ((lane >> 4) & 7u);
+    const uint32_t c_odd = pchunk ^ ((4u + (lane >> 4)) & 7u);
+    const int64_t a_rows = min((int64_t)kBM, g.M - T.m0);
+    int64_t w_first, w_rows;
+    if (EPI == SPG_EPI_SWIGLU) {
+        w_rows = min((int64_t)128, Nh - T.n0);
+        w_first = (wave < 2 ? T.n0 : Nh + T.n0);
+    } else {
+        const int64_t half0 = T.n0 + (wave < 2 ? 0 : 128);
+        w_rows = min((int64_t)128, g.N - half0);
+        w_first = half0;
+    }
+    w_rows = max(w_rows, (int64_t)0);
+    const uint8_t *A = g.A, *W = g.W;
+    const uint8_t *SA = (const uint8_t *)g.sa, *SW = (const uint8_t *)g.sw;
+    const v4i rs_a = make_rsrc(A + T.m0 * g.lda, (uint32_t)(a_rows * g.lda));
+    const v4i rs_w = make_rsrc(W + w_first * g.ldw, (uint32_t)(w_rows * g.ldw));
+    const v4i rs_sa = make_rsrc(SA + T.m0 * G, (uint32_t)(a_rows * G));
+    const v4i rs_sw = make_rsrc(SW + w_first * G, (uint32_t)(w_rows * G));
+    const uint32_t ra0 = (uint32_t)(wave * 64) + rib, rw0 = (uint32_t)((wave & 1) * 64) + rib;
+    const uint32_t va_e = ra0 * (uint32_t)g.lda + c_even * 16u, va_o = ra0 * (uint32_t)g.lda + c_odd * 16u;
+    const uint32_t vw_e = rw0 * (uint32_t)g.ldw + c_even * 16u, vw_o = rw0 * (uint32_t)g.ldw + c_odd * 16u;
+    // scales: lane L of wave w copies the 16 bytes of tile row 64 w + L
+    const uint32_t vsa = (uint32_t)(wave * 64 + lane) * (uint32_t)G;
+    const uint32_t vsw = (uint32_t)((wave & 1) * 64 + lane) * (uint32_t)G;
+    const uint32_t lds_base =
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&lds[0];
+
+    // 18 copy instructions per wave per stage: 8 + 8 code blocks, 1 + 1 scale blocks
+    auto issue_stage = [&](int kt) {
+        const int slot = kt & 1;
+        const uint32_t kc = (uint32_t)((k_begin + (int64_t)kt * kBKF) / 2);    // code byte offset
+        const uint32_t ks = (uint32_t)((k_begin + (int64_t)kt * kBKF) / 16);   // scale byte offset
+        const uint32_t sbase = lds_base + (uint32_t)(slot * kSlotF);
+        const uint32_t soff_c = (uint32_t)__builtin_amdgcn_readfirstlane((int)kc);
+        const uint32_t soff_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)ks);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sbase + (uint32_t)(wave * 64 * 128 + i * 8 * 128)));
+            dma16(la, ((i & 1) ? va_o : va_e) + (uint32_t)(8 * i) * (uint32_t)g.lda, rs_a, soff_c);
+            dma16(la + (uint32_t)kCodeOp, ((i & 1) ? vw_o : vw_e) + (uint32_t)(8 * i) * (uint32_t)g.ldw, rs_w, soff_c);
+        }
+        const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sbase + 2u * kCodeOp + (uint32_t)(wave * 64 * 16)));
+        dma16(ls, vsa, rs_sa, soff_s);
+        dma16(ls + (uint32_t)kScaleOp, vsw, rs_sw, soff_s);
+    };
+
+    // ---- fragment addressing ---------------------------------------------------
+    const int l32 = lane & 31, khalf = lane >> 5;
+    const uint32_t fx = ((uint32_t)l32 >> 1) & 7u;       // swizzle term of every fragment row
+    uint32_t arow[4], wrow[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) arow[y] = (uint32_t)(wm * 128 + y * 32 + l32);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) wrow[x] = (uint32_t)(wtile_row0<EPI>(wn, x) + l32);
+
+    Acc acc;
+    zero_acc(acc);
+
+    // one stage: scales of the lane's 8 fragment rows, then 8 chunks of two
+    // k-steps (8-byte code reads one chunk ahead of their use)
+    auto compute = [&](int slot) {
+        const uint8_t *base = &lds[slot * kSlotF];
+        uint4 sca[4], scw[4];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) sca[y] = *reinterpret_cast<const uint4 *>(base + 2 * kCodeOp + arow[y] * 16);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) scw[x] = *reinterpret_cast<const uint4 *>(base + 2 * kCodeOp + kScaleOp + wrow[x] * 16);
+        auto codes = [&](int c, uint2 (&ca)[4], uint2 (&cw)[4]) {
+            const uint32_t off = (((uint32_t)c ^ fx) << 4) + (uint32_t)khalf * 8;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) ca[y] = *reinterpret_cast<const uint2 *>(base + arow[y] * 128 + off);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) cw[x] = *reinterpret_cast<const uint2 *>(base + kCodeOp + wrow[x] * 128 + off);
+        };
+        auto scale_byte = [&](const uint4 &v, int c) -> uint32_t {
+            const int b = 2 * c + khalf;                 // block 2c + h of the stage
+            const uint32_t w = (b >> 2) == 0 ? v.x : (b >> 2) == 1 ? v.y : (b >> 2) == 2 ? v.z : v.w;
+            return (w >> (8 * (b & 3))) & 0xFFu;
+        };
+        uint2 ca[2][4], cw[2][4];
+        codes(0, ca[0], cw[0]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if (c + 1 < 8) codes(c + 1, ca[(c + 1) & 1], cw[(c + 1) & 1]);
+            BlockScale sa2[4], sw2[4];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) sa2[y] = block_scale(scale_byte(sca[y], c));
+#pragma unroll
+            for (int x = 0; x < 4; ++x) sw2[x] = block_scale(scale_byte(scw[x], c));
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                v8h af[4], bf[4];
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+                    af[y] = __builtin_bit_cast(v8h, decode8_cvt(d ? ca[c & 1][y].y : ca[c & 1][y].x, sa2[y]));
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    bf[x] = __builtin_bit_cast(v8h, decode8_cvt(d ? cw[c & 1][x].y : cw[c & 1][x].x, sw2[x]));
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[x], af[y], acc[x][y], 0, 0, 0);
+            }
+        }
+    };
+
+    // two stages in flight; stage kt + 2 is copied once every wave has
+    // finished reading stage kt's slot
+    if (nk > 0) issue_stage(0);
+    if (nk > 1) issue_stage(1);
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) wait_vmem<18>();
+        else wait_vmem<0>();
+        block_barrier();                         // stage kt published
+        compute(kt & 1);
+        if (kt + 2 < nk) {
+            wait_lds();
+            block_barrier();                     // slot kt & 1 free
+            issue_stage(kt + 2);
+        }
+    }
+    __syncthreads();
+
+    if (SPLIT) {
+        splitk_store(g, T, acc);                 // the slices are summed by splitk_reduce_kernel
+        return;
+    }
+    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // slots free after the barrier
+}
+
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 {
     dim3 grid((unsigned)p.tiles, (unsigned)g.split_k, 1);
-    gemm_nvfp4_kernel<EPI><<<grid, kThreads, 0, s>>>(g);
+    // the fast path copies 16-byte pieces of the scale planes: both must be
+    // 16-byte aligned (rows are, since K / 16 is then a multiple of 16)
+    const bool fast = p.bk == kBKF && (((uintptr_t)g.sa | (uintptr_t)g.sw) & 15) == 0;
+    if (fast) {
+        if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true><<<grid, kThreads, 0, s>>>(g);
+        else gemm_nvfp4_kernel<EPI, false><<<grid, kThreads, 0, s>>>(g);
+    } else {
+        gemm_nvfp4_general_kernel<EPI><<<grid, kThreads, 0, s>>>(g);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && g.split_k > 1) e = launch_splitk_reduce(g, p.tiles, s);
     return e;

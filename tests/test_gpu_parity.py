@@ -338,6 +338,22 @@ def test_gemm_nvfp4_small_shapes(spg, shape, epi):
     check_close(gpu, ref["y"], ref["S"], f"nvfp4 {shape} {epi}")
 
 
+# K a multiple of 256: the path that copies codes and scales straight into
+# LDS (several tiles, ragged edges, and a single tile that the planner splits
+# along K)
+@pytest.mark.parametrize("epi", ["store", "add", "swiglu"])
+@pytest.mark.parametrize("shape", [(64, 64, 256), (257, 300, 512), (300, 520, 1024), (256, 256, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_nvfp4_stage256_shapes(spg, shape, epi):
+    M, N, K = shape
+    A16 = bf16_normal((M, K), 1.0, 60 + M)
+    W16 = bf16_normal((N, K), 0.02, 61 + N)
+    R16 = bf16_normal((M, N), 1.0, 62) if epi == "add" else None
+    gpu = run_nvfp4(spg, A16, W16, epi, R16)
+    ref = oracle_nvfp4(A16, W16, epi, R16)
+    check_close(gpu, ref["y"], ref["S"], f"nvfp4 {shape} {epi}")
+
+
 def test_gemm_nvfp4_wide_scale_range(spg):
     # block scales spanning subnormal E4M3 codes exercise every decode path
     M, N, K = 96, 64, 512

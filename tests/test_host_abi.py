@@ -214,7 +214,9 @@ def test_plans_for_the_workloads(spg):
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (512, 1, 512)
     # NVFP4 runs one workgroup per tile
     p = spg.gemm_plan(4096, 5120, 6144, "nvfp4", "add")
-    assert (p["tiles"], p["split_k"], p["bk"], p["workgroups"]) == (320, 1, 64, 320)
+    assert (p["tiles"], p["split_k"], p["bk"], p["workgroups"]) == (320, 1, 256, 320)
+    p = spg.gemm_plan(4096, 5120, 6176, "nvfp4", "add")   # K not a multiple of 256: general path
+    assert (p["tiles"], p["bk"]) == (320, 64)
 
 
 # ---------------------------------------------------------------------------
