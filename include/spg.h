@@ -203,17 +203,23 @@ int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t
 
 /*
  * The plan gemm_scaled would launch for `d` on a device with `units` compute
- * units: tile shape, K-split and the number of workgroups.  Returns SPG_OK or
- * the validation error gemm_scaled would return.
+ * units: tile shape, K-split, the number of workgroups and the tail split.
+ * Returns SPG_OK or the validation error gemm_scaled would return.  The
+ * workspace holds one fp32 256x256 partial tile per split tile and slice.
  */
 typedef struct spg_plan {
     int32_t bm, bn, bk;      /* workgroup tile (output rows, weight rows, K)  */
     int32_t split_k;         /* K partitions reduced through the workspace    */
     int64_t tiles;           /* output tiles over the whole batch             */
-    int64_t workgroups;      /* workgroups launched: tiles * split_k, or at  */
-                             /* most one per compute unit when the FP8 kernel */
-                             /* runs an unsplit product persistently         */
+    int64_t workgroups;      /* workgroups of the first launch: tiles (minus  */
+                             /* the tail) * split_k, or at most one per       */
+                             /* compute unit when the FP8 kernel runs an      */
+                             /* unsplit product persistently                  */
     int32_t kernel;          /* internal kernel id                            */
+    int32_t tail_split;      /* > 1: the last tail_tiles tiles run in a second */
+                             /* launch split tail_split ways along K (whole   */
+                             /* rounds of tiles stay unsplit), else 1         */
+    int64_t tail_tiles;
 } spg_plan;
 
 int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units, spg_plan *plan);

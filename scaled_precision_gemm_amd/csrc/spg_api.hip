@@ -94,18 +94,46 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     p->tiles = tiles_m * tiles_n * d->batch;
     p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->K, units, p->bk) : 1;
     p->kernel = d->format == SPG_FMT_NVFP4 ? 1 : 0;
+    p->tail_split = 1;
+    p->tail_tiles = 0;
+    // Tail split: when the tiles fill several whole rounds of the compute
+    // units plus a partial one, the whole rounds run unsplit and the
+    // remaining tiles run split along K in a second launch (so the last round
+    // is short instead of mostly idle).  Taken when the time it saves, from
+    // the per-unit rate these kernels reach (FP8 ~9.6, NVFP4 ~4.1 TFLOP/s per
+    // compute unit), exceeds the partial tiles' extra traffic (written and
+    // read back at ~4 TB/s) plus ~10 us of launches.
+    if (p->split_k == 1 && p->tiles > units && d->K > 0) {
+        const int64_t rem = p->tiles % units;
+        if (rem > 0) {
+            int s = (int)(units / rem < 8 ? units / rem : 8);
+            while (s > 1 && (d->K / s < 1024 || cdiv(d->K, s) < 2 * (int64_t)p->bk)) --s;
+            if (s >= 2) {
+                const double rate = d->format == SPG_FMT_NVFP4 ? 4.1e12 : 9.6e12;
+                const double t_tile = 2.0 * kTile * kTile * (double)d->K / rate;
+                const double gain = t_tile * (1.0 - 1.0 / s);
+                const double cost = 2.0 * (double)rem * s * kTile * kTile * 4.0 / 4e12 + 10e-6;
+                if (gain > cost) {
+                    p->tail_tiles = rem;
+                    p->tail_split = s;
+                }
+            }
+        }
+    }
+    const int64_t main_tiles = p->tiles - p->tail_tiles;
     // The FP8 kernel runs unsplit products with two or more K stages
     // persistently: one workgroup per compute unit walking its tiles.
     if (p->kernel == 0 && p->split_k == 1 && cdiv(d->K, p->bk) >= 2)
-        p->workgroups = p->tiles < units ? p->tiles : units;
+        p->workgroups = main_tiles < units ? main_tiles : units;
     else
-        p->workgroups = p->tiles * p->split_k;
+        p->workgroups = main_tiles * p->split_k;
 }
 
 size_t plan_workspace(const spg_plan *p)
 {
-    if (p->split_k <= 1) return 0;
-    return (size_t)p->tiles * p->split_k * kTile * kTile * sizeof(float);
+    if (p->split_k > 1) return (size_t)p->tiles * p->split_k * kTile * kTile * sizeof(float);
+    if (p->tail_split > 1) return (size_t)p->tail_tiles * p->tail_split * kTile * kTile * sizeof(float);
+    return 0;
 }
 
 }  // namespace
@@ -238,8 +266,29 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.tiles_m = cdiv(d->M, kTile);
     g.tiles_n = epilogue == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
     if (p.split_k > 1) g.partials = (float *)ws;
+    g.tile_begin = 0;
+    g.tile_count = p.tiles - p.tail_tiles;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = d->format == SPG_FMT_NVFP4 ? launch_gemm_nvfp4(g, p, s) : launch_gemm_fp8(g, p, s);
+    auto launch = [&](const GemmArgs &a, const spg_plan &q) {
+        return d->format == SPG_FMT_NVFP4 ? launch_gemm_nvfp4(a, q, s) : launch_gemm_fp8(a, q, s);
+    };
+    spg_plan pm = p;
+    pm.tiles = g.tile_count;
+    hipError_t e = launch(g, pm);
+    if (e == hipSuccess && p.tail_tiles > 0) {
+        // the tail: the last tail_tiles tiles, split along K, then reduced
+        GemmArgs gt = g;
+        gt.tile_begin = p.tiles - p.tail_tiles;
+        gt.tile_count = p.tail_tiles;
+        gt.split_k = p.tail_split;
+        gt.k_chunk = cdiv(cdiv(d->K, p.tail_split), unit_k) * unit_k;
+        gt.partials = (float *)ws;
+        spg_plan pt = p;
+        pt.tiles = p.tail_tiles;
+        pt.split_k = p.tail_split;
+        pt.workgroups = p.tail_tiles * p.tail_split;
+        e = launch(gt, pt);
+    }
     return e == hipSuccess ? SPG_OK : SPG_EHIP;
 }
 

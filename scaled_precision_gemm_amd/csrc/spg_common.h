@@ -107,6 +107,7 @@ struct GemmArgs {
     int32_t split_k;
     int64_t k_chunk;                  // K per split (multiple of the tile K)
     int64_t tiles_m, tiles_n;         // output tiles per product
+    int64_t tile_begin, tile_count;   // the tiles this launch computes (of batch*tiles_m*tiles_n)
 };
 
 hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s);

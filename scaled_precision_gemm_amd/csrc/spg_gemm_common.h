@@ -119,7 +119,7 @@ __device__ __forceinline__ Tile tile_from_id(const GemmArgs &g, int64_t t)
 template <int EPI>
 __device__ __forceinline__ Tile tile_of(const GemmArgs &g)
 {
-    return tile_from_id<EPI>(g, xcd_remap(blockIdx.x, gridDim.x));
+    return tile_from_id<EPI>(g, g.tile_begin + xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // W row of tile row r (0..255) and whether it exists.  SWIGLU: rows 0..127
@@ -195,11 +195,12 @@ __device__ __forceinline__ void stage_scales(const GemmArgs &g, const Tile &T, f
 // finished - the kernel boundary orders the stores before the loads, so no
 // device-scope fence or counter is needed.  A lane's 16 accumulators of one
 // 32x32 block are stored contiguously (four 16-byte stores; a wave writes
-// 4 KiB contiguous per block): slice s of tile t, block b = 4 x + y, thread
-// i starts at ((t * S + s) * 16 + b) * 4096 + i * 16 floats.
+// 4 KiB contiguous per block): slice s of the launch's tile t (counted from
+// tile_begin), block b = 4 x + y, thread i starts at
+// ((t * S + s) * 16 + b) * 4096 + i * 16 floats.
 __device__ __forceinline__ void splitk_store(const GemmArgs &g, const Tile &T, const Acc &acc)
 {
-    float *base = g.partials + (T.global * g.split_k + blockIdx.y) * (int64_t)(kBM * kBN) + threadIdx.x * 16;
+    float *base = g.partials + ((T.global - g.tile_begin) * g.split_k + blockIdx.y) * (int64_t)(kBM * kBN) + threadIdx.x * 16;
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk) {
         v4f *dst = reinterpret_cast<v4f *>(base + blk * (kThreads * 16));

@@ -74,10 +74,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     // Tiles of this workgroup: virtual workgroup ids blockIdx.x + i * gridDim.x
     // (a persistent grid of one workgroup per compute unit walks the same
     // XCD-aware order a one-tile-per-workgroup launch would).
-    const int64_t total = g.batch * g.tiles_m * g.tiles_n;
+    const int64_t total = g.tile_count;
     const int ntile = (int)((total - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x);
     auto tile_i = [&](int i) -> Tile {
-        return tile_from_id<EPI>(g, xcd_remap((int64_t)blockIdx.x + (int64_t)i * gridDim.x, total));
+        return tile_from_id<EPI>(g, g.tile_begin + xcd_remap((int64_t)blockIdx.x + (int64_t)i * gridDim.x, total));
     };
 
     const int split = blockIdx.y;

@@ -305,51 +305,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     Acc acc;
     zero_acc(acc);
 
-    // one stage: scales of the lane's 8 fragment rows, then 8 chunks of two
-    // k-steps (8-byte code reads one chunk ahead of their use)
+    // One stage = 8 chunks x 2 k-steps x 16 MFMAs, in a fixed order with the
+    // decode and LDS work of the next k-step slotted between the MFMAs of the
+    // current one (one wave per SIMD: the MFMA pipe idles whenever the wave
+    // stops to wait for LDS or to decode):
+    //   k-step (c, 0): after MFMA j (j even) decode fragment j/2 of (c, 1);
+    //                  after MFMA 1 read chunk c + 1's codes; after MFMA j
+    //                  (j odd) prepare one block scale of chunk c + 1
+    //   k-step (c, 1): after MFMA j decode fragment j/2 of (c + 1, 0)
+    // Fragments 0..3 are the A blocks y, 4..7 the W blocks x.
     auto compute = [&](int slot) {
         const uint8_t *base = &lds[slot * kSlotF];
-        uint4 sca[4], scw[4];
+        uint4 sc[8];                                   // the 16 scale bytes of each fragment row
 #pragma unroll
-        for (int y = 0; y < 4; ++y) sca[y] = *reinterpret_cast<const uint4 *>(base + 2 * kCodeOp + arow[y] * 16);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) scw[x] = *reinterpret_cast<const uint4 *>(base + 2 * kCodeOp + kScaleOp + wrow[x] * 16);
-        auto codes = [&](int c, uint2 (&ca)[4], uint2 (&cw)[4]) {
+        for (int f = 0; f < 8; ++f)
+            sc[f] = *reinterpret_cast<const uint4 *>(base + 2 * kCodeOp + (f < 4 ? arow[f] * 16 : kScaleOp + wrow[f - 4] * 16));
+        auto read_code = [&](int c, int f) -> uint2 {
             const uint32_t off = (((uint32_t)c ^ fx) << 4) + (uint32_t)khalf * 8;
-#pragma unroll
-            for (int y = 0; y < 4; ++y) ca[y] = *reinterpret_cast<const uint2 *>(base + arow[y] * 128 + off);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) cw[x] = *reinterpret_cast<const uint2 *>(base + kCodeOp + wrow[x] * 128 + off);
+            return *reinterpret_cast<const uint2 *>(base + (f < 4 ? arow[f] * 128 : kCodeOp + wrow[f - 4] * 128) + off);
         };
-        auto scale_byte = [&](const uint4 &v, int c) -> uint32_t {
-            const int b = 2 * c + khalf;                 // block 2c + h of the stage
+        auto scale_of = [&](int c, int f) -> BlockScale {
+            const int b = 2 * c + khalf;               // block 2c + h of the stage
+            const uint4 &v = sc[f];
             const uint32_t w = (b >> 2) == 0 ? v.x : (b >> 2) == 1 ? v.y : (b >> 2) == 2 ? v.z : v.w;
-            return (w >> (8 * (b & 3))) & 0xFFu;
+            return block_scale((w >> (8 * (b & 3))) & 0xFFu);
         };
-        uint2 ca[2][4], cw[2][4];
-        codes(0, ca[0], cw[0]);
+        uint2 code[2][8];
+        BlockScale bs[2][8];
+        uint4 fr[2][8];                                // decoded fragments of the current / next k-step
+#pragma unroll
+        for (int f = 0; f < 8; ++f) code[0][f] = read_code(0, f);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) bs[0][f] = scale_of(0, f);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) fr[0][f] = decode8_cvt(code[0][f].x, bs[0][f]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            if (c + 1 < 8) codes(c + 1, ca[(c + 1) & 1], cw[(c + 1) & 1]);
-            BlockScale sa2[4], sw2[4];
-#pragma unroll
-            for (int y = 0; y < 4; ++y) sa2[y] = block_scale(scale_byte(sca[y], c));
-#pragma unroll
-            for (int x = 0; x < 4; ++x) sw2[x] = block_scale(scale_byte(scw[x], c));
+            const int cb = c & 1, nb = cb ^ 1;
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
-                v8h af[4], bf[4];
+                const int fc = d, fn = d ^ 1;          // fr index of this k-step / the next
 #pragma unroll
-                for (int y = 0; y < 4; ++y)
-                    af[y] = __builtin_bit_cast(v8h, decode8_cvt(d ? ca[c & 1][y].y : ca[c & 1][y].x, sa2[y]));
+                for (int j = 0; j < 16; ++j) {
+                    const int y = j >> 2, x = j & 3;
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fr[fc][4 + x]),
+                                                                     __builtin_bit_cast(v8h, fr[fc][y]), acc[x][y], 0, 0, 0);
+                    if (d == 0) {
+                        if ((j & 1) == 0) fr[fn][j >> 1] = decode8_cvt(code[cb][j >> 1].y, bs[cb][j >> 1]);
+                        if (j == 1 && c + 1 < 8) {
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    bf[x] = __builtin_bit_cast(v8h, decode8_cvt(d ? cw[c & 1][x].y : cw[c & 1][x].x, sw2[x]));
-#pragma unroll
-                for (int y = 0; y < 4; ++y)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[x], af[y], acc[x][y], 0, 0, 0);
+                            for (int f = 0; f < 8; ++f) code[nb][f] = read_code(c + 1, f);
+                        }
+                        if ((j & 1) == 1 && c + 1 < 8) bs[nb][j >> 1] = scale_of(c + 1, j >> 1);
+                    } else if (c + 1 < 8) {
+                        if (j == 0) wait_lds();
+                        if ((j & 1) == 0) fr[fn][j >> 1] = decode8_cvt(code[nb][j >> 1].x, bs[nb][j >> 1]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };

@@ -19,14 +19,14 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const GemmArgs 
 {
     __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
     __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
-    const Tile T = tile_from_id<EPI>(g, blockIdx.x);
+    const Tile T = tile_from_id<EPI>(g, g.tile_begin + blockIdx.x);
     stage_scales<EPI, SMODE>(g, T, lds_sa, lds_sw);
 
     // Thread i handles the 16 accumulators thread i of the GEMM workgroup
     // held for block (x, y), so the GEMM's epilogue code applies unchanged.
     const int x = (int)blockIdx.y >> 2;    // SWIGLU: 0..1 (gate blocks), else 0..3
     const int y = (int)blockIdx.y & 3;
-    const float *tile_base = g.partials + T.global * g.split_k * (int64_t)(kBM * kBN) + threadIdx.x * 16;
+    const float *tile_base = g.partials + (int64_t)blockIdx.x * g.split_k * (kBM * kBN) + threadIdx.x * 16;
     auto sum_block = [&](int blk) -> v16f {
         v16f t;
         for (int s = 0; s < g.split_k; ++s) {

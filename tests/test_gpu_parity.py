@@ -430,3 +430,46 @@ def test_workload_full_size_sampled(spg, name):
             sa_o, sw_o = ta_o, tw_o
         y, S, _ = oracle.epilogue(wl.epilogue, D, Da, sa_o, sw_o, Rs)
         check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"{name} batch {b}")
+
+
+# ---------------------------------------------------------------------------
+# tail split: 272 tiles on 256 compute units; the last 16 tiles (tile rows
+# 8..15, tile columns 15 and 16 in the raster order) run split along K in a
+# second launch.  Outputs are sampled in both parts.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,K", [("nvfp4", 4096), ("e4m3_row", 16384)])
+def test_gemm_tail_split_sampled(spg, fmt, K):
+    M, N = 4096, 4352
+    plan = spg.gemm_plan(M, N, K, fmt, "store")
+    assert plan["tail_tiles"] == 16 and plan["tail_split"] > 1
+    rng = np.random.default_rng(123)
+    A16 = bf16_normal((M, K), 1.0, 70)
+    W16 = bf16_normal((N, K), 0.02, 71)
+    A, W = dev(A16), dev(W16)
+    if fmt == "nvfp4":
+        qa, sa, ta = spg.quantize_block16(A)
+        qw, sw, tw = spg.quantize_block16(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, "store", fmt="nvfp4", tscale_a=ta, tscale_w=tw)
+    else:
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, "store")
+    torch.cuda.synchronize()
+    gpu = host_u16(out)
+    del A, W, qa, qw, out
+    torch.cuda.empty_cache()
+    rows = np.unique(np.concatenate([sample(M, 24, rng), rng.choice(np.arange(2048, M), 16, replace=False)]))
+    cols = np.unique(np.concatenate([sample(N, 24, rng), rng.choice(np.arange(3840, N), 16, replace=False), [3840, N - 1]]))
+    if fmt == "nvfp4":
+        ta_o, tw_o = oracle.nvfp4_tensor_scale(A16), oracle.nvfp4_tensor_scale(W16)
+        qa_o, bsa_o = oracle.quantize_block16_rows(np.ascontiguousarray(A16[rows]), ta_o)
+        qw_o, bsw_o = oracle.quantize_block16_rows(np.ascontiguousarray(W16[cols]), tw_o)
+        D, Da = oracle.gemm_nvfp4_sums(qa_o, bsa_o, qw_o, bsw_o)
+        y, S, _ = oracle.epilogue("store", D, Da, ta_o, tw_o, None)
+    else:
+        qa_o, sa_o = oracle.quantize_rowwise(np.ascontiguousarray(A16[rows]))
+        qw_o, sw_o = oracle.quantize_rowwise(np.ascontiguousarray(W16[cols]))
+        D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+        y, S, _ = oracle.epilogue("store", D, Da, sa_o, sw_o, None)
+    check_close(np.ascontiguousarray(gpu[np.ix_(rows, cols)]), y, S, f"tail split {fmt} K={K}")

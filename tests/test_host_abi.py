@@ -212,11 +212,30 @@ def test_plans_for_the_workloads(spg):
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (256, 1, 256)
     p = spg.gemm_plan(8192, 4096, 128, "e4m3_tensor", "store")
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (512, 1, 512)
-    # NVFP4 runs one workgroup per tile
+    # NVFP4: 320 tiles = one round of 256 + 64 more; the 64 run split 4 ways
+    # along K in a second launch (tail split), the first launch takes 256
     p = spg.gemm_plan(4096, 5120, 6144, "nvfp4", "add")
-    assert (p["tiles"], p["split_k"], p["bk"], p["workgroups"]) == (320, 1, 256, 320)
+    assert (p["tiles"], p["split_k"], p["bk"], p["workgroups"]) == (320, 1, 256, 256)
+    assert (p["tail_tiles"], p["tail_split"]) == (64, 4)
+    # FP8 at T=4096 SwiGLU: 8.5 rounds, but a half round of 70 us tiles does
+    # not pay for the partial-tile traffic
+    p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu")
+    assert (p["tail_tiles"], p["tail_split"]) == (0, 1)
+    # long K: worth it for FP8 too (K / 8 still >= 1024)
+    p = spg.gemm_plan(4096, 4352, 16384, "e4m3_row", "store")
+    assert (p["tiles"], p["workgroups"], p["tail_tiles"], p["tail_split"]) == (272, 256, 16, 8)
+    # whole rounds: no tail
+    p = spg.gemm_plan(8192, 8192, 8192, "e4m3_tensor", "store")
+    assert (p["tail_tiles"], p["tail_split"]) == (0, 1)
     p = spg.gemm_plan(4096, 5120, 6176, "nvfp4", "add")   # K not a multiple of 256: general path
     assert (p["tiles"], p["bk"]) == (320, 64)
+
+
+def test_workspace_covers_the_tail_split(spg):
+    d = desc(spg, 4096, 5120, 6144, 2)
+    assert spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), 1) == 64 * 4 * 256 * 256 * 4
+    d = desc(spg, 4096, 34816, 5120, 0)
+    assert spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), 2) == 0
 
 
 # ---------------------------------------------------------------------------
