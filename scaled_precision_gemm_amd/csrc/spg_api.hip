@@ -53,6 +53,12 @@ int validate_desc(const spg_gemm_desc *d, int epi)
     if ((d->stride_a & 15) || (d->stride_w & 15)) return SPG_EINVAL;
     if (d->ldo < nout) return SPG_EINVAL;
     if (epi == SPG_EPI_ADD && d->ldr < nout) return SPG_EINVAL;
+    // tile ids are computed in 32-bit arithmetic
+    {
+        const int64_t tm = cdiv(d->M, kTile), tn = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
+        if (tm > 0 && tn > 0 && (tm * tn > (INT64_C(1) << 28) || d->batch * tm * tn >= (INT64_C(1) << 31)))
+            return SPG_EUNSUPPORTED;
+    }
     // the epilogue addresses a 32-row block with 32-bit byte offsets
     if (d->ldo >= (INT64_C(1) << 26) || (epi == SPG_EPI_ADD && d->ldr >= (INT64_C(1) << 26)))
         return SPG_EUNSUPPORTED;
@@ -265,6 +271,9 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.k_chunk = p.split_k > 1 ? cdiv(cdiv(d->K, p.split_k), unit_k) * unit_k : (d->K > 0 ? d->K : 1);
     g.tiles_m = cdiv(d->M, kTile);
     g.tiles_n = epilogue == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
+    g.div_per = make_fastdiv((uint32_t)(g.tiles_m * g.tiles_n));
+    g.div_span = make_fastdiv((uint32_t)(8 * g.tiles_n));
+    g.div_gm_last = make_fastdiv(g.tiles_m % 8 ? (uint32_t)(g.tiles_m % 8) : 8u);
     if (p.split_k > 1) g.partials = (float *)ws;
     g.tile_begin = 0;
     g.tile_count = p.tiles - p.tail_tiles;

@@ -90,6 +90,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 // ---------------------------------------------------------------------------
 // Host-side launchers shared between translation units
 // ---------------------------------------------------------------------------
+// Division by a launch constant d >= 1 for n < 2^31 as (umulhi(n, m) + n) >> s
+// with s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1 (computed on the
+// host): scalar multiply-high and shift instead of a division expanded on the
+// vector unit.
+struct FastDiv {
+    uint32_t m, s;
+};
+
 struct GemmArgs {
     void *out;
     const uint8_t *A;
@@ -108,7 +116,15 @@ struct GemmArgs {
     int64_t k_chunk;                  // K per split (multiple of the tile K)
     int64_t tiles_m, tiles_n;         // output tiles per product
     int64_t tile_begin, tile_count;   // the tiles this launch computes (of batch*tiles_m*tiles_n)
+    FastDiv div_per, div_span, div_gm_last;   // by tiles_m*tiles_n, 8*tiles_n, tiles_m % 8
 };
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t sh = 0;
+    while ((1ull << sh) < d) ++sh;
+    return FastDiv{(uint32_t)((((1ull << sh) - d) << 32) / d + 1), sh};
+}
 
 hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s);
 hipError_t launch_gemm_nvfp4(const GemmArgs &g, const spg_plan &p, hipStream_t s);

@@ -83,6 +83,17 @@ __device__ __forceinline__ void block_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Lane index 0..63 recomputed from the execution mask (full at every call
+// site): cheaper for the register allocator than keeping threadIdx.x alive,
+// whose spill reload would wait on every outstanding memory operation.
+// (volatile assembly: the builtins would be computed once and spilled).
+__device__ __forceinline__ int lane_id()
+{
+    int r;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 struct Tile {
@@ -97,21 +108,29 @@ struct Tile {
 // Tiles of one product are rasterized in groups of kGroupM tile-rows,
 // column-major inside a group, so neighbouring tile ids share A panels
 // (same rows) and W panels (same columns) through the L2 of their XCD.
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f)
+{
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// All in 32-bit scalar arithmetic (tile counts are below 2^31).
 template <int EPI>
 __device__ __forceinline__ Tile tile_from_id(const GemmArgs &g, int64_t t)
 {
     Tile T;
     T.global = t;
-    const int64_t per = g.tiles_m * g.tiles_n;
-    T.b = t / per;
-    t -= T.b * per;
-    const int64_t span = (int64_t)kGroupM * g.tiles_n;
-    const int64_t first_m = (t / span) * kGroupM;
-    const int64_t gm = min((int64_t)kGroupM, g.tiles_m - first_m);
-    const int64_t tin = t % span;
-    T.m0 = (first_m + tin % gm) * kBM;
-    T.tn = tin / gm;
-    T.n0 = EPI == SPG_EPI_SWIGLU ? T.tn * (kBN / 2) : T.tn * kBN;
+    const uint32_t tt = (uint32_t)t, tiles_m = (uint32_t)g.tiles_m, tiles_n = (uint32_t)g.tiles_n;
+    const uint32_t b = fdiv(tt, g.div_per);
+    const uint32_t rem = tt - b * (tiles_m * tiles_n);
+    const uint32_t grp = fdiv(rem, g.div_span);
+    const uint32_t first_m = grp * kGroupM;
+    const uint32_t tin = rem - grp * (kGroupM * tiles_n);
+    const uint32_t gm = min((uint32_t)kGroupM, tiles_m - first_m);
+    const uint32_t tn = gm == (uint32_t)kGroupM ? tin / kGroupM : fdiv(tin, g.div_gm_last);
+    T.b = b;
+    T.m0 = (int64_t)(first_m + (tin - tn * gm)) * kBM;
+    T.tn = tn;
+    T.n0 = EPI == SPG_EPI_SWIGLU ? (int64_t)tn * (kBN / 2) : (int64_t)tn * kBN;
     T.c0 = T.n0;
     return T;
 }
@@ -162,32 +181,42 @@ __device__ __forceinline__ int wtile_row0(int wn, int x)
     return wn * 128 + x * 32;
 }
 
-// Scale factors of the tile into LDS, one entry per A-tile row (lds_sa) and
-// per W-tile row (lds_sw); the epilogue forms acc * lds_sa * lds_sw.
-//   E4M3 per row:    lds_sa = s_a[row], lds_sw = s_w[W row]
-//   E4M3 per tensor: lds_sa = s_a, lds_sw = s_w (of the batch entry)
-//   NVFP4:           lds_sa = 2^14 * tA * tW (2^14 undoes the two 2^-7
-//                    operand offsets of the kernel's f16 decode), lds_sw = 1
-// Must be called by all kThreads threads; a barrier must follow before use.
+// Scale factors of the tile, one entry per A-tile row (sa) and per W-tile
+// row (sw); the epilogue forms acc * sa * sw.  Thread i supplies row i:
+//   E4M3 per row:    sa = s_a[row], sw = s_w[W row]
+//   E4M3 per tensor: sa = s_a, sw = s_w (of the batch entry)
+//   NVFP4:           sa = 2^14 * tA * tW (2^14 undoes the two 2^-7
+//                    operand offsets of the kernel's f16 decode), sw = 1
 template <int EPI, int SMODE>
-__device__ __forceinline__ void stage_scales(const GemmArgs &g, const Tile &T, float *lds_sa, float *lds_sw)
+__device__ __forceinline__ void scale_values(const GemmArgs &g, const Tile &T, float &va, float &vw)
 {
     const int tid = threadIdx.x;
     if (SMODE == SPG_FMT_NVFP4) {
-        lds_sa[tid] = 16384.0f * *g.tscale_a * *g.tscale_w;
-        lds_sw[tid] = 1.0f;
+        va = 16384.0f * *g.tscale_a * *g.tscale_w;
+        vw = 1.0f;
     } else if (SMODE == SPG_FMT_E4M3_ROW) {
         bool wok;
         const int64_t wr = w_row<EPI>(g, T, tid, wok);
         const int64_t r = T.m0 + tid;
         const float *sa = (const float *)g.sa + (g.stride_a ? T.b * g.sa_bstride : 0);
         const float *sw = (const float *)g.sw + (g.stride_w ? T.b * g.sw_bstride : 0);
-        lds_sa[tid] = r < g.M ? sa[r] : 0.0f;
-        lds_sw[tid] = wok ? sw[wr] : 0.0f;
+        va = r < g.M ? sa[r] : 0.0f;
+        vw = wok ? sw[wr] : 0.0f;
     } else {
-        lds_sa[tid] = ((const float *)g.sa)[g.stride_a ? T.b : 0];
-        lds_sw[tid] = ((const float *)g.sw)[g.stride_w ? T.b : 0];
+        va = ((const float *)g.sa)[g.stride_a ? T.b : 0];
+        vw = ((const float *)g.sw)[g.stride_w ? T.b : 0];
     }
+}
+
+// The tile's scale factors into LDS.  Must be called by all kThreads
+// threads; a barrier must follow before use.
+template <int EPI, int SMODE>
+__device__ __forceinline__ void stage_scales(const GemmArgs &g, const Tile &T, float *lds_sa, float *lds_sw)
+{
+    float va, vw;
+    scale_values<EPI, SMODE>(g, T, va, vw);
+    lds_sa[threadIdx.x] = va;
+    lds_sw[threadIdx.x] = vw;
 }
 
 // Split-K, part 1: every K slice stores its fp32 partial tile and stops; a
@@ -253,7 +282,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
                                                const v16f &a, const v16f &up, const float *lds_sa,
                                                const float *lds_sw)
 {
-    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    const int lane = threadIdx.x & 63, wm = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >> 1;
     const int l32 = lane & 31, khalf = lane >> 5;
     const int rl = wm * 128 + y * 32 + l32;
     const int64_t row = T.m0 + rl;
@@ -339,11 +368,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const
 {
     constexpr bool SW = EPI == SPG_EPI_SWIGLU;
     constexpr int NP = SW ? 1 : 2;            // 64-column passes per 32-row block
-    int lane = threadIdx.x & 63;
-    // Opaque to the optimizer: lane-derived offsets are recomputed per call
-    // instead of being hoisted (and spilled) across a persistent tile loop.
-    asm volatile("" : "+v"(lane));
-    const int wave = threadIdx.x >> 6;
+    // opaque to the optimizer: lane-derived offsets are recomputed per call
+    // instead of being hoisted (and spilled) across a persistent tile loop
+    const int lane = lane_id();
+    // the wave index is uniform: keeping it (and every row / column bound
+    // derived from it) in scalar registers keeps the pass branches uniform
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
     const EpiOut o = epi_out<EPI>(g, T);
     const bool vec16 = ((((uintptr_t)o.out) & 15) == 0) && ((g.ldo & 7) == 0);
@@ -353,18 +383,35 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const
     // 32-bit element offsets inside a 32-row block (ldo, ldr < 2^26)
     const uint32_t ldo = (uint32_t)g.ldo, ldr = (uint32_t)g.ldr;
 
+    // every scale factor this lane needs, read from LDS before any region
+    // write (the compiler cannot move LDS reads across LDS writes it cannot
+    // prove disjoint, so reading them per element would wait on each)
+    constexpr int NX = SW ? 2 : 4;
+    float sa_r[4];
+    v4f sw_r[NX][4], swu_r[SW ? 2 : 1][4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) sa_r[y] = lds_sa[wm * 128 + y * 32 + l32];
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int wl = wtile_row0<EPI>(wn, x) + q * 8 + khalf * 4;
+            sw_r[x][q] = *reinterpret_cast<const v4f *>(lds_sw + wl);
+            if (SW) swu_r[x & 1][q] = *reinterpret_cast<const v4f *>(lds_sw + 128 + wl);
+        }
+
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
         const int64_t row0 = T.m0 + wm * 128 + y * 32;
         const int rows_valid = (int)min((int64_t)32, g.M - row0);
         if (rows_valid <= 0) break;                                 // uniform per wave
-        const float sa = lds_sa[wm * 128 + y * 32 + l32];
+        const float sa = sa_r[y];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int64_t col0 = T.c0 + (SW ? wn * 64 : wn * 128 + p * 64);
             const int cols_valid = (int)min((int64_t)64, o.nvalid - col0);
             if (cols_valid <= 0) break;                             // uniform per wave
-            // keep each pass's loads inside the pass (hoisting them all would
+            // keep each pass's work inside the pass (hoisting it all would
             // need more registers than the accumulators leave)
             __builtin_amdgcn_sched_barrier(0);
             uint16_t *const obase = o.out + row0 * g.ldo + col0;   // uniform
@@ -396,12 +443,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const
 #pragma unroll
             for (int xx = 0; xx < 2; ++xx) {
                 const int x = SW ? xx : p * 2 + xx;
-                const int w0 = wtile_row0<EPI>(wn, x);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int wl = w0 + q * 8 + khalf * 4;
-                    const v4f sw = *reinterpret_cast<const v4f *>(lds_sw + wl);
-                    const v4f swu = SW ? *reinterpret_cast<const v4f *>(lds_sw + 128 + wl) : v4f{};
+                    const v4f sw = sw_r[x][q];
+                    const v4f swu = SW ? swu_r[x & 1][q] : v4f{};
                     uint2 *dst = reinterpret_cast<uint2 *>(region + l32 * 128 + phys(l32, xx * 4 + q) * 16 + khalf * 8);
                     float v[4];
 #pragma unroll

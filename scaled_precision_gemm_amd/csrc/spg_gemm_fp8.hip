@@ -120,8 +120,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         uint32_t foff[2][2];
     };
     auto lane_ctx = [&]() -> LaneCtx {
-        int ln = tid & 63;
-        asm volatile("" : "+v"(ln));
+        const int ln = lane_id();
         LaneCtx c;
         const uint32_t rib = (uint32_t)ln >> 3, pchunk = (uint32_t)ln & 7;
         c.c_even = pchunk ^ (((uint32_t)ln >> 4) & 7u);
@@ -278,6 +277,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         ++G;
     };
     for (int i = 0; i < ntile; ++i) {
+        // The next tile's scale factors are loaded now, a whole tile before
+        // they are written to LDS: loads and stores retire in issue order, so
+        // loading them next to this tile's output stores would make every
+        // wave wait for its stores (and for the loads' own latency).
+        float nsa = 0.0f, nsw = 0.0f;
+        if (i + 1 < ntile) scale_values<EPI, SMODE>(g, Tn, nsa, nsw);
         Acc acc;
         zero_acc(acc);
         for (int kt = 0; kt + 1 < nk; ++kt) stage(acc, kt, std::false_type{});
@@ -301,7 +306,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
             }
             // Every wave has passed this tile's barriers, so none still reads
             // the scales of tile i - 1 that share this buffer.
-            stage_scales<EPI, SMODE>(g, Tc, lds_scale[(i + 1) & 1][0], lds_scale[(i + 1) & 1][1]);
+            const int t = wave * 64 + lane_id();
+            lds_scale[(i + 1) & 1][0][t] = nsa;
+            lds_scale[(i + 1) & 1][1][t] = nsw;
         }
     }
     wait_vmem<0>();   // no copy into LDS may still be in flight when the workgroup ends
