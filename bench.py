@@ -116,23 +116,57 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command=""):
     kname = "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel"
     stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
     lines = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
-    gemm_avg_us = None
     for r in stats:
         short = r["Name"].replace("void ", "").replace("spg::(anonymous namespace)::", "").split("(")[0]
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-        if kname in r["Name"]:
-            gemm_avg_us = float(r["AverageNs"]) / 1e3
 
-    def per_dispatch(d, counter):
-        rows = _read_csv(_find(d, "counter_collection.csv"))
-        gemm = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and kname in r["Kernel_Name"]]
+    # One gemm_scaled call is one to three dispatches (main tiles, a K-split
+    # tail, its reduction); bench.py's events bracket the whole call.  The
+    # timed steps are the last `--steps` calls of the traced run.
+    first = command.strip().splitlines()[0].split() if command.strip() else []
+    steps, warmup = 200, 150
+    for i, a in enumerate(first):
+        if a == "--steps":
+            steps = int(first[i + 1])
+        if a == "--warmup":
+            warmup = int(first[i + 1])
+    timed_avg_us = None
+    try:
+        trace = _read_csv(_find(stats_dir, "kernel_trace.csv"))
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in
+                sorted(trace, key=lambda r: int(r["Start_Timestamp"]))
+                if "gemm_" in r["Kernel_Name"] or "splitk_reduce" in r["Kernel_Name"]]
+        per_call = len(durs) // (steps + warmup)
+        if per_call >= 1 and len(durs) == per_call * (steps + warmup):
+            timed_avg_us = float(np.sum(durs[-steps * per_call:])) / steps / 1e3
+    except FileNotFoundError:
+        pass
+
+    def per_call(d, counter, line):
+        """Counter value of each gemm_scaled call (summed over its dispatches)
+        and of the copy dispatches, from the run of command line `line`."""
+        calls = 4
+        toks = command.strip().splitlines()[line].split() if len(command.strip().splitlines()) > line else []
+        st = wu = None
+        for i, a in enumerate(toks):
+            if a == "--steps":
+                st = int(toks[i + 1])
+            if a == "--warmup":
+                wu = int(toks[i + 1])
+        if st is not None and wu is not None:
+            calls = st + wu
+        rows = sorted(_read_csv(_find(d, "counter_collection.csv")), key=lambda r: int(r["Dispatch_Id"]))
+        vals = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter
+                and ("gemm_" in r["Kernel_Name"] or "splitk_reduce" in r["Kernel_Name"])]
+        k = max(1, len(vals) // calls)
+        gemm = [sum(vals[i:i + k]) for i in range(0, k * calls, k)] if len(vals) == k * calls else vals
         copy = [(float(r["Counter_Value"]), int(r["Grid_Size"])) for r in rows
                 if r["Counter_Name"] == counter and "copy" in r["Kernel_Name"].lower()]
         return gemm, copy
 
-    g_fetch, c_fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
-    g_write, c_write = per_dispatch(write_dir, "WRITE_SIZE")
+    g_fetch, c_fetch = per_call(fetch_dir, "FETCH_SIZE", 1)
+    g_write, c_write = per_call(write_dir, "WRITE_SIZE", 2)
     copy_bytes = None
     for i, a in enumerate(command.split()):
         if a == "--copy-probe-mib":
@@ -145,7 +179,7 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command=""):
         "kernel": kname, "workload": name, "kernel_source_hash": kernel_source_hash(wl.fmt),
         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
         "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": gemm_bytes(wl),
-        "fetch_scale": f_read, "write_scale": f_write, "rocprof_avg_launch_us": gemm_avg_us,
+        "fetch_scale": f_read, "write_scale": f_write, "rocprof_avg_call_us": timed_avg_us,
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
@@ -158,8 +192,13 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command=""):
         fh.write(f"# {kname} on {name} (M={wl.M}, N={wl.N}, K={wl.K}, batch={wl.batch}, {wl.fmt}, {wl.epilogue})\n\n")
         fh.write(f"Kernel statistics, `rocprofv3 --kernel-trace --stats` (one MI355X):\n\n")
         fh.write("\n".join(lines) + "\n\n")
-        fh.write(f"HBM traffic of one {kname} launch (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, "
-                 f"median over launches), scaled by the counters' reading for a plain copy of "
+        if timed_avg_us is not None:
+            fh.write(f"GPU time of one gemm_scaled call (all its dispatches: main tiles, K-split tail and "
+                     f"reduction where the plan has them) averaged over the {steps} timed steps alone, the "
+                     f"last {steps} calls of the kernel trace (the warmup calls above include the power "
+                     f"controller's throttling dip): {timed_avg_us:.1f} us\n\n")
+        fh.write(f"HBM traffic of one gemm_scaled call, all its dispatches (`rocprofv3 --pmc FETCH_SIZE`, "
+                 f"then `--pmc WRITE_SIZE`, median over calls), scaled by the counters' reading for a plain copy of "
                  f"{(copy_bytes or 0) >> 20} MiB (read scale {f_read:.4f}, write scale {f_write:.4f}):\n\n")
         fh.write(f"- read  {rd / 1e6:.1f} MB, write {wr / 1e6:.1f} MB, total {(rd + wr) / 1e6:.1f} MB\n")
         fh.write(f"- algorithmic (A and W codes once, residual once, output once): {gemm_bytes(wl) / 1e6:.1f} MB\n")
@@ -232,8 +271,11 @@ def cpu_baseline(wl, A16, W16, R16, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # MI355X's power controller throttles hard a few launches after an idle
+    # spell and needs ~100 launches (~60 ms) of this load to settle; the
+    # default warmup covers that so the timed steps see the sustained clock
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=3, help="rotating input/weight buffer sets")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
