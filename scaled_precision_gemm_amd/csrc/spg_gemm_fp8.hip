@@ -24,9 +24,9 @@
 //    fetches the chunk that belongs in its fixed LDS slot.
 //  * A stage is two K=64 sub-steps with two fragment register sets.  Two
 //    barriers per stage: after the stage's second fragment set is in
-//    registers ("slot free": the copy of stage kt+2 starts), and before the
-//    last 4 MFMAs ("stage kt+1 published": its first fragments are read while
-//    those MFMAs run).  A copy thus has about 1.4 stages to land.
+//    registers ("slot free": the copy of stage kt+2 starts), and after MFMA
+//    19 ("stage kt+1 published": its first fragments are read while the last
+//    12 MFMAs run).  A copy has between 21 and 43 MFMAs to land.
 //  * SWIGLU pairs weight rows inside one 256-row W tile (128 gate + 128 up).
 //  * XCD-aware tile order; optional split-K through the workspace;
 //    epilogue straight from registers with 8-byte stores (W fragments are the
@@ -196,8 +196,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     auto read_frags = [&](int slot, int ks, Frags &F, int r0, int r1) {
         const uint8_t *la = &lds[slot * kSlot];
         const uint8_t *lb = la + kOp;
+        // A fixed 16-trip loop with the range as a condition: it unrolls before
+        // the schedule's loop does, so every fragment index is a constant (a
+        // loop over r0 .. r1 can stay rolled, and then the fragment registers
+        // are indexed at run time, i.e. kept in scratch memory).
 #pragma unroll
-        for (int r = r0; r < r1; ++r) {
+        for (int r = 0; r < 16; ++r) {
+            if (r < r0 || r >= r1) continue;
             const int h = r & 1;
             if (r < 8) {
                 const int ni = r >> 1;
@@ -223,9 +228,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     // that the single wave per SIMD never stalls its MFMA issue for long:
     //   after MFMA 0..5   : the 16 fragment reads of F1 (sub-step 1, this stage)
     //   after MFMA 7      : F1 complete -> barrier: the stage's slot is free
-    //   after MFMA 8..23  : one copy instruction each for the stage after next
-    //   after MFMA 23     : own copy of the next stage landed -> barrier: published
-    //   after MFMA 24..31 : the 16 fragment reads of F0 (sub-step 0, next stage)
+    //   after MFMA 8..30  : the 16 copy instructions for the stage after next,
+    //                       two in every three MFMAs (at 8 + floor(3 i / 2))
+    //   after MFMA 19     : own copy of the next stage landed -> barrier: published
+    //   after MFMA 20..31 : the 16 fragment reads of F0 (sub-step 0, next stage)
+    // Spreading the copies over 24 MFMAs instead of 16 keeps the memory path's
+    // issue queue from filling (measured: steady stage 2565 -> 2470 cycles
+    // against the 2048 of the MFMAs alone).
     // "Next" runs on into the following tile of the workgroup, whose first two
     // stages are thus copied during the last two stages of the current tile
     // and land while its epilogue runs.  Stages alternate between the two
@@ -266,12 +275,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
                 wait_lds();
                 block_barrier();
             }
-            if (j >= 8 && j <= 23) issue_one(c2, slot, j - 8);
-            if (j == 23) {
-                wait_vmem<16>();               // stage G + 1 landed (stage G + 2 in flight)
+#pragma unroll
+            for (int ci = 0; ci < 16; ++ci)
+                if (j == 8 + (3 * ci) / 2) issue_one(c2, slot, ci);
+            if (j == 19) {
+                // copies 0..7 of stage G + 2 are issued by now (j <= 19)
+                wait_vmem<8>();                // stage G + 1 landed (stage G + 2 in flight)
                 block_barrier();
             }
-            if (!LAST && j >= 24) read_frags(slot ^ 1, 0, F0, (j - 24) * 2, (j - 24) * 2 + 2);
+            if (!LAST && j >= 20) read_frags(slot ^ 1, 0, F0, (j - 20) * 4 / 3, (j - 19) * 4 / 3);
             __builtin_amdgcn_sched_barrier(0);
         }
         ++G;
