@@ -400,15 +400,24 @@ def main():
     achieved = flops / (gemm_avg * 1e-3) / 1e12
     peak_key = "f16" if wl.fmt == "nvfp4" else "fp8"
     peak = PEAK_TFLOPS[peak_key]
+    # the GEMM is bound by whichever roof its arithmetic intensity reaches
+    # first: MFMA above the ridge (peak flops / HBM bandwidth), HBM below
+    alg_bytes = gemm_bytes(wl)
+    hbm_bound = flops / alg_bytes < peak * 1e12 / (HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved_v, peak_v, unit = alg_bytes / (gemm_avg * 1e-3) / 1e9, HBM_GBS, "GB/s"
+    else:
+        achieved_v, peak_v, unit = achieved, peak, "TFLOP/s"
     roofline = {
-        "bound": "mfma",
+        "bound": "hbm" if hbm_bound else "mfma",
         "kernel": "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel",
-        "achieved": round(achieved, 1),
-        "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4),
+        "achieved": round(achieved_v, 1),
+        "peak": peak_v,
+        "unit": unit,
+        "frac": round(achieved_v / peak_v, 4),
+        "gemm_tflops": round(achieved, 1),
         "traffic": traffic_from_profiles(wl, args.workload),
-        "algorithmic_bytes": gemm_bytes(wl),
+        "algorithmic_bytes": alg_bytes,
         "flops_per_launch": flops,
         "launch_ms_avg": round(gemm_avg, 4),
         "launch_ms_p10_p90": [round(float(np.percentile(gemm_ms, 10)), 4),
