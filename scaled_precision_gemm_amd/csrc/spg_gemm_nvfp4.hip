@@ -167,37 +167,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const G
     epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
 }
 
-// Decode for the fast path, with the hardware FP4 -> f16 conversion:
-// v_cvt_scalef32_pk_f16_fp4 multiplies by the power-of-two part of its f32
-// scale operand only, so S * 2^-7 is split as P * m with
-//   P = 2^(max(E, 1) - 14)        (exact; every e2m1 * P is a normal f16)
-//   m = (E > 0 ? 8 + M : M) / 8   (the E4M3 significand, exact in f16)
-// for a scale byte with exponent field E and mantissa field M; one packed
-// f16 multiply by m then gives e2m1 * S * 2^-7, exactly as decode8_f16.
-// Checked on the GPU against decode8_f16 for every code byte in every byte
-// position with every non-negative scale byte (the quantizer writes no
-// negative scales).
-struct BlockScale {
-    float p;
-    h2 m;
-};
-
-__device__ __forceinline__ BlockScale block_scale(uint32_t sb)
+// Decode for the fast path, with the hardware conversions.  Every E4M3
+// scale S is exact in f16, and v_cvt_scalef32_pk_f16_fp8 turns two scale
+// bytes into an f16 pair; a byte permute first puts the lane's scale byte in
+// both bytes of the converted word, giving (S, S).  v_cvt_scalef32_pk_f16_fp4
+// applies the power-of-two scale 2^-7 exactly, and one packed f16 multiply by
+// (S, S) gives e2m1 * S * 2^-7 with no rounding (at most 6 significant bits,
+// a multiple of 2^-17, so exact also where it is an f16 subnormal) - the
+// value decode8_f16 builds.  Checked on the GPU against the previous decode
+// of this path (scale split into a power of two for the conversion and an
+// f16 significand) for every code byte in every byte position, with every
+// non-negative scale byte in every byte position of its word.
+__device__ __forceinline__ h2 scale_pair(uint32_t word, uint32_t sel)
 {
-    const uint32_t E = (sb >> 3) & 15u, M = sb & 7u;
-    BlockScale b;
-    b.p = __uint_as_float(((E > 0 ? E : 1u) + 113u) << 23);
-    const _Float16 m = (_Float16)(float)((E > 0 ? 8u : 0u) + M) * (_Float16)0.125f;
-    b.m = h2{m, m};
-    return b;
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(word, word, sel), 1.0f, false);
 }
 
-__device__ __forceinline__ uint4 decode8_cvt(uint32_t w, const BlockScale &b)
+__device__ __forceinline__ uint4 decode8_cvt(uint32_t w, h2 s)
 {
-    const h2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 0) * b.m;
-    const h2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 1) * b.m;
-    const h2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 2) * b.m;
-    const h2 r3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, b.p, 3) * b.m;
+    const h2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0.0078125f, 0) * s;
+    const h2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0.0078125f, 1) * s;
+    const h2 r2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0.0078125f, 2) * s;
+    const h2 r3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0.0078125f, 3) * s;
     return make_uint4(__builtin_bit_cast(uint32_t, r0), __builtin_bit_cast(uint32_t, r1),
                       __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3));
 }
@@ -296,6 +287,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     // ---- fragment addressing ---------------------------------------------------
     const int l32 = lane & 31, khalf = lane >> 5;
     const uint32_t fx = ((uint32_t)l32 >> 1) & 7u;       // swizzle term of every fragment row
+    // v_perm selectors putting scale byte h (even chunks) or 2 + h (odd
+    // chunks) of a word in its low two bytes
+    const uint32_t sel_even = (uint32_t)khalf * 0x0101u, sel_odd = (2u + (uint32_t)khalf) * 0x0101u;
     uint32_t arow[4], wrow[4];
 #pragma unroll
     for (int y = 0; y < 4; ++y) arow[y] = (uint32_t)(wm * 128 + y * 32 + l32);
@@ -324,14 +318,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
             const uint32_t off = (((uint32_t)c ^ fx) << 4) + (uint32_t)khalf * 8;
             return *reinterpret_cast<const uint2 *>(base + (f < 4 ? arow[f] * 128 : kCodeOp + wrow[f - 4] * 128) + off);
         };
-        auto scale_of = [&](int c, int f) -> BlockScale {
-            const int b = 2 * c + khalf;               // block 2c + h of the stage
+        // block 2c + h of the stage: byte 2 (c & 1) + h of word c / 2
+        auto scale_of = [&](int c, int f) -> h2 {
             const uint4 &v = sc[f];
-            const uint32_t w = (b >> 2) == 0 ? v.x : (b >> 2) == 1 ? v.y : (b >> 2) == 2 ? v.z : v.w;
-            return block_scale((w >> (8 * (b & 3))) & 0xFFu);
+            const int wi = c >> 1;
+            const uint32_t w = wi == 0 ? v.x : wi == 1 ? v.y : wi == 2 ? v.z : v.w;
+            return scale_pair(w, (c & 1) ? sel_odd : sel_even);
         };
         uint2 code[2][8];
-        BlockScale bs[2][8];
+        h2 bs[2][8];
         uint4 fr[2][8];                                // decoded fragments of the current / next k-step
 #pragma unroll
         for (int f = 0; f < 8; ++f) code[0][f] = read_code(0, f);
