@@ -224,21 +224,25 @@ __device__ __forceinline__ void stage_scales(const GemmArgs &g, const Tile &T, f
 // Split-K, part 1: every K slice stores its fp32 partial tile and stops; a
 // second kernel (splitk_reduce_kernel) sums the slices once all have
 // finished - the kernel boundary orders the stores before the loads, so no
-// device-scope fence or counter is needed.  A lane's 16 accumulators of one
-// 32x32 block are stored contiguously (four 16-byte stores; a wave writes
-// 4 KiB contiguous per block): slice s of the launch's tile t (counted from
-// tile_begin), block b = 4 x + y, thread i starts at
-// ((t * S + s) * 16 + b) * 4096 + i * 16 floats.
+// device-scope fence or counter is needed.  Layout of one (tile, slice)
+// partial, 65536 floats: element 4q + r (q, r = 0..3) of block b = 4x + y of
+// thread i at (4b + q) * 1024 + 4i + r, so every store instruction of a wave
+// writes 1 KiB of whole cache lines.  (Storing a thread's 16 elements
+// contiguously instead made each instruction write 16 bytes into each of 32
+// lines: the 61 MB of partials of 1024 x 5120 x 17408 in three slices then
+// took ~45 us and the whole call 0.143 ms, against 0.095 ms now.)  Partial
+// (t, s) of a launch starts at float (t * S + s) * 65536, t counted from
+// tile_begin.
 __device__ __forceinline__ void splitk_store(const GemmArgs &g, const Tile &T, const Acc &acc)
 {
-    float *base = g.partials + ((T.global - g.tile_begin) * g.split_k + blockIdx.y) * (int64_t)(kBM * kBN) + threadIdx.x * 16;
+    float *base = g.partials + ((T.global - g.tile_begin) * g.split_k + blockIdx.y) * (int64_t)(kBM * kBN) + threadIdx.x * 4;
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk) {
-        v4f *dst = reinterpret_cast<v4f *>(base + blk * (kThreads * 16));
         const v16f &a = acc[blk >> 2][blk & 3];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            __builtin_nontemporal_store(v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, dst + q);
+            *reinterpret_cast<v4f *>(base + (blk * 4 + q) * (kThreads * 4)) =
+                v4f{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
     }
 }
 

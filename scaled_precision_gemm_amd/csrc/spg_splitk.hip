@@ -26,15 +26,17 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const GemmArgs 
     // held for block (x, y), so the GEMM's epilogue code applies unchanged.
     const int x = (int)blockIdx.y >> 2;    // SWIGLU: 0..1 (gate blocks), else 0..3
     const int y = (int)blockIdx.y & 3;
-    const float *tile_base = g.partials + (int64_t)blockIdx.x * g.split_k * (kBM * kBN) + threadIdx.x * 16;
+    // the layout splitk_store writes: element 4q + r of block b of thread i
+    // at (4b + q) * 1024 + 4i + r within a (tile, slice) partial
+    const float *tile_base = g.partials + (int64_t)blockIdx.x * g.split_k * (kBM * kBN) + threadIdx.x * 4;
     auto sum_block = [&](int blk) -> v16f {
         v16f t;
         for (int s = 0; s < g.split_k; ++s) {
-            const v4f *src = reinterpret_cast<const v4f *>(tile_base + ((int64_t)s * 16 + blk) * (kThreads * 16));
+            const float *src = tile_base + (int64_t)s * (kBM * kBN) + blk * 4 * (kThreads * 4);
             v16f p;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const v4f v = __builtin_nontemporal_load(src + q);
+                const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(src + q * (kThreads * 4)));
                 p[4 * q] = v[0];
                 p[4 * q + 1] = v[1];
                 p[4 * q + 2] = v[2];
