@@ -203,7 +203,8 @@ int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t
 
 /*
  * The plan gemm_scaled would launch for `d` on a device with `units` compute
- * units: tile shape, K-split, the number of workgroups and the tail split.
+ * units: tile shape, K-split, the number of workgroups and the tail (split
+ * along K, or run as half-height tiles).
  * Returns SPG_OK or the validation error gemm_scaled would return.  The
  * workspace holds one fp32 256x256 partial tile per split tile and slice.
  */
@@ -220,6 +221,10 @@ typedef struct spg_plan {
                              /* launch split tail_split ways along K (whole   */
                              /* rounds of tiles stay unsplit), else 1         */
     int64_t tail_tiles;
+    int32_t tail_bm;         /* output rows per workgroup of the tail launch: */
+                             /* 256, or 128 when the tail tiles run unsplit   */
+                             /* as two half-height tiles each (FP8 formats)   */
+    int32_t reserved;
 } spg_plan;
 
 int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units, spg_plan *plan);

@@ -51,6 +51,7 @@ class Plan(ctypes.Structure):
         ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32), ("split_k", ctypes.c_int32),
         ("tiles", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("kernel", ctypes.c_int32),
         ("tail_split", ctypes.c_int32), ("tail_tiles", ctypes.c_int64),
+        ("tail_bm", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 

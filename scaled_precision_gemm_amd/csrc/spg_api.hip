@@ -102,26 +102,45 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     p->kernel = d->format == SPG_FMT_NVFP4 ? 1 : 0;
     p->tail_split = 1;
     p->tail_tiles = 0;
-    // Tail split: when the tiles fill several whole rounds of the compute
-    // units plus a partial one, the whole rounds run unsplit and the
-    // remaining tiles run split along K in a second launch (so the last round
-    // is short instead of mostly idle).  Taken when the time it saves, from
-    // the per-unit rate these kernels reach (FP8 ~9.6, NVFP4 ~4.1 TFLOP/s per
-    // compute unit), exceeds the partial tiles' extra traffic (written and
-    // read back at ~4 TB/s) plus ~10 us of launches.
+    p->tail_bm = (int32_t)kTile;
+    // The tail: when the tiles fill several whole rounds of the compute units
+    // plus a partial one, the whole rounds run unsplit and the remaining
+    // tiles run in a second launch, so that the last round is short instead
+    // of mostly idle, in one of two ways:
+    //  - split along K into s slices (partial tiles through the workspace
+    //    and a reduction), or
+    //  - (FP8, at most half a round left) as two 128 x 256 half-height tiles
+    //    each, no partials.
+    // Each option's time for the last round is estimated from the per-unit
+    // rate these kernels reach (FP8 ~9.6, NVFP4 ~4.1 TFLOP/s per compute
+    // unit): a K split costs t_tile / s plus the partial tiles' traffic
+    // (written and read back at ~4 TB/s) and ~10 us of launches; a half tile
+    // ~0.55 t_tile (it carries the same copies per stage for half the MFMAs)
+    // plus ~5 us for its launch.  The cheapest of these and the unsplit round
+    // (t_tile) is taken.
     if (p->split_k == 1 && p->tiles > units && d->K > 0) {
         const int64_t rem = p->tiles % units;
         if (rem > 0) {
+            const double rate = d->format == SPG_FMT_NVFP4 ? 4.1e12 : 9.6e12;
+            const double t_tile = 2.0 * kTile * kTile * (double)d->K / rate;
+            double best = t_tile;
             int s = (int)(units / rem < 8 ? units / rem : 8);
             while (s > 1 && (d->K / s < 1024 || cdiv(d->K, s) < 2 * (int64_t)p->bk)) --s;
             if (s >= 2) {
-                const double rate = d->format == SPG_FMT_NVFP4 ? 4.1e12 : 9.6e12;
-                const double t_tile = 2.0 * kTile * kTile * (double)d->K / rate;
-                const double gain = t_tile * (1.0 - 1.0 / s);
-                const double cost = 2.0 * (double)rem * s * kTile * kTile * 4.0 / 4e12 + 10e-6;
-                if (gain > cost) {
+                const double t = t_tile / s + 2.0 * (double)rem * s * kTile * kTile * 4.0 / 4e12 + 10e-6;
+                if (t < best) {
+                    best = t;
                     p->tail_tiles = rem;
                     p->tail_split = s;
+                }
+            }
+            if (p->kernel == 0 && 2 * rem <= units && cdiv(d->K, p->bk) >= 2) {
+                const double t = 0.55 * t_tile + 5e-6;
+                if (t < best) {
+                    best = t;
+                    p->tail_tiles = rem;
+                    p->tail_split = 1;
+                    p->tail_bm = (int32_t)(kTile / 2);
                 }
             }
         }
@@ -284,7 +303,13 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     spg_plan pm = p;
     pm.tiles = g.tile_count;
     hipError_t e = launch(g, pm);
-    if (e == hipSuccess && p.tail_tiles > 0) {
+    if (e == hipSuccess && p.tail_tiles > 0 && p.tail_bm < kTile) {
+        // the tail: the last tail_tiles tiles as half-height tiles
+        GemmArgs gt = g;
+        gt.tile_begin = p.tiles - p.tail_tiles;
+        gt.tile_count = p.tail_tiles;
+        e = launch_gemm_fp8_half(gt, s);
+    } else if (e == hipSuccess && p.tail_tiles > 0) {
         // the tail: the last tail_tiles tiles, split along K, then reduced
         GemmArgs gt = g;
         gt.tile_begin = p.tiles - p.tail_tiles;

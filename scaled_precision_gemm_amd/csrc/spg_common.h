@@ -127,6 +127,7 @@ inline FastDiv make_fastdiv(uint32_t d)
 }
 
 hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s);
+hipError_t launch_gemm_fp8_half(const GemmArgs &g, hipStream_t s);   // tiles tile_begin.. as 128-row halves
 hipError_t launch_gemm_nvfp4(const GemmArgs &g, const spg_plan &p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs &g, int64_t tiles, hipStream_t s);
 hipError_t launch_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t K, int64_t ldx,

@@ -137,10 +137,24 @@ __device__ __forceinline__ Tile tile_from_id(const GemmArgs &g, int64_t t)
     return T;
 }
 
-template <int EPI>
-__device__ __forceinline__ Tile tile_of(const GemmArgs &g)
+// Work item of a launch over tile_count * split_k workgroups (1-D grid): the
+// tile (counted from tile_begin) and its K slice.  Work ids run slice-major
+// (all tiles of slice 0, then slice 1, ...) and each XCD takes one
+// contiguous range of them, so the workgroups sharing an XCD's L2 mostly
+// work on the same K slice of neighbouring tiles and share its A and W
+// panels (ordering tiles first, slices last, would give every XCD all
+// slices of fewer tiles: about twice the distinct panel bytes per XCD).
+struct WorkItem {
+    int64_t tile;
+    int split;
+};
+
+__device__ __forceinline__ WorkItem work_item(const GemmArgs &g)
 {
-    return tile_from_id<EPI>(g, g.tile_begin + xcd_remap(blockIdx.x, gridDim.x));
+    const uint32_t n = (uint32_t)(g.tile_count * g.split_k);
+    const uint32_t v = (uint32_t)xcd_remap(blockIdx.x, n);
+    const uint32_t s = v / (uint32_t)g.tile_count;
+    return WorkItem{(int64_t)(v - s * (uint32_t)g.tile_count), (int)s};
 }
 
 // W row of tile row r (0..255) and whether it exists.  SWIGLU: rows 0..127
@@ -233,9 +247,9 @@ __device__ __forceinline__ void stage_scales(const GemmArgs &g, const Tile &T, f
 // took ~45 us and the whole call 0.143 ms, against 0.095 ms now.)  Partial
 // (t, s) of a launch starts at float (t * S + s) * 65536, t counted from
 // tile_begin.
-__device__ __forceinline__ void splitk_store(const GemmArgs &g, const Tile &T, const Acc &acc)
+__device__ __forceinline__ void splitk_store(const GemmArgs &g, const Tile &T, int split, const Acc &acc)
 {
-    float *base = g.partials + ((T.global - g.tile_begin) * g.split_k + blockIdx.y) * (int64_t)(kBM * kBN) + threadIdx.x * 4;
+    float *base = g.partials + ((T.global - g.tile_begin) * g.split_k + split) * (int64_t)(kBM * kBN) + threadIdx.x * 4;
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk) {
         const v16f &a = acc[blk >> 2][blk & 3];
@@ -371,7 +385,9 @@ constexpr int kEpiRegionBytes = 4 * 4096;   // per workgroup
 // FULL: the wave's whole quadrant lies inside the output (and residual) and
 // both are 16-byte aligned with row strides a multiple of 8 elements - no
 // bounds checks or narrow-store paths, hence no per-store branches.
-template <int EPI, bool FULL>
+// MI: 32-row A blocks per wave (4; 2 in a half-height tile, whose waves
+// hold acc[x][0..1] and cover token rows wm * 64 .. wm * 64 + 63).
+template <int EPI, bool FULL, int MI = 4>
 __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
                                               const float *lds_sw, uint8_t *region)
 {
@@ -396,10 +412,10 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
     // write (the compiler cannot move LDS reads across LDS writes it cannot
     // prove disjoint, so reading them per element would wait on each)
     constexpr int NX = SW ? 2 : 4;
-    float sa_r[4];
+    float sa_r[MI];
     v4f sw_r[NX][4], swu_r[SW ? 2 : 1][4];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) sa_r[y] = lds_sa[wm * 128 + y * 32 + l32];
+    for (int y = 0; y < MI; ++y) sa_r[y] = lds_sa[wm * (MI * 32) + y * 32 + l32];
 #pragma unroll
     for (int x = 0; x < NX; ++x)
 #pragma unroll
@@ -410,8 +426,8 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
         }
 
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-        const int64_t row0 = T.m0 + wm * 128 + y * 32;
+    for (int y = 0; y < MI; ++y) {
+        const int64_t row0 = T.m0 + wm * (MI * 32) + y * 32;
         const int rows_valid = FULL ? 32 : (int)min((int64_t)32, g.M - row0);
         if (rows_valid <= 0) break;                                 // uniform per wave
         const float sa = sa_r[y];
@@ -512,7 +528,7 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
 }
 
 // Fused epilogue of the whole tile (no split).
-template <int EPI>
+template <int EPI, int MI = 4>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
                                          const float *lds_sw, uint8_t *region)
 {
@@ -520,13 +536,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave >> 1, wn = wave & 1;
     const EpiOut o = epi_out<EPI>(g, T);
-    const bool full = T.m0 + wm * 128 + 128 <= g.M && T.c0 + (SW ? wn * 64 + 64 : wn * 128 + 128) <= o.nvalid &&
+    const bool full = T.m0 + wm * (MI * 32) + MI * 32 <= g.M && T.c0 + (SW ? wn * 64 + 64 : wn * 128 + 128) <= o.nvalid &&
                       (((uintptr_t)o.out) & 15) == 0 && (g.ldo & 7) == 0 &&
                       (EPI != SPG_EPI_ADD || ((((uintptr_t)o.res) & 15) == 0 && (g.ldr & 7) == 0));
     if (full)
-        epilogue_impl<EPI, true>(g, T, acc, lds_sa, lds_sw, region);
+        epilogue_impl<EPI, true, MI>(g, T, acc, lds_sa, lds_sw, region);
     else
-        epilogue_impl<EPI, false>(g, T, acc, lds_sa, lds_sw, region);
+        epilogue_impl<EPI, false, MI>(g, T, acc, lds_sa, lds_sw, region);
 }
 
 }  // namespace gemm

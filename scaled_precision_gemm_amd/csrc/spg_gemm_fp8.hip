@@ -74,13 +74,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     // Tiles of this workgroup: virtual workgroup ids blockIdx.x + i * gridDim.x
     // (a persistent grid of one workgroup per compute unit walks the same
     // XCD-aware order a one-tile-per-workgroup launch would).
+    // A split launch has one workgroup per (tile, K slice) work item.
     const int64_t total = g.tile_count;
-    const int ntile = (int)((total - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x);
+    const WorkItem wi = SPLIT ? work_item(g) : WorkItem{0, 0};
+    const int ntile = SPLIT ? 1 : (int)((total - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x);
     auto tile_i = [&](int i) -> Tile {
+        if (SPLIT) return tile_from_id<EPI>(g, g.tile_begin + wi.tile);
         return tile_from_id<EPI>(g, g.tile_begin + xcd_remap((int64_t)blockIdx.x + (int64_t)i * gridDim.x, total));
     };
 
-    const int split = blockIdx.y;
+    // (unsplit: blockIdx.y is 0; kept as a run-time value because folding
+    // the constant changes the register allocation of the whole kernel and
+    // measured 13% slower on 4096 x 34816 x 5120)
+    const int split = SPLIT ? wi.split : (int)blockIdx.y;
     const int64_t k_begin = (int64_t)split * g.k_chunk;
     const int64_t k_end = min(g.K, k_begin + g.k_chunk);
     const int nk = (int)((k_end - k_begin + kBK - 1) / kBK);
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         if (nk > 0) stage(acc, nk - 1, std::true_type{});
 
         if (SPLIT) {
-            splitk_store(g, Tc, acc);          // the slices are summed by splitk_reduce_kernel
+            splitk_store(g, Tc, split, acc);   // the slices are summed by splitk_reduce_kernel
         } else {
             epilogue<EPI>(g, Tc, acc, lds_scale[i & 1][0], lds_scale[i & 1][1],
                           &lds[2 * kSlot + wave * (kEpiRegionBytes / 4)]);
@@ -326,12 +332,229 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     wait_vmem<0>();   // no copy into LDS may still be in flight when the workgroup ends
 }
 
+// ---------------------------------------------------------------------------
+// Half-height tiles for a short last round.  When the tiles leave a last
+// round that fills at most half of the compute units (4096 x 34816 x 5120
+// SwiGLU: 2176 tiles = 8.5 rounds of 256), those tiles run in a second launch
+// as 128 x 256 halves, one per workgroup, so the round is spread over every
+// compute unit and takes about half as long; unlike a K split this needs no
+// partial tiles and no reduction.
+//
+// Same data path as the full kernel (direct-to-LDS copies of 128-byte row
+// segments, the same swizzle, W fragments first), with the A side halved:
+// waves (wm, wn) hold 64 token rows x 128 weight rows (2 x 4 blocks of
+// 32x32), and a stage is 16 MFMAs.  A stage of the slot holds 128 A rows
+// (16 KiB) and 256 W rows (32 KiB); three slots, so a copy is issued two
+// stages ahead of its use and still has ~30 MFMAs to land.  Per stage:
+//   after MFMA 0..3   : the 12 fragment reads of F1 (sub-step 1)
+//   after MFMA 5      : F1 complete -> barrier: this stage's slot is free
+//   after MFMA 6..13  : the 12 copies of the stage three ahead into it
+//   after MFMA 9      : the next stage landed -> barrier: published
+//   after MFMA 10..15 : the 12 fragment reads of F0 of the next stage
+// ---------------------------------------------------------------------------
+constexpr int kHalfRows = 128;                     // A rows of a half tile
+constexpr int kOpAh = kHalfRows * kBK;             // A bytes of one stage: 16 KiB
+constexpr int kSlotH = kOpAh + kOp;                // A + W of one stage: 48 KiB
+constexpr int kSlotsH = 3;
+
+struct FragsH {
+    uint4 a[2][2], b[4][2];
+};
+
+template <int EPI, int SMODE>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmArgs g)
+{
+    __shared__ __attribute__((aligned(2048))) uint8_t lds[kSlotsH * kSlotH];
+    __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
+    __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // work item v: half v & 1 of tile tile_begin + v / 2 (the two halves of a
+    // tile are neighbours in the XCD-aware order and share its W panel)
+    const uint32_t v = (uint32_t)xcd_remap(blockIdx.x, (int64_t)2 * g.tile_count);
+    Tile T = tile_from_id<EPI>(g, g.tile_begin + (v >> 1));
+    T.m0 += (int64_t)(v & 1u) * kHalfRows;
+    if (T.m0 >= g.M) return;                       // lower half of a ragged last tile row
+
+    // The scale factors are written to LDS after the main loop: a wait the
+    // compiler inserts for these loads would also wait for every copy.
+    float va, vw;
+    scale_values<EPI, SMODE>(g, T, va, vw);
+
+    const int nk = (int)((g.K + kBK - 1) / kBK);
+    const int64_t Nh = g.N / 2;
+
+    // ---- copy setup (as the full kernel; wave w copies A rows 32 w .. 32 w + 31
+    // in four 8-row blocks and W rows 64 w .. 64 w + 63 in eight) -------------
+    const uint8_t *A = g.A + (g.stride_a ? T.b * g.stride_a : 0);
+    const uint8_t *W = g.W + (g.stride_w ? T.b * g.stride_w : 0);
+    const int64_t a_rows = min((int64_t)kHalfRows, g.M - T.m0);
+    int64_t w_first, w_rows;
+    if (EPI == SPG_EPI_SWIGLU) {
+        w_rows = min((int64_t)128, Nh - T.n0);
+        w_first = (wave < 2 ? T.n0 : Nh + T.n0);
+    } else {
+        const int64_t half0 = T.n0 + (wave < 2 ? 0 : 128);
+        w_rows = min((int64_t)128, g.N - half0);
+        w_first = half0;
+    }
+    w_rows = max(w_rows, (int64_t)0);
+    const v4i rs_a = make_rsrc(A + T.m0 * g.lda, (uint32_t)(a_rows * g.lda));
+    const v4i rs_w = make_rsrc(W + w_first * g.ldw, (uint32_t)(w_rows * g.ldw));
+    const int ln = lane_id();
+    const uint32_t rib = (uint32_t)ln >> 3, pchunk = (uint32_t)ln & 7;
+    // 8-row blocks start at multiples of 8 rows, so the swizzle term of a
+    // lane is 4 (block & 1) + lane / 16 (mod 8), for A (rows 32 w + 8 i) as
+    // for W (rows 64 w + 8 i)
+    const uint32_t c_even = pchunk ^ (((uint32_t)ln >> 4) & 7u);
+    const uint32_t c_odd = pchunk ^ ((4u + ((uint32_t)ln >> 4)) & 7u);
+    const uint32_t ra0 = (uint32_t)(wave * 32) + rib;
+    const uint32_t rw0 = (uint32_t)((wave & 1) * 64) + rib;
+    const uint32_t va_e = ra0 * (uint32_t)g.lda + c_even * 16u, va_o = ra0 * (uint32_t)g.lda + c_odd * 16u;
+    const uint32_t vw_e = rw0 * (uint32_t)g.ldw + c_even * 16u, vw_o = rw0 * (uint32_t)g.ldw + c_odd * 16u;
+    const uint32_t lds_base =
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&lds[0];
+
+    struct StageCopy {
+        uint32_t soff, a_e, a_o, w_e, w_o;
+    };
+    // offsets of stage kt; kOOB for bytes past K and for stages past the end
+    // (zeros into a slot nobody reads again: every wait count stays uniform)
+    auto plan_stage = [&](int kt) -> StageCopy {
+        const bool exists = kt < nk;
+        const int64_t k0 = (int64_t)kt * kBK;
+        const bool full = k0 + kBK <= g.K;
+        const bool in_e = exists && (full || k0 + (int64_t)c_even * 16 < g.K);
+        const bool in_o = exists && (full || k0 + (int64_t)c_odd * 16 < g.K);
+        StageCopy c;
+        c.soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)(exists ? k0 : 0));
+        c.a_e = in_e ? va_e : kOOB;
+        c.a_o = in_o ? va_o : kOOB;
+        c.w_e = in_e ? vw_e : kOOB;
+        c.w_o = in_o ? vw_o : kOOB;
+        return c;
+    };
+    // copy instruction idx (0..11) of a stage: W, W, A, W, W, A, ... (W blocks
+    // 0..7, A blocks 0..3)
+    auto issue_one = [&](const StageCopy &c, int slot, int idx) {
+        const uint32_t sb = lds_base + (uint32_t)(slot * kSlotH);
+        if (idx % 3 == 2) {
+            const int i = idx / 3;
+            const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)(sb + (uint32_t)(wave * 32 * kBK) + (uint32_t)(i * 8 * kBK)));
+            dma16(la, ((i & 1) ? c.a_o : c.a_e) + (uint32_t)(8 * i) * (uint32_t)g.lda, rs_a, c.soff);
+        } else {
+            const int i = (idx / 3) * 2 + (idx % 3);
+            const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)(sb + (uint32_t)kOpAh + (uint32_t)(wave * 64 * kBK) + (uint32_t)(i * 8 * kBK)));
+            dma16(la, ((i & 1) ? c.w_o : c.w_e) + (uint32_t)(8 * i) * (uint32_t)g.ldw, rs_w, c.soff);
+        }
+    };
+
+    // ---- fragments: reads 0..7 are the W halves, 8..11 the A halves -----------
+    const uint32_t l32 = (uint32_t)ln & 31, khalf = (uint32_t)ln >> 5, fx = (l32 >> 1) & 7u;
+    uint32_t foff[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            foff[ks][h] = l32 * kBK + ((((uint32_t)ks * 4 + khalf * 2 + (uint32_t)h) ^ fx) << 4);
+    auto read_frags = [&](int slot, int ks, FragsH &F, int r0, int r1) {
+        const uint8_t *la = &lds[slot * kSlotH];
+        const uint8_t *lb = la + kOpAh;
+#pragma unroll
+        for (int r = 0; r < 12; ++r) {
+            if (r < r0 || r >= r1) continue;
+            const int h = r & 1;
+            if (r < 8) {
+                const int ni = r >> 1;
+                F.b[ni][h] = *reinterpret_cast<const uint4 *>(lb + (uint32_t)wtile_row0<EPI>(wn, ni) * kBK + foff[ks][h]);
+            } else {
+                const int mi = (r - 8) >> 1;
+                F.a[mi][h] = *reinterpret_cast<const uint4 *>(la + (uint32_t)(wm * 64 + mi * 32) * kBK + foff[ks][h]);
+            }
+        }
+    };
+
+    FragsH F0, F1;
+    {
+        const StageCopy c0 = plan_stage(0), c1 = plan_stage(1), c2 = plan_stage(2);
+#pragma unroll
+        for (int idx = 0; idx < 12; ++idx) issue_one(c0, 0, idx);
+#pragma unroll
+        for (int idx = 0; idx < 12; ++idx) issue_one(c1, 1, idx);
+#pragma unroll
+        for (int idx = 0; idx < 12; ++idx) issue_one(c2, 2, idx);
+        wait_vmem<24>();                           // stage 0 landed (and the scale loads)
+        block_barrier();
+        read_frags(0, 0, F0, 0, 12);
+    }
+
+    Acc acc;                                       // blocks acc[x][0..1] are used
+    zero_acc(acc);
+    int slot = 0;                                  // slot of stage kt = kt % 3
+    auto stage = [&](int kt, auto last_c) {
+        constexpr bool LAST = decltype(last_c)::value;
+        const int next = slot == 2 ? 0 : slot + 1;
+        const StageCopy c3 = plan_stage(kt + 3);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int mi = (j & 7) >> 2, ni = j & 3;
+            const FragsH &F = j < 8 ? F0 : F1;
+            acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(F.b[ni]), op(F.a[mi]), acc[ni][mi],
+                                                                          0, 0, 0, 0, 0, 0);
+            if (j <= 3) read_frags(slot, 1, F1, j * 3, j * 3 + 3);
+            if (j == 5) {
+                wait_lds();
+                block_barrier();                   // every wave is done with this slot
+            }
+#pragma unroll
+            for (int ci = 0; ci < 12; ++ci)
+                if (j == 6 + (2 * ci) / 3) issue_one(c3, slot, ci);
+            if (j == 9) {
+                // copies 0..5 of stage kt + 3 are issued by now; stage kt + 2
+                // (12) is older: everything before them, stage kt + 1, landed
+                wait_vmem<18>();
+                block_barrier();
+            }
+            if (!LAST && j >= 10) read_frags(next, 0, F0, (j - 10) * 2, (j - 10) * 2 + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        slot = next;
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::false_type{});
+    if (nk > 0) stage(nk - 1, std::true_type{});
+
+    // no copy may still be landing in LDS: the epilogue's staging region
+    // overlaps the slots
+    wait_vmem<0>();
+    lds_sa[tid] = va;
+    lds_sw[tid] = vw;
+    block_barrier();
+    epilogue<EPI, 2>(g, T, acc, lds_sa, lds_sw, &lds[wave * (kEpiRegionBytes / 4)]);
+}
+
+template <int EPI>
+hipError_t launch_half(const GemmArgs &g, hipStream_t s)
+{
+    const dim3 grid((unsigned)(2 * g.tile_count));
+    if (g.format == SPG_FMT_E4M3_ROW)
+        gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_ROW><<<grid, kThreads, 0, s>>>(g);
+    else
+        gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_TENSOR><<<grid, kThreads, 0, s>>>(g);
+    return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 {
-    // p.workgroups: one per (tile, slice), or a persistent grid of at most
-    // one per compute unit for unsplit products with two or more K stages.
-    dim3 grid((unsigned)(p.workgroups / g.split_k), (unsigned)g.split_k, 1);
+    // p.workgroups: one per (tile, slice) work item, or a persistent grid of
+    // at most one per compute unit for unsplit products with two or more K
+    // stages.
+    const dim3 grid((unsigned)p.workgroups);
     const bool split = g.split_k > 1;
     if (g.format == SPG_FMT_E4M3_ROW) {
         if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true><<<grid, kThreads, 0, s>>>(g);
@@ -346,6 +569,15 @@ hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t launch_gemm_fp8_half(const GemmArgs &g, hipStream_t s)
+{
+    switch (g.epilogue) {
+    case SPG_EPI_STORE: return launch_half<SPG_EPI_STORE>(g, s);
+    case SPG_EPI_ADD: return launch_half<SPG_EPI_ADD>(g, s);
+    default: return launch_half<SPG_EPI_SWIGLU>(g, s);
+    }
+}
 
 hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 {

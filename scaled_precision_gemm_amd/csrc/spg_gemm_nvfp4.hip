@@ -72,9 +72,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const G
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const Tile T = tile_of<EPI>(g);
+    const WorkItem wi = work_item(g);
+    const Tile T = tile_from_id<EPI>(g, g.tile_begin + wi.tile);
 
-    const int split = blockIdx.y;
+    const int split = wi.split;
     const int64_t k_begin = (int64_t)split * g.k_chunk;
     const int64_t k_end = min(g.K, k_begin + g.k_chunk);
     const int nk = (int)((k_end - k_begin + kBK - 1) / kBK);
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const G
     }
 
     if (g.split_k > 1) {
-        splitk_store(g, T, acc);      // the slices are summed by splitk_reduce_kernel
+        splitk_store(g, T, split, acc);   // the slices are summed by splitk_reduce_kernel
         return;
     }
     epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
@@ -227,8 +228,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const Tile T = tile_of<EPI>(g);
-    const int64_t k_begin = (int64_t)blockIdx.y * g.k_chunk;
+    const WorkItem wi = work_item(g);
+    const Tile T = tile_from_id<EPI>(g, g.tile_begin + wi.tile);
+    const int64_t k_begin = (int64_t)wi.split * g.k_chunk;
     const int64_t k_end = min(g.K, k_begin + g.k_chunk);
     const int nk = (int)((k_end - k_begin) / kBKF);       // whole stages (K, k_chunk multiples of 256)
     const int64_t Nh = g.N / 2, G = g.K / 16;            // scale bytes per row
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     __syncthreads();
 
     if (SPLIT) {
-        splitk_store(g, T, acc);                 // the slices are summed by splitk_reduce_kernel
+        splitk_store(g, T, wi.split, acc);       // the slices are summed by splitk_reduce_kernel
         return;
     }
     epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // slots free after the barrier
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
 {
-    dim3 grid((unsigned)p.tiles, (unsigned)g.split_k, 1);
+    const dim3 grid((unsigned)(p.tiles * g.split_k));    // (tile, slice) work items, see work_item
     // the fast path copies 16-byte pieces of the scale planes: both must be
     // 16-byte aligned (rows are, since K / 16 is then a multiple of 16)
     const bool fast = p.bk == kBKF && (((uintptr_t)g.sa | (uintptr_t)g.sw) & 15) == 0;

@@ -473,3 +473,65 @@ def test_gemm_tail_split_sampled(spg, fmt, K):
         D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
         y, S, _ = oracle.epilogue("store", D, Da, sa_o, sw_o, None)
     check_close(np.ascontiguousarray(gpu[np.ix_(rows, cols)]), y, S, f"tail split {fmt} K={K}")
+
+
+# ---------------------------------------------------------------------------
+# half-height tail: 272 (or 544) tiles on 256 compute units; the last round's
+# tiles run as 128-row halves in a second launch.  Every output column of the
+# tail's tile columns is checked on sampled rows of both halves, with ragged
+# M (a last tile row whose lower half is partly or wholly empty), ragged N, a
+# K tail inside a stage, SwiGLU pairing and per-tensor batches.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,epi,fmt,B", [
+    (4096, 4352, 1024, "store", "e4m3_row", 1),
+    (4000, 4312, 1040, "add", "e4m3_row", 1),
+    (3900, 8704, 1024, "swiglu", "e4m3_row", 1),
+    (2048, 4352, 1024, "store", "e4m3_tensor", 2),
+], ids=["store", "add_ragged", "swiglu_ragged", "tensor_batch2"])
+def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
+    plan = spg.gemm_plan(M, N, K, fmt, epi, batch=B)
+    assert plan["tail_bm"] == 128 and plan["tail_tiles"] in (16, 32) and plan["tail_split"] == 1
+    rng = np.random.default_rng(M + N + K)
+    A16 = bf16_normal((B, M, K) if B > 1 else (M, K), 1.0, 80)
+    W16 = bf16_normal((N, K), 0.02, 81)
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, 82) if epi == "add" else None
+    A, W = dev(A16), dev(W16)
+    if fmt == "e4m3_row":
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=dev(R16) if R16 is not None else None)
+    else:
+        qa, sa = spg.quantize_tensor(A)
+        qw, sw = spg.quantize_tensor(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, fmt="e4m3_tensor")
+    torch.cuda.synchronize()
+    gpu = host_u16(out)
+    del A, W, qa, qw, out
+    torch.cuda.empty_cache()
+    # tail tile columns: the last tiles in the raster order sit in the last
+    # group of eight tile rows, at the highest tile columns
+    tile_n = 128 if epi == "swiglu" else 256
+    first_tail_col = ((n_out + tile_n - 1) // tile_n - (2 if plan["tail_tiles"] == 16 else 4)) * tile_n
+    cols = np.unique(np.concatenate([sample(n_out, 16, rng), np.arange(first_tail_col, n_out)]))
+    wrows = np.concatenate([cols, cols + N // 2]) if epi == "swiglu" else cols
+    for b in range(B):
+        Ab = A16[b] if B > 1 else A16
+        g = gpu[b] if B > 1 else gpu
+        last = ((M - 1) // 256) * 256       # first row of the last tile row
+        rows = np.unique(np.concatenate([sample(M, 24, rng), rng.choice(np.arange(M // 2, M), 24, replace=False),
+                                         [M // 2, M // 2 + 127, M // 2 + 128, last, min(last + 127, M - 1),
+                                          min(last + 128, M - 1), M - 1]]))
+        Rs = np.ascontiguousarray(R16[np.ix_(rows, cols)]) if R16 is not None else None
+        if fmt == "e4m3_row":
+            qa_o, sa_o = oracle.quantize_rowwise(np.ascontiguousarray(Ab[rows]))
+            qw_o, sw_o = oracle.quantize_rowwise(np.ascontiguousarray(W16[wrows]))
+        else:
+            sa_o = oracle.amax(Ab) / np.float32(448.0)
+            sw_o = oracle.amax(W16) / np.float32(448.0)
+            qa_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(Ab[rows]), sa_o)
+            qw_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(W16[wrows]), sw_o)
+        D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+        y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, Rs)
+        check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"half tail {M}x{N}x{K} {epi} {fmt} batch {b}")

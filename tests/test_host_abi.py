@@ -217,13 +217,22 @@ def test_plans_for_the_workloads(spg):
     p = spg.gemm_plan(4096, 5120, 6144, "nvfp4", "add")
     assert (p["tiles"], p["split_k"], p["bk"], p["workgroups"]) == (320, 1, 256, 256)
     assert (p["tail_tiles"], p["tail_split"]) == (64, 4)
-    # FP8 at T=4096 SwiGLU: 8.5 rounds, but a half round of 70 us tiles does
-    # not pay for the partial-tile traffic
+    # FP8 at T=4096 SwiGLU: 8.5 rounds; a K split of the last half round of
+    # 70 us tiles does not pay for the partial-tile traffic, half-height
+    # tiles (no partials) do: 8 whole rounds, then 256 halves of 128 tiles
     p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu")
-    assert (p["tail_tiles"], p["tail_split"]) == (0, 1)
+    assert (p["workgroups"], p["tail_tiles"], p["tail_split"], p["tail_bm"]) == (256, 128, 1, 128)
+    # short K, 16 tiles left: half-height tiles (a K split of 1024 is too short)
+    p = spg.gemm_plan(4096, 4352, 1024, "e4m3_row", "store")
+    assert (p["tiles"], p["tail_tiles"], p["tail_split"], p["tail_bm"]) == (272, 16, 1, 128)
+    # more than half a round left: no half-height tail (it would take 2 rounds)
+    p = spg.gemm_plan(4096, 4096 + 12 * 256, 5120, "e4m3_row", "store")
+    assert p["tiles"] == 16 * 28 and p["tail_bm"] == 256
+    # NVFP4 has no half-height kernel
+    assert spg.gemm_plan(4096, 5120, 6144, "nvfp4", "add")["tail_bm"] == 256
     # long K: worth it for FP8 too (K / 8 still >= 1024)
     p = spg.gemm_plan(4096, 4352, 16384, "e4m3_row", "store")
-    assert (p["tiles"], p["workgroups"], p["tail_tiles"], p["tail_split"]) == (272, 256, 16, 8)
+    assert (p["tiles"], p["workgroups"], p["tail_tiles"], p["tail_split"], p["tail_bm"]) == (272, 256, 16, 8, 256)
     # whole rounds: no tail
     p = spg.gemm_plan(8192, 8192, 8192, "e4m3_tensor", "store")
     assert (p["tail_tiles"], p["tail_split"]) == (0, 1)
