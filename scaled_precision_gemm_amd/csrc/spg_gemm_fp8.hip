@@ -345,12 +345,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 // waves (wm, wn) hold 64 token rows x 128 weight rows (2 x 4 blocks of
 // 32x32), and a stage is 16 MFMAs.  A stage of the slot holds 128 A rows
 // (16 KiB) and 256 W rows (32 KiB); three slots, so a copy is issued two
-// stages ahead of its use and still has ~30 MFMAs to land.  Per stage:
+// stages ahead of its use and still has ~25 MFMAs to land, and one barrier
+// per stage both frees the current slot and publishes the next.  Per stage:
 //   after MFMA 0..3   : the 12 fragment reads of F1 (sub-step 1)
-//   after MFMA 5      : F1 complete -> barrier: this stage's slot is free
-//   after MFMA 6..13  : the 12 copies of the stage three ahead into it
-//   after MFMA 9      : the next stage landed -> barrier: published
-//   after MFMA 10..15 : the 12 fragment reads of F0 of the next stage
+//   after MFMA 5      : F1 complete and the next stage landed -> barrier
+//   after MFMA 6..13  : the 12 copies of the stage three ahead into this slot
+//   after MFMA 8..11  : the 12 fragment reads of F0 of the next stage (F0's
+//                       last MFMA is 7)
 // ---------------------------------------------------------------------------
 constexpr int kHalfRows = 128;                     // A rows of a half tile
 constexpr int kOpAh = kHalfRows * kBK;             // A bytes of one stage: 16 KiB
@@ -508,19 +509,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
                                                                           0, 0, 0, 0, 0, 0);
             if (j <= 3) read_frags(slot, 1, F1, j * 3, j * 3 + 3);
             if (j == 5) {
+                // in flight: stages kt + 1 and kt + 2 (12 copies each, oldest
+                // first); stage kt + 3 is not issued yet
                 wait_lds();
-                block_barrier();                   // every wave is done with this slot
+                wait_vmem<12>();
+                block_barrier();                   // this slot is free, stage kt + 1 published
             }
 #pragma unroll
             for (int ci = 0; ci < 12; ++ci)
                 if (j == 6 + (2 * ci) / 3) issue_one(c3, slot, ci);
-            if (j == 9) {
-                // copies 0..5 of stage kt + 3 are issued by now; stage kt + 2
-                // (12) is older: everything before them, stage kt + 1, landed
-                wait_vmem<18>();
-                block_barrier();
-            }
-            if (!LAST && j >= 10) read_frags(next, 0, F0, (j - 10) * 2, (j - 10) * 2 + 2);
+            if (!LAST && j >= 8 && j <= 11) read_frags(next, 0, F0, (j - 8) * 3, (j - 8) * 3 + 3);
             __builtin_amdgcn_sched_barrier(0);
         }
         slot = next;
