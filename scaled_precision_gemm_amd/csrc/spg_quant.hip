@@ -16,6 +16,8 @@
 // correctly rounded reference.
 #include "spg_common.h"
 
+#include <type_traits>
+
 namespace spg {
 
 namespace {
@@ -65,25 +67,36 @@ __device__ __forceinline__ RowScale row_scale(float amax)
     return t;
 }
 
+// SCALED: the row needs the 2^100 scaling (k != 1); the common case skips
+// the multiplications by k (exact either way: k = 1 makes them identities).
+// The clamp is one v_med3_f32.
+template <bool SCALED>
 __device__ __forceinline__ float quot(float x, const RowScale &t)
 {
-    const float xs = x * t.k;
+    const float xs = SCALED ? x * t.k : x;
     const float q0 = xs * t.r;
     const float e = __builtin_fmaf(-q0, t.ss, xs);
     const float q = __builtin_copysignf(__builtin_fmaf(e, t.r, q0), x);
-    return __builtin_fminf(__builtin_fmaxf(q, -448.0f), 448.0f);
+    return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
 }
 
-// Encode 8 bf16 values (one 16-byte vector) to 8 E4M3 codes.
+// Encode 8 bf16 values (one 16-byte vector) to 8 E4M3 codes.  MODE (the
+// same for a whole row or matrix): 0 the exact slow path (zero, infinite or
+// NaN scale: IEEE division or signed zeros), 1 the fast path, 2 the fast path
+// with the 2^100 scaling of tiny rows.
+template <int MODE>
 __device__ __forceinline__ uint2 encode8_e4m3(const uint4 &v, const RowScale &t)
 {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t out[2];
-    if (t.fast) {
+    if (MODE > 0) {
+        constexpr bool SC = MODE == 2;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            int d = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h]), t), quot(bf16_hi(w[2 * h]), t), 0, false);
-            d = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h + 1]), t), quot(bf16_hi(w[2 * h + 1]), t), d, true);
+            int d = __builtin_amdgcn_cvt_pk_fp8_f32(quot<SC>(bf16_lo(w[2 * h]), t), quot<SC>(bf16_hi(w[2 * h]), t),
+                                                    0, false);
+            d = __builtin_amdgcn_cvt_pk_fp8_f32(quot<SC>(bf16_lo(w[2 * h + 1]), t),
+                                                quot<SC>(bf16_hi(w[2 * h + 1]), t), d, true);
             out[h] = (uint32_t)d;
         }
     } else {
@@ -106,6 +119,18 @@ __device__ __forceinline__ uint2 encode8_e4m3(const uint4 &v, const RowScale &t)
         }
     }
     return make_uint2(out[0], out[1]);
+}
+
+// Calls f(std::integral_constant<int, MODE>) with the encode mode of scale t.
+template <typename F>
+__device__ __forceinline__ void with_encode_mode(const RowScale &t, F &&f)
+{
+    if (!t.fast)
+        f(std::integral_constant<int, 0>{});
+    else if (t.k == 1.0f)
+        f(std::integral_constant<int, 1>{});
+    else
+        f(std::integral_constant<int, 2>{});
 }
 
 // Block-wide max of a per-thread value (256 threads = 4 waves).
@@ -171,16 +196,19 @@ __global__ __launch_bounds__(kThreads) void quant_rowwise_kernel(
     const RowScale t = row_scale(__uint_as_float(m << 16));
     if (lane == 0) scale[row] = t.s;
     uint8_t *qr = q + row * ldq;
-    if (CACHE > 0) {
+    with_encode_mode(t, [&](auto mode_c) {
+        constexpr int MODE = decltype(mode_c)::value;
+        if (CACHE > 0) {
 #pragma unroll
-        for (int c = 0; c < CACHE; ++c) {
-            int64_t v = lane + (int64_t)c * TPR;
-            if (v < nvec) *reinterpret_cast<uint2 *>(qr + v * 8) = encode8_e4m3(cache[c], t);
+            for (int c = 0; c < CACHE; ++c) {
+                int64_t v = lane + (int64_t)c * TPR;
+                if (v < nvec) *reinterpret_cast<uint2 *>(qr + v * 8) = encode8_e4m3<MODE>(cache[c], t);
+            }
+        } else {
+            for (int64_t v = lane; v < nvec; v += TPR)
+                *reinterpret_cast<uint2 *>(qr + v * 8) = encode8_e4m3<MODE>(ld16(xr + v * 8), t);
         }
-    } else {
-        for (int64_t v = lane; v < nvec; v += TPR)
-            *reinterpret_cast<uint2 *>(qr + v * 8) = encode8_e4m3(ld16(xr + v * 8), t);
-    }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -223,8 +251,11 @@ __global__ __launch_bounds__(kThreads) void quant_tensor_encode_kernel(
     const uint16_t *xb = x + b * bstride;
     uint8_t *qb = q + b * elems;
     const int64_t nvec = elems / 8;
-    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads)
-        *reinterpret_cast<uint2 *>(qb + v * 8) = encode8_e4m3(ld16(xb + v * 8), t);
+    with_encode_mode(t, [&](auto mode_c) {
+        constexpr int MODE = decltype(mode_c)::value;
+        for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += (int64_t)gridDim.x * kThreads)
+            *reinterpret_cast<uint2 *>(qb + v * 8) = encode8_e4m3<MODE>(ld16(xb + v * 8), t);
+    });
 }
 
 // ---------------------------------------------------------------------------
