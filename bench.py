@@ -105,13 +105,16 @@ def _find(d, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
-def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command=""):
-    """Write profiles/<kernel>_<workload>.md (rocprofv3 kernel statistics and
-    HBM traffic per launch) and the traffic record bench.py reports.
+def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counters_dir=None):
+    """Write profiles/<kernel>_<workload>.md (rocprofv3 kernel statistics, HBM
+    traffic per launch and, given a counters run, MFMA and LDS utilisation)
+    and the traffic record bench.py reports.
 
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM are scaled by what
     the same counters read for the plain copy dispatch of known size that
-    --copy-probe-mib runs in the same process."""
+    --copy-probe-mib runs in the same process.  MfmaUtil and LdsUtil are
+    rocprofv3's derived metrics (MFMA busy cycles over SIMD cycles, LDS busy
+    cycles over CU cycles, at the clock the kernel actually ran)."""
     wl = WORKLOADS[name]
     kname = "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel"
     stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
@@ -175,12 +178,37 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command=""):
     f_write = (max(v for v, _ in c_write) * 1024 / copy_bytes) if (c_write and copy_bytes) else 1.0
     rd = float(np.median(g_fetch)) * 1024 / f_read
     wr = float(np.median(g_write)) * 1024 / f_write
+    util = None
+    if counters_dir:
+        # duration-weighted over the dispatches of each call, median over the
+        # timed calls (command line 4 names its --steps / --warmup)
+        toks = command.strip().splitlines()[3].split() if len(command.strip().splitlines()) > 3 else []
+        st, wu = 20, 100
+        for i, a in enumerate(toks):
+            if a == "--steps":
+                st = int(toks[i + 1])
+            if a == "--warmup":
+                wu = int(toks[i + 1])
+        rows = sorted(_read_csv(_find(counters_dir, "counter_collection.csv")), key=lambda r: int(r["Dispatch_Id"]))
+        util = {}
+        for metric in ("MfmaUtil", "LdsUtil"):
+            disp = [(float(r["Counter_Value"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows
+                    if r["Counter_Name"] == metric and ("gemm_" in r["Kernel_Name"] or "splitk_reduce" in r["Kernel_Name"])]
+            k = max(1, len(disp) // (st + wu))
+            calls = [disp[i:i + k] for i in range(0, len(disp) - k + 1, k)][-st:]
+            per_call = [sum(v * d for v, d in c) / max(1, sum(d for _, d in c)) for c in calls]
+            util[metric] = float(np.median(per_call)) if per_call else None
+        util["dispatches_per_call"] = k
+
     rec = {
         "kernel": kname, "workload": name, "kernel_source_hash": kernel_source_hash(wl.fmt),
         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
         "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": gemm_bytes(wl),
         "fetch_scale": f_read, "write_scale": f_write, "rocprof_avg_call_us": timed_avg_us,
     }
+    if util:
+        rec["mfma_util_pct"] = util["MfmaUtil"]
+        rec["lds_util_pct"] = util["LdsUtil"]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     allrec = json.load(open(tpath)) if os.path.exists(tpath) else {}
@@ -203,6 +231,15 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command=""):
         fh.write(f"- read  {rd / 1e6:.1f} MB, write {wr / 1e6:.1f} MB, total {(rd + wr) / 1e6:.1f} MB\n")
         fh.write(f"- algorithmic (A and W codes once, residual once, output once): {gemm_bytes(wl) / 1e6:.1f} MB\n")
         fh.write(f"- kernel source hash {rec['kernel_source_hash']}\n\n")
+        if timed_avg_us:
+            fh.write(f"Achieved over the call: {wl.flops / (timed_avg_us * 1e-6) / 1e12:.0f} TFLOP/s; HBM "
+                     f"{(rd + wr) / (timed_avg_us * 1e-6) / 1e9:.0f} GB/s measured, "
+                     f"{gemm_bytes(wl) / (timed_avg_us * 1e-6) / 1e9:.0f} GB/s algorithmic (of 8000).\n\n")
+        if util:
+            fh.write(f"Utilisation (`rocprofv3 --pmc MfmaUtil LdsUtil`, duration-weighted over the call's "
+                     f"{util['dispatches_per_call']} dispatch(es), median over the timed calls): MFMA busy "
+                     f"{util['MfmaUtil']:.1f}% of SIMD cycles, LDS busy {util['LdsUtil']:.1f}% of CU cycles, "
+                     f"both at the clock the kernels ran at.\n\n")
         fh.write("Commands (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):\n\n")
         fh.write("```\n" + command.strip() + "\n```\n")
     print(f"wrote {md} and {tpath}")
@@ -283,13 +320,18 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one plain bf16->f16 copy of this many MiB (the reference "
                          "dispatch for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU work: turn rocprofv3 output of this workload into profiles/ summaries")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="no GPU work: turn rocprofv3 output of this workload (STATS_DIR FETCH_DIR WRITE_DIR "
+                         "[COUNTERS_DIR]) into profiles/ summaries")
     ap.add_argument("--command", default="", help="with --summarize: the command line that produced the runs")
     args = ap.parse_args()
 
     if args.summarize:
-        summarize_profiles(args.workload, *args.summarize, command=args.command)
+        if len(args.summarize) not in (3, 4):
+            ap.error("--summarize takes STATS_DIR FETCH_DIR WRITE_DIR [COUNTERS_DIR]")
+        d = args.summarize
+        summarize_profiles(args.workload, d[0], d[1], d[2], command=args.command,
+                           counters_dir=d[3] if len(d) == 4 else None)
         return
 
     if args.gpus != 1:
