@@ -65,6 +65,18 @@ def gemm_bytes(wl) -> int:
     return b * (ab + wb + out + res)
 
 
+def quantize_bytes(wl) -> int:
+    """Algorithmic bytes of the step's activation quantization: bf16 in, codes
+    and scales out (per-tensor and NVFP4 read the activations twice: a
+    partial-maximum pass, then the encode pass)."""
+    elems = wl.batch * wl.M * wl.K
+    if wl.fmt == "e4m3_row":
+        return 3 * elems + 4 * wl.batch * wl.M
+    if wl.fmt == "e4m3_tensor":
+        return 5 * elems + 4 * wl.batch
+    return 4 * elems + elems // 2 + elems // 16 + 4
+
+
 def operator_bytes(M, N, K, n_out, residual: bool, fmt: str) -> int:
     """Bytes of the quantize + GEMM operator as ninfer PR #160's operator
     table counts them: bf16 activations in, weight codes and scales, bf16
@@ -245,6 +257,48 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
     print(f"wrote {md} and {tpath}")
 
 
+def run_probes(torch, spg):
+    """The device's own ceilings, measured after the timed steps: MFMA-only
+    rates (E4M3 32x32x64 and f16 32x32x16 on register operands) with the
+    shader clock they ran at, and a read-only HBM stream over 1 GiB."""
+    units = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    out = {}
+    for kind, name, iters in ((0, "fp8", 40000), (1, "f16", 80000)):
+        spg.probe_mfma(kind, iters // 10, 2 * units)            # settle
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            _, clocks, flops = spg.probe_mfma(kind, iters, 2 * units)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = clocks.cpu().tolist()
+            sclk = (c[1] - c[0]) / max(1, c[3] - c[2]) * 0.1
+            if best is None or ms < best[0]:
+                best = (ms, flops, sclk)
+        out[f"mfma_{name}_tflops"] = round(best[1] / (best[0] * 1e-3) / 1e12, 1)
+        out[f"mfma_{name}_sclk_ghz"] = round(best[2], 3)
+    buf = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
+    spg.probe_read(buf, 8 * units)
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        spg.probe_read(buf, 8 * units)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    out["hbm_read_gbs"] = round(buf.numel() / (best * 1e-3) / 1e9, 1)
+    del buf
+    out["note"] = ("after the timed steps, same device: MFMA-only loops on random register operands "
+                   "(4 independent chains per wave, 2 workgroups of 4 waves per CU), best of 3; "
+                   "sclk from s_memtime against the 100 MHz s_memrealtime; 1 GiB read-only stream")
+    return out
+
+
 def to_dev(x16, torch):
     return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -317,6 +371,7 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating input/weight buffer sets")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the MFMA-only and HBM read probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run one plain bf16->f16 copy of this many MiB (the reference "
                          "dispatch for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -490,6 +545,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    line["quantize_gbs"] = round(quantize_bytes(wl) / (line["quantize_ms_avg"] * 1e-3) / 1e9, 1)
+    if not args.no_probes:
+        line["probes"] = run_probes(torch, spg)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(wl, A16, W16, R16, args.cpu_budget)
         line["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()}

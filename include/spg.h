@@ -229,6 +229,32 @@ typedef struct spg_plan {
 
 int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units, spg_plan *plan);
 
+/* ---- measurement probes (not steps of the method) ------------------------
+ * The machine's own ceilings, measured on the device at hand and quoted next
+ * to the GEMM figures (ninfer PR #160 compares its kernels with a measured
+ * MMA ceiling in the same way).
+ *
+ * spg_probe_mfma: `workgroups` workgroups of 256 threads each run `iters`
+ * rounds of four independent back-to-back MFMAs on register operands (fixed
+ * pseudo-random bits, no NaN or infinity): kind 0 = E4M3 32x32x64 (131072
+ * flops each), kind 1 = f16 32x32x16 (32768 flops).  Total flops =
+ * workgroups * 4 waves * iters * 4 * flops-per-MFMA.  sink: device, one
+ * float per thread (workgroups * 256), keeps the results live.  clocks:
+ * device, 4 x uint64: shader-clock counter before / after the loop of wave 0
+ * of workgroup 0, then the 100 MHz reference counter before / after, so
+ * (c[1] - c[0]) / (c[3] - c[2]) * 100 MHz is the shader clock it ran at.
+ * SPG_EINVAL for kind not 0/1, iters or workgroups < 1, null or misaligned
+ * pointers.
+ *
+ * spg_probe_read: a read-only stream over `bytes` (a multiple of 16, >= 16)
+ * at device pointer src (16-byte aligned) by `workgroups` workgroups of 256
+ * threads; thread t writes to sink[t] the XOR of the 32-bit words it read
+ * (words t*4 .. t*4+3 of every 16-byte vector v = t, t + 256 * workgroups,
+ * ...), so the XOR of all sink words is the XOR of the whole buffer.
+ */
+int spg_probe_mfma(int kind, int64_t iters, int32_t workgroups, float *sink, uint64_t *clocks, void *stream);
+int spg_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "quantize_rowwise", "quantize_tensor", "quantize_block16", "gemm_scaled",
-    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "lib", "LIB_PATH",
+    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read", "lib", "LIB_PATH",
     "FMT_E4M3_ROW", "FMT_E4M3_TENSOR", "FMT_NVFP4", "EPI_STORE", "EPI_ADD", "EPI_SWIGLU",
     "SpgError",
 ]
@@ -75,6 +75,8 @@ SIGNATURES = {
     "spg_route_cost": (ctypes.c_double, [ctypes.POINTER(RouteCandidate), _I64, _I64, _I64, _I32]),
     "spg_route_select": (ctypes.c_int, [ctypes.POINTER(RouteCandidate), _I32, _I64, _I64, _I64, _I32]),
     "spg_gemm_plan": (ctypes.c_int, [ctypes.POINTER(GemmDesc), ctypes.c_int, _I32, ctypes.POINTER(Plan)]),
+    "spg_probe_mfma": (ctypes.c_int, [ctypes.c_int, _I64, _I32, _P, _P, _P]),
+    "spg_probe_read": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
 }
 
 
@@ -260,3 +262,26 @@ def route_cost(bm, bn, per_unit, factor, M, N, batch, units) -> float:
 def route_select(cands, M, N, batch, units) -> int:
     arr = (RouteCandidate * len(cands))(*[RouteCandidate(*c) for c in cands])
     return lib.spg_route_select(arr, len(cands), M, N, batch, units)
+
+
+# ---- measurement probes (not steps of the method) ------------------------
+PROBE_MFMA_FLOPS = {0: 131072, 1: 32768}     # per MFMA: E4M3 32x32x64, f16 32x32x16
+
+
+def probe_mfma(kind: int, iters: int, workgroups: int, device="cuda"):
+    """Enqueue the MFMA-only probe on the current stream; returns (sink,
+    clocks) device tensors (see spg_probe_mfma) and the flops it performs."""
+    sink = torch.empty((workgroups * 256,), dtype=torch.float32, device=device)
+    clocks = torch.zeros((4,), dtype=torch.int64, device=device)
+    _check(lib.spg_probe_mfma(kind, iters, workgroups, _ptr(sink), _ptr(clocks), _stream(sink)), "spg_probe_mfma")
+    return sink, clocks, workgroups * 4 * iters * 4 * PROBE_MFMA_FLOPS[kind]
+
+
+def probe_read(buf: torch.Tensor, workgroups: int):
+    """Enqueue the HBM read probe over the bytes of contiguous `buf` on the
+    current stream; returns the sink (one XOR-folded word per thread)."""
+    _need(buf.is_contiguous(), "probe_read: buf must be contiguous")
+    sink = torch.empty((workgroups * 256,), dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.spg_probe_read(_ptr(buf), nbytes, workgroups, _ptr(sink), _stream(buf)), "spg_probe_read")
+    return sink

@@ -290,3 +290,18 @@ def test_route_cost_is_waves_times_work_per_sm(spg):
     assert spg.route_cost(256, 128, 1, 1.0, 1024, 14336, 1, 170) == 3 * 256 * 128
     # 16 x 112 = 1792 cp.async tiles over 340 slots -> 6 waves of 2 x 64 x 128
     assert spg.route_cost(64, 128, 2, 1.0, 1024, 14336, 1, 170) == 6 * 2 * 64 * 128
+
+
+def test_probe_validation_errors(spg):
+    # every case is rejected before anything is enqueued (no GPU needed)
+    P = ctypes.c_void_p
+    buf = P(0x10000)
+    assert spg.lib.spg_probe_mfma(2, 10, 1, buf, buf, None) == 1          # unknown kind
+    assert spg.lib.spg_probe_mfma(0, 0, 1, buf, buf, None) == 1           # no iterations
+    assert spg.lib.spg_probe_mfma(1, 10, 0, buf, buf, None) == 1          # no workgroups
+    assert spg.lib.spg_probe_mfma(0, 10, 1, None, buf, None) == 1         # null sink
+    assert spg.lib.spg_probe_mfma(0, 10, 1, buf, P(0x10004), None) == 1  # clocks not 8-byte aligned
+    assert spg.lib.spg_probe_read(None, 1024, 1, buf, None) == 1
+    assert spg.lib.spg_probe_read(buf, 1000, 1, buf, None) == 1          # not a multiple of 16
+    assert spg.lib.spg_probe_read(P(0x10008), 1024, 1, buf, None) == 1   # source not 16-byte aligned
+    assert spg.lib.spg_probe_read(buf, 1024, 0, buf, None) == 1
