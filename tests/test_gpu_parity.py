@@ -88,15 +88,16 @@ def test_quantize_rowwise_every_bf16_value_with_unit_and_pow2_scales(spg):
         assert np.array_equal(q.cpu().numpy(), qo)
 
 
-def test_quantize_rowwise_every_amax_exponent(spg):
+@pytest.mark.parametrize("K", [256, 2064], ids=["one_wave_per_row", "one_block_per_row"])
+def test_quantize_rowwise_every_amax_exponent(spg, K):
     # one row per amax: every bf16 exponent (subnormal amax included), both
     # sides of 2^-40 and the largest finite bf16; the rest of each row is
     # random bit patterns of magnitude <= amax with random signs, so values
-    # of every size down to subnormals meet a scale of every size
+    # of every size down to subnormals meet a scale of every size (K = 2064:
+    # rows for the four-wave kernel, with a partly filled last vector column)
     rng = np.random.default_rng(77)
     amax = [(e << 7) | int(rng.integers(0, 128)) for e in range(0, 255)]
     amax += [0x0001, 0x007F, 0x0080, 0x2B7F, 0x2B80, 0x2B81, 0x7F7F]
-    K = 256
     x = np.zeros((len(amax), K), np.uint16)
     for i, a in enumerate(amax):
         body = rng.integers(0, a + 1, size=K - 1).astype(np.uint16)
@@ -240,6 +241,26 @@ def test_gemm_fp8_small_shapes(spg, shape, epi, fmt):
     ref = oracle_fp8(A16, W16, epi, fmt, R16)
     assert gpu.shape == ref["out"].shape
     check_close(gpu, ref["y"], ref["S"], f"{shape} {epi} {fmt}")
+
+
+# extreme aspect ratios: many tiles along one dimension (more tiles than
+# compute units, so the persistent grid walks several per workgroup), and the
+# longest K the oracle's fp64 sums keep exact (2^16; split 8 ways along K)
+EXTREME = [((70000, 40, 256), "add"), ((3, 70000, 256), "store"), ((5, 80000, 64), "swiglu"),
+           ((40, 72, 65536), "store"), ((130, 264, 65536), "swiglu")]
+
+
+@pytest.mark.parametrize("shape,epi", EXTREME, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_gemm_fp8_extreme_shapes(spg, shape, epi):
+    M, N, K = shape
+    A16 = bf16_normal((M, K), 1.0, M + 3 * K)
+    W16 = bf16_normal((N, K), 0.02, N + 5 * K)
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, M + N + 1) if epi == "add" else None
+    gpu = run_fp8(spg, A16, W16, epi, "e4m3_row", R16)
+    ref = oracle_fp8(A16, W16, epi, "e4m3_row", R16)
+    assert gpu.shape == ref["out"].shape
+    check_close(gpu, ref["y"], ref["S"], f"{shape} {epi}")
 
 
 def test_gemm_zero_weight_add_returns_residual_bitwise(spg):
