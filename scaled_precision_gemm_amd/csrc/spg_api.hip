@@ -65,12 +65,14 @@ int validate_desc(const spg_gemm_desc *d, int epi)
     return SPG_OK;
 }
 
-// The split-K factor: only when the output tiles fill less than half of
-// the compute units, pick the split s <= 8 (K / s >= 1024) that minimises
-// waves(tiles * s) / s, i.e. the wave-quantised time of the K-split work.
-int choose_split(int64_t tiles, int64_t K, int units, int bk)
+// The split-K factor: when the output tiles fill less than half of the
+// compute units - or for up to 64 tokens, where the partial tiles hold only
+// those rows and the product streams its weights (more compute units stream
+// more of them at once) - pick the split s <= 8 (K / s >= 1024) that
+// minimises waves(tiles * s) / s, the wave-quantised time of the split work.
+int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk)
 {
-    if (tiles * 2 > units) return 1;
+    if (tiles * 2 > units && M > 64) return 1;
     int best = 1;
     double best_cost = 1.0;
     for (int s = 2; s <= 8; ++s) {
@@ -98,7 +100,7 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     const int64_t tiles_m = cdiv(d->M, kTile);
     const int64_t tiles_n = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
     p->tiles = tiles_m * tiles_n * d->batch;
-    p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->K, units, p->bk) : 1;
+    p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->M, d->K, units, p->bk) : 1;
     p->kernel = d->format == SPG_FMT_NVFP4 ? 1 : 0;
     p->tail_split = 1;
     p->tail_tiles = 0;

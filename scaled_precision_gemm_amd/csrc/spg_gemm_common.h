@@ -247,12 +247,16 @@ __device__ __forceinline__ void stage_scales(const GemmArgs &g, const Tile &T, f
 // took ~45 us and the whole call 0.143 ms, against 0.095 ms now.)  Partial
 // (t, s) of a launch starts at float (t * S + s) * 65536, t counted from
 // tile_begin.
+// Only token rows below M are stored (the reduction reads no others): with a
+// few tokens per tile (decode widths) that is a small part of the tile.
 __device__ __forceinline__ void splitk_store(const GemmArgs &g, const Tile &T, int split, const Acc &acc)
 {
     float *base = g.partials + ((T.global - g.tile_begin) * g.split_k + split) * (int64_t)(kBM * kBN) + threadIdx.x * 4;
+    const int64_t row_l = T.m0 + (int64_t)(threadIdx.x >> 7) * 128 + (threadIdx.x & 31);   // block y = 0
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk) {
         const v16f &a = acc[blk >> 2][blk & 3];
+        if (row_l + (blk & 3) * 32 >= g.M) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             *reinterpret_cast<v4f *>(base + (blk * 4 + q) * (kThreads * 4)) =

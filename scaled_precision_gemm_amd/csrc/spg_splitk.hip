@@ -46,12 +46,19 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const GemmArgs 
         }
         return t;
     };
-    const v16f acc = sum_block(x * 4 + y);
-    const v16f acc_up = EPI == SPG_EPI_SWIGLU ? sum_block((x + 2) * 4 + y) : acc;
+    // only token rows below M were stored (the others are not read, and the
+    // epilogue skips them)
+    const bool live = T.m0 + (int64_t)(threadIdx.x >> 7) * 128 + y * 32 + (threadIdx.x & 31) < g.M;
+    v16f acc = {}, acc_up = {};
+    if (live) {
+        acc = sum_block(x * 4 + y);
+        if (EPI == SPG_EPI_SWIGLU) acc_up = sum_block((x + 2) * 4 + y);
+    }
     __syncthreads();   // scales staged
 
     const int wn = (threadIdx.x >> 6) & 1;
-    epilogue_block<EPI>(g, T, epi_out<EPI>(g, T), wtile_row0<EPI>(wn, x), y, acc, acc_up, lds_sa, lds_sw);
+    epilogue_block<EPI>(g, T, epi_out<EPI>(g, T), wtile_row0<EPI>(wn, x), y, acc, EPI == SPG_EPI_SWIGLU ? acc_up : acc,
+                        lds_sa, lds_sw);
 }
 
 template <int EPI>

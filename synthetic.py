@@ -88,4 +88,7 @@ WORKLOADS = {
                                      batch=64, w_std=1.0, seed=500),
     "fp8_tensor_square_8192": Workload("fp8_tensor_square_8192", "e4m3_tensor", "store", 8192, 8192, 8192,
                                        w_std=1.0, seed=510),
+    # the same two FP8 linears at 16 tokens (the narrow, weight-streaming route)
+    "fp8_row_add_t16": Workload("fp8_row_add_t16", "e4m3_row", "add", 16, 5120, 17408, seed=600),
+    "fp8_row_swiglu_t16": Workload("fp8_row_swiglu_t16", "e4m3_row", "swiglu", 16, 34816, 5120, seed=610),
 }

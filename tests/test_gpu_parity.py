@@ -556,3 +556,46 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
         D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
         y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, Rs)
         check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"half tail {M}x{N}x{K} {epi} {fmt} batch {b}")
+
+
+# ---------------------------------------------------------------------------
+# few tokens (M <= 32, decode widths): one partly filled tile row, K split
+# over many slices.  Ragged N (SwiGLU halves that are not a multiple of 4
+# columns), K not a multiple of 64, one to 32 tokens, per-tensor batches with
+# a broadcast weight, and the two prefill linears at 16 tokens.
+# ---------------------------------------------------------------------------
+
+NARROW = [((1, 64, 256), "store", "e4m3_row"), ((5, 200, 1040), "add", "e4m3_row"),
+          ((16, 2060, 528), "swiglu", "e4m3_row"), ((31, 130, 4112), "store", "e4m3_tensor"),
+          ((32, 520, 2048), "add", "e4m3_tensor"), ((7, 34, 48), "swiglu", "e4m3_tensor"),
+          ((16, 5120, 17408), "add", "e4m3_row"), ((16, 34816, 5120), "swiglu", "e4m3_row")]
+
+
+@pytest.mark.parametrize("shape,epi,fmt", NARROW, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_gemm_narrow(spg, shape, epi, fmt):
+    M, N, K = shape
+    A16 = bf16_normal((M, K), 1.0, 4 * M + K)
+    W16 = bf16_normal((N, K), 0.02, 6 * N + K)
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, M + N + 2) if epi == "add" else None
+    gpu = run_fp8(spg, A16, W16, epi, fmt, R16)
+    ref = oracle_fp8(A16, W16, epi, fmt, R16)
+    assert gpu.shape == ref["out"].shape
+    check_close(gpu, ref["y"], ref["S"], f"narrow {shape} {epi} {fmt}")
+
+
+def test_gemm_narrow_batched_broadcast_and_deterministic(spg):
+    B, M, N, K = 3, 9, 300, 1536
+    A16 = bf16_normal((B, M, K), 1.0, 91)
+    W16 = bf16_normal((N, K), 0.02, 92)
+    qa, sa = spg.quantize_tensor(dev(A16))
+    qw, sw = spg.quantize_tensor(dev(W16))
+    out1 = host_u16(spg.gemm_scaled(qa, sa, qw, sw, "store", fmt="e4m3_tensor"))
+    out2 = host_u16(spg.gemm_scaled(qa, sa, qw, sw, "store", fmt="e4m3_tensor"))
+    assert np.array_equal(out1, out2)
+    qwo, swo = oracle.quantize_tensor(W16)
+    for b in range(B):
+        qao, sao = oracle.quantize_tensor(A16[b])
+        D, Da = oracle.gemm_e4m3_sums(qao, qwo)
+        y, S, _ = oracle.epilogue("store", D, Da, sao[0], swo[0])
+        check_close(out1[b], y, S, f"narrow batch {b}")
