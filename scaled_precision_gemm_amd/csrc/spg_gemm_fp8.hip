@@ -61,7 +61,13 @@ struct CopySrc {
     v4i a, w;
 };
 
-template <int EPI, int SMODE, bool SPLIT>
+// AM: A blocks per wave that take part in the MFMAs.  4 in general; 1 for
+// products of at most 32 tokens, where only the first 32 rows of a tile
+// exist: the MFMAs (and fragment reads) of the empty blocks are left out, so
+// the stage is paced by the weight copies instead of 32 MFMAs on zeros (the
+// waves of the lower half compute the zero block 0 of their rows, which keeps
+// all four waves equally busy).
+template <int EPI, int SMODE, bool SPLIT, int AM = 4>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 {
     __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlot + kEpiRegionBytes];
@@ -274,8 +280,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         for (int j = 0; j < 32; ++j) {
             const int mi = (j & 15) >> 2, ni = j & 3;
             const Frags &F = j < 16 ? F0 : F1;
-            acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(F.b[ni]), op(F.a[mi]), acc[ni][mi],
-                                                                          0, 0, 0, 0, 0, 0);
+            if (mi < AM)
+                acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(F.b[ni]), op(F.a[mi]), acc[ni][mi],
+                                                                              0, 0, 0, 0, 0, 0);
             if (j <= 5) read_frags(slot, 1, F1, j * 3, j == 5 ? 16 : j * 3 + 3);
             if (j == 7) {
                 wait_lds();
@@ -554,7 +561,16 @@ hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
     // stages.
     const dim3 grid((unsigned)p.workgroups);
     const bool split = g.split_k > 1;
-    if (g.format == SPG_FMT_E4M3_ROW) {
+    if (g.M <= 32) {
+        // at most 32 tokens: one active A block per wave
+        if (g.format == SPG_FMT_E4M3_ROW) {
+            if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true, 1><<<grid, kThreads, 0, s>>>(g);
+            else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false, 1><<<grid, kThreads, 0, s>>>(g);
+        } else {
+            if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, true, 1><<<grid, kThreads, 0, s>>>(g);
+            else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 1><<<grid, kThreads, 0, s>>>(g);
+        }
+    } else if (g.format == SPG_FMT_E4M3_ROW) {
         if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true><<<grid, kThreads, 0, s>>>(g);
         else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false><<<grid, kThreads, 0, s>>>(g);
     } else {
