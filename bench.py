@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -42,11 +43,25 @@ GEMM_SOURCES = {
 }
 
 
-def kernel_source_hash(fmt: str) -> str:
+def code_only(text: str) -> str:
+    """Source text without comments and blank space differences: what the
+    compiler sees (a comment edit does not change the kernel)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(fmt: str, read=None) -> str:
+    """Hash of the GEMM kernel sources of a format, comments ignored.  `read`
+    maps a csrc file name to its text (default: the working tree)."""
     h = hashlib.sha256()
     for f in GEMM_SOURCES[fmt]:
-        with open(os.path.join(ROOT, "scaled_precision_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(ROOT, "scaled_precision_gemm_amd", "csrc", f)) as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -28,9 +28,14 @@
 //    19 ("stage kt+1 published": its first fragments are read while the last
 //    12 MFMAs run).  A copy has between 21 and 43 MFMAs to land.
 //  * SWIGLU pairs weight rows inside one 256-row W tile (128 gate + 128 up).
-//  * XCD-aware tile order; optional split-K through the workspace;
-//    epilogue straight from registers with 8-byte stores (W fragments are the
+//  * XCD-aware tile order; a persistent grid (one workgroup per compute
+//    unit) whose copy pipeline runs on into the next tile; optional split-K
+//    through the workspace; a half-height kernel for a short last round.
+//  * Epilogue from the accumulators, transposed through a per-wave LDS region
+//    so the output leaves in whole 128-byte row segments (W fragments are the
 //    first MFMA operand, so a lane holds four adjacent output columns).
+//  * Products of at most 32 tokens use an instantiation that leaves out the
+//    MFMAs of the empty A blocks.
 #include "spg_gemm_common.h"
 
 #include <type_traits>
