@@ -599,3 +599,39 @@ def test_gemm_narrow_batched_broadcast_and_deterministic(spg):
         D, Da = oracle.gemm_e4m3_sums(qao, qwo)
         y, S, _ = oracle.epilogue("store", D, Da, sao[0], swo[0])
         check_close(out1[b], y, S, f"narrow batch {b}")
+
+
+# ---------------------------------------------------------------------------
+# padded leading dimensions: codes with row strides above K, output and
+# residual with row strides above N (odd element strides for the bf16 ones);
+# the padding of the output must stay untouched.  General tiles, split-K and
+# the few-token instantiation.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,epi", [(300, 260, 320, "add"), (1000, 1030, 4096, "add"), (16, 520, 2080, "swiglu"),
+                                       (130, 264, 512, "store")])
+def test_gemm_padded_leading_dimensions(spg, M, N, K, epi):
+    A16 = bf16_normal((M, K), 1.0, M + 11)
+    W16 = bf16_normal((N, K), 0.02, N + 13)
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, M + 17) if epi == "add" else None
+    qa_buf = torch.zeros((M, K + 32), dtype=torch.uint8, device="cuda")
+    qw_buf = torch.zeros((N, K + 48), dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M, dtype=torch.float32, device="cuda")
+    sw = torch.empty(N, dtype=torch.float32, device="cuda")
+    spg.quantize_rowwise(dev(A16), out=qa_buf[:, :K], scale=sa)
+    spg.quantize_rowwise(dev(W16), out=qw_buf[:, :K], scale=sw)
+    out_buf = torch.full((M, n_out + 7), -7.0, dtype=torch.bfloat16, device="cuda")   # ldo odd
+    res = None
+    if R16 is not None:
+        r_buf = torch.zeros((M, n_out + 5), dtype=torch.bfloat16, device="cuda")      # ldr odd
+        r_buf[:, :n_out] = dev(R16)
+        res = r_buf[:, :n_out]
+    ws = spg.gemm_workspace(qa_buf[:, :K], qw_buf[:, :K], "e4m3_row", epi, out=out_buf[:, :n_out], residual=res)
+    spg.gemm_scaled(qa_buf[:, :K], sa, qw_buf[:, :K], sw, epi, residual=res, out=out_buf[:, :n_out], workspace=ws)
+    torch.cuda.synchronize()
+    got = host_u16(out_buf)
+    ref = oracle.linear_e4m3_rowwise(A16, W16, epi, R16)
+    check_close(np.ascontiguousarray(got[:, :n_out]), ref["y"], ref["S"], f"padded {M}x{N}x{K} {epi}")
+    pad = np.float32(-7.0).view(np.uint32) >> 16
+    assert np.all(got[:, n_out:] == pad), "output padding written"
