@@ -20,7 +20,11 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const GemmArgs 
     __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
     __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
     const Tile T = tile_from_id<EPI>(g, g.tile_begin + blockIdx.x);
-    stage_scales<EPI, SMODE>(g, T, lds_sa, lds_sw);
+    // the tile's scale factors: loads issued now, written to LDS once the
+    // partial sums are in (a wait for them before the partial loads are
+    // issued would serialize the two)
+    float va, vw;
+    scale_values<EPI, SMODE>(g, T, va, vw);
 
     // Thread i handles the 16 accumulators thread i of the GEMM workgroup
     // held for block (x, y), so the GEMM's epilogue code applies unchanged.
@@ -29,31 +33,50 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const GemmArgs 
     // the layout splitk_store writes: element 4q + r of block b of thread i
     // at (4b + q) * 1024 + 4i + r within a (tile, slice) partial
     const float *tile_base = g.partials + (int64_t)blockIdx.x * g.split_k * (kBM * kBN) + threadIdx.x * 4;
-    auto sum_block = [&](int blk) -> v16f {
-        v16f t;
-        for (int s = 0; s < g.split_k; ++s) {
-            const float *src = tile_base + (int64_t)s * (kBM * kBN) + blk * 4 * (kThreads * 4);
-            v16f p;
+    // The slices of a block (and of its up partner for SWIGLU) are loaded
+    // four at a time, every load issued before any is summed, then added in
+    // slice order (deterministic; the same order as one slice at a time).
+    auto load_part = [&](int s, int blk, v4f (&p)[4]) {
+        const float *src = tile_base + (int64_t)s * (kBM * kBN) + blk * 4 * (kThreads * 4);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(src + q * (kThreads * 4)));
-                p[4 * q] = v[0];
-                p[4 * q + 1] = v[1];
-                p[4 * q + 2] = v[2];
-                p[4 * q + 3] = v[3];
-            }
-            t = s == 0 ? p : t + p;
-        }
-        return t;
+        for (int q = 0; q < 4; ++q)
+            p[q] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(src + q * (kThreads * 4)));
     };
+    auto add_part = [&](int s, const v4f (&p)[4], v16f &t) {
+        v16f v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[4 * q] = p[q][0];
+            v[4 * q + 1] = p[q][1];
+            v[4 * q + 2] = p[q][2];
+            v[4 * q + 3] = p[q][3];
+        }
+        t = s == 0 ? v : t + v;
+    };
+    constexpr bool SW = EPI == SPG_EPI_SWIGLU;
     // only token rows below M were stored (the others are not read, and the
     // epilogue skips them)
     const bool live = T.m0 + (int64_t)(threadIdx.x >> 7) * 128 + y * 32 + (threadIdx.x & 31) < g.M;
     v16f acc = {}, acc_up = {};
     if (live) {
-        acc = sum_block(x * 4 + y);
-        if (EPI == SPG_EPI_SWIGLU) acc_up = sum_block((x + 2) * 4 + y);
+        for (int s0 = 0; s0 < g.split_k; s0 += 4) {
+            v4f p[4][4], pu[4][4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                if (s0 + d < g.split_k) {
+                    load_part(s0 + d, x * 4 + y, p[d]);
+                    if (SW) load_part(s0 + d, (x + 2) * 4 + y, pu[d]);
+                }
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                if (s0 + d < g.split_k) {
+                    add_part(s0 + d, p[d], acc);
+                    if (SW) add_part(s0 + d, pu[d], acc_up);
+                }
+        }
     }
+    lds_sa[threadIdx.x] = va;
+    lds_sw[threadIdx.x] = vw;
     __syncthreads();   // scales staged
 
     const int wn = (threadIdx.x >> 6) & 1;
