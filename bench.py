@@ -36,10 +36,11 @@ DEFAULT_WORKLOAD = "fp8_row_swiglu_t4096"
 PEAK_TFLOPS = {"fp8": 5000.0, "f16": 2500.0}
 HBM_GBS = 8000.0
 
+# the kernels of one gemm_scaled call: the GEMM, its split-K reduction
 GEMM_SOURCES = {
-    "e4m3_row": ["spg_gemm_fp8.hip", "spg_gemm_common.h"],
-    "e4m3_tensor": ["spg_gemm_fp8.hip", "spg_gemm_common.h"],
-    "nvfp4": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h"],
+    "e4m3_row": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip"],
+    "e4m3_tensor": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip"],
+    "nvfp4": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h", "spg_splitk.hip"],
 }
 
 
