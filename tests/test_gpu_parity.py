@@ -635,3 +635,53 @@ def test_gemm_padded_leading_dimensions(spg, M, N, K, epi):
     check_close(np.ascontiguousarray(got[:, :n_out]), ref["y"], ref["S"], f"padded {M}x{N}x{K} {epi}")
     pad = np.float32(-7.0).view(np.uint32) >> 16
     assert np.all(got[:, n_out:] == pad), "output padding written"
+
+
+# ---------------------------------------------------------------------------
+# the tail-exercising widths the pages test their ops at (ninfer PR #167:
+# 1345, 1153, 4001 and 321 - widths that are not whole tiles), with canary
+# guard bands around every output: quantized codes, scales and the GEMM
+# output are written into the interior of larger buffers whose borders must
+# keep their sentinel bytes.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,epi", [(321, 1345, 512, "store"), (1153, 321, 1040, "add"), (1345, 2 * 1153, 256, "swiglu"),
+                                       (4001, 321, 128, "add"), (33, 4001, 2064, "store")])
+def test_gemm_page_tail_widths_with_guard_bands(spg, M, N, K, epi):
+    A16 = bf16_normal((M, K), 1.0, M * 3 + 1)
+    W16 = bf16_normal((N, K), 0.02, N * 5 + 2)
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, M + N + 3) if epi == "add" else None
+    G = 16                                                         # guard rows / columns
+    qa_buf = torch.full((M + 2, K + G), 0xA5, dtype=torch.uint8, device="cuda")
+    qw_buf = torch.full((N + 2, K + G), 0x5A, dtype=torch.uint8, device="cuda")
+    sa_buf = torch.full((M + G,), -3.0, dtype=torch.float32, device="cuda")
+    sw_buf = torch.full((N + G,), -5.0, dtype=torch.float32, device="cuda")
+    qa, sa = qa_buf[1:M + 1, :K], sa_buf[4:M + 4]
+    qw, sw = qw_buf[1:N + 1, :K], sw_buf[4:N + 4]
+    spg.quantize_rowwise(dev(A16), out=qa, scale=sa)
+    spg.quantize_rowwise(dev(W16), out=qw, scale=sw)
+    out_buf = torch.full((M + 2, n_out + G), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = out_buf[1:M + 1, 8:8 + n_out]
+    res = dev(R16) if R16 is not None else None
+    spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res, out=out)
+    torch.cuda.synchronize()
+
+    qa_h, qw_h = qa_buf.cpu().numpy(), qw_buf.cpu().numpy()
+    qao, sao = oracle.quantize_rowwise(A16)
+    qwo, swo = oracle.quantize_rowwise(W16)
+    assert np.array_equal(qa_h[1:M + 1, :K], qao) and np.array_equal(qw_h[1:N + 1, :K], qwo)
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sao.view(np.uint32))
+    assert np.array_equal(sw.cpu().numpy().view(np.uint32), swo.view(np.uint32))
+    qa_h[1:M + 1, :K] = 0xA5
+    qw_h[1:N + 1, :K] = 0x5A
+    assert np.all(qa_h == 0xA5) and np.all(qw_h == 0x5A), "code guard bands written"
+    sa_h, sw_h = sa_buf.cpu().numpy(), sw_buf.cpu().numpy()
+    assert np.all(np.delete(sa_h, np.s_[4:M + 4]) == -3.0) and np.all(np.delete(sw_h, np.s_[4:N + 4]) == -5.0)
+
+    got = host_u16(out_buf)
+    ref = oracle.linear_e4m3_rowwise(A16, W16, epi, R16)
+    check_close(np.ascontiguousarray(got[1:M + 1, 8:8 + n_out]), ref["y"], ref["S"], f"widths {M}x{N}x{K} {epi}")
+    sentinel = np.float32(-7.0).view(np.uint32) >> 16
+    got[1:M + 1, 8:8 + n_out] = sentinel
+    assert np.all(got == sentinel), "output guard band written"
