@@ -685,3 +685,66 @@ def test_gemm_page_tail_widths_with_guard_bands(spg, M, N, K, epi):
     sentinel = np.float32(-7.0).view(np.uint32) >> 16
     got[1:M + 1, 8:8 + n_out] = sentinel
     assert np.all(got == sentinel), "output guard band written"
+
+
+def _interior(buf: torch.Tensor, off: int, n: int) -> torch.Tensor:
+    return buf[off:off + n]
+
+
+@pytest.mark.parametrize("M,N,K", [(321, 1345, 1024), (33, 300, 1056)])
+def test_nvfp4_and_tensor_quantizers_and_gemm_with_guard_bands(spg, M, N, K):
+    # quantize_block16 / quantize_tensor through the C ABI into the middle of
+    # larger buffers, then the NVFP4 GEMM into the middle of a larger output;
+    # every byte outside the written ranges must keep its sentinel
+    G = 64
+    A16 = bf16_normal((M, K), 1.0, M + 71)
+    W16 = bf16_normal((N, K), 0.02, N + 72)
+    outs = {}
+    for name, x16 in (("a", A16), ("w", W16)):
+        R = x16.shape[0]
+        x = dev(x16)
+        qbuf = torch.full((R * K // 2 + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda")
+        sbuf = torch.full((R * K // 16 + 2 * G,), 0x5A, dtype=torch.uint8, device="cuda")
+        tbuf = torch.full((2 * G // 4 + 1,), -9.0, dtype=torch.float32, device="cuda")
+        nws = spg.lib.quantize_block16_workspace_bytes(R, K)
+        ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device="cuda")
+        q, bs, t = _interior(qbuf, G, R * K // 2), _interior(sbuf, G + 3, R * K // 16), _interior(tbuf, G // 4, 1)
+        st = spg.lib.quantize_block16(spg._ptr(x), R, K, spg._ptr(q), spg._ptr(bs), spg._ptr(t), spg._ptr(ws),
+                                      ws.numel(), spg._stream(x))
+        assert st == 0
+        torch.cuda.synchronize()
+        qo, bso, to = oracle.quantize_block16(x16)
+        assert np.array_equal(q.cpu().numpy(), qo.reshape(-1)) and np.array_equal(bs.cpu().numpy(), bso.reshape(-1))
+        assert t.cpu().numpy().view(np.uint32)[0] == np.float32(to).view(np.uint32)
+        qh, sh, th = qbuf.cpu().numpy(), sbuf.cpu().numpy(), tbuf.cpu().numpy()
+        assert np.all(qh[:G] == 0xA5) and np.all(qh[G + R * K // 2:] == 0xA5)
+        assert np.all(sh[:G + 3] == 0x5A) and np.all(sh[G + 3 + R * K // 16:] == 0x5A)
+        assert np.all(np.delete(th, G // 4) == -9.0)
+        outs[name] = (q.view(R, K // 2), bs.view(R, K // 16), t)
+        # per-tensor FP8 of the same matrix, as a batch of one, into a guarded buffer
+        qt_buf = torch.full((R * K + 2 * G,), 0x3C, dtype=torch.uint8, device="cuda")
+        st_buf = torch.full((8,), -9.0, dtype=torch.float32, device="cuda")
+        nws = spg.lib.quantize_tensor_workspace_bytes(1, R, K)
+        ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device="cuda")
+        qt, stt = _interior(qt_buf, G, R * K), _interior(st_buf, 4, 1)
+        assert spg.lib.quantize_tensor(spg._ptr(x), 1, R, K, R * K, spg._ptr(qt), spg._ptr(stt), spg._ptr(ws),
+                                       ws.numel(), spg._stream(x)) == 0
+        torch.cuda.synchronize()
+        qto, sto = oracle.quantize_tensor(x16)
+        assert np.array_equal(qt.cpu().numpy(), qto.reshape(-1))
+        assert st_buf.cpu().numpy().view(np.uint32)[4] == sto.view(np.uint32)[0]
+        qth = qt_buf.cpu().numpy()
+        assert np.all(qth[:G] == 0x3C) and np.all(qth[G + R * K:] == 0x3C)
+        assert np.all(np.delete(st_buf.cpu().numpy(), 4) == -9.0)
+
+    (qa, bsa, ta), (qw, bsw, tw) = outs["a"], outs["w"]
+    out_buf = torch.full((M + 2, N + 16), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = out_buf[1:M + 1, 8:8 + N]
+    spg.gemm_scaled(qa, bsa, qw, bsw, "store", fmt="nvfp4", tscale_a=ta, tscale_w=tw, out=out)
+    torch.cuda.synchronize()
+    got = host_u16(out_buf)
+    ref = oracle_nvfp4(A16, W16, "store")
+    check_close(np.ascontiguousarray(got[1:M + 1, 8:8 + N]), ref["y"], ref["S"], f"nvfp4 guard {M}x{N}x{K}")
+    sentinel = np.float32(-7.0).view(np.uint32) >> 16
+    got[1:M + 1, 8:8 + N] = sentinel
+    assert np.all(got == sentinel), "NVFP4 output guard band written"
