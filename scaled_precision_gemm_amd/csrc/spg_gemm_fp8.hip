@@ -66,12 +66,12 @@ struct CopySrc {
     v4i a, w;
 };
 
-// AM: A blocks per wave that take part in the MFMAs.  4 in general; 1 for
-// products of at most 32 tokens, where only the first 32 rows of a tile
-// exist: the MFMAs (and fragment reads) of the empty blocks are left out, so
-// the stage is paced by the weight copies instead of 32 MFMAs on zeros (the
-// waves of the lower half compute the zero block 0 of their rows, which keeps
-// all four waves equally busy).
+// AM: A blocks per wave that take part in the MFMAs.  4 in general; 1 (2)
+// for products of at most 32 (64) tokens, where only the first 32 (64) rows
+// of a tile exist: the MFMAs (and fragment reads) of the empty blocks are
+// left out, so the stage is paced by the weight copies instead of 32 MFMAs on
+// zeros (the waves of the lower half compute the zero blocks of their rows,
+// which keeps all four waves equally busy).
 template <int EPI, int SMODE, bool SPLIT, int AM = 4>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 {
@@ -574,6 +574,15 @@ hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
         } else {
             if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, true, 1><<<grid, kThreads, 0, s>>>(g);
             else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 1><<<grid, kThreads, 0, s>>>(g);
+        }
+    } else if (g.M <= 64) {
+        // at most 64 tokens: two active A blocks per wave
+        if (g.format == SPG_FMT_E4M3_ROW) {
+            if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true, 2><<<grid, kThreads, 0, s>>>(g);
+            else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false, 2><<<grid, kThreads, 0, s>>>(g);
+        } else {
+            if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, true, 2><<<grid, kThreads, 0, s>>>(g);
+            else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 2><<<grid, kThreads, 0, s>>>(g);
         }
     } else if (g.format == SPG_FMT_E4M3_ROW) {
         if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true><<<grid, kThreads, 0, s>>>(g);

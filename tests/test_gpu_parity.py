@@ -559,8 +559,8 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
 
 
 # ---------------------------------------------------------------------------
-# few tokens (M <= 32, decode widths): one partly filled tile row, K split
-# over many slices.  Ragged N (SwiGLU halves that are not a multiple of 4
+# few tokens (M <= 64, decode widths): one partly filled tile row, K split
+# over many slices; the instantiations for at most 32 and at most 64 tokens.  Ragged N (SwiGLU halves that are not a multiple of 4
 # columns), K not a multiple of 64, one to 32 tokens, per-tensor batches with
 # a broadcast weight, and the two prefill linears at 16 tokens.
 # ---------------------------------------------------------------------------
@@ -568,7 +568,9 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
 NARROW = [((1, 64, 256), "store", "e4m3_row"), ((5, 200, 1040), "add", "e4m3_row"),
           ((16, 2060, 528), "swiglu", "e4m3_row"), ((31, 130, 4112), "store", "e4m3_tensor"),
           ((32, 520, 2048), "add", "e4m3_tensor"), ((7, 34, 48), "swiglu", "e4m3_tensor"),
-          ((16, 5120, 17408), "add", "e4m3_row"), ((16, 34816, 5120), "swiglu", "e4m3_row")]
+          ((16, 5120, 17408), "add", "e4m3_row"), ((16, 34816, 5120), "swiglu", "e4m3_row"),
+          ((33, 300, 1040), "store", "e4m3_row"), ((48, 2060, 528), "swiglu", "e4m3_tensor"),
+          ((64, 5120, 4096), "add", "e4m3_row")]
 
 
 @pytest.mark.parametrize("shape,epi,fmt", NARROW, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
