@@ -268,7 +268,8 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
                      f"{util['dispatches_per_call']} dispatch(es), median over the timed calls): MFMA busy "
                      f"{util['MfmaUtil']:.1f}% of SIMD cycles, LDS busy {util['LdsUtil']:.1f}% of CU cycles, "
                      f"both at the clock the kernels ran at.\n\n")
-        fh.write("Commands (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):\n\n")
+        fh.write("Commands (run from the repository root on the GPU box with `TMPDIR=/tmp` exported; each "
+                 "under `timeout`):\n\n")
         fh.write("```\n" + command.strip() + "\n```\n")
     print(f"wrote {md} and {tpath}")
 
