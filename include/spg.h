@@ -2,22 +2,22 @@
  * spg.h - C ABI of the scaled low-precision GEMM path for MI355X (gfx950).
  *
  * The path computes the linear layers of LLM prefill in two primitives, the
- * quantizer and the GEMM, the split AstrAI's commit log calls its
- * "two-primitive API" (quantize + mm_fp8):
+ * quantizer and the GEMM - the same split into a quantize primitive and an
+ * FP8 GEMM primitive that AstrAI's commit log describes for its API:
  *
  *   1. quantize bf16 activations per token row to FP8 E4M3 (ninfer PR #167,
  *      "The fp8 A8 GEMM stages its operands through TMA", opening summary and
  *      "Measured": row-scaled A8, FP8_E4M3FN weights with row scales), per
- *      matrix (AstrAI, "Benchmark: ... E4M3, NT pre-quantized"), or per 16
+ *      matrix (AstrAI's per-tensor E4M3 benchmark on pre-quantized NT operands), or per 16
  *      K-elements to NVFP4 (ninfer PR #160, "The NVFP4 TMA route reads
- *      activation scales as one tile": E2M1 codes, E4M3 scales over
- *      "[BlockM tokens, 16 groups]" tiles);
+ *      activation scales as one tile": E2M1 codes, E4M3 scales in tiles of
+ *      a block of tokens by 16 groups);
  *   2. multiply by pre-quantized weights with fp32 accumulation and apply the
  *      scales after accumulation, then one fused bf16 epilogue: plain store
  *      (linear), residual add (linear_add) or paired SwiGLU (linear_swiglu)
- *      (PR #167 opening summary and the maintainer review's note on "explicit
- *      paired SwiGLU handling").  The output is always bf16 (AstrAI: "GEMM
- *      output is always bf16").
+ *      (PR #167 opening summary, and the maintainer review asking for the
+ *      SwiGLU pairing to be handled explicitly).  The output is always bf16,
+ *      as AstrAI's commit log fixes it for its GEMM.
  *
  * Conventions for every entry point
  *  - All matrices are row-major.  A is [M, K] (tokens x reduction), W is
@@ -55,7 +55,7 @@ enum {
     SPG_EHIP = 4           /* a HIP call or kernel launch reported an error */
 };
 
-/* ---- operand formats (AstrAI: "validate the fmt enum") ----------------- */
+/* ---- operand formats (validated, as AstrAI validates its format enum) - */
 enum {
     SPG_FMT_E4M3_ROW = 0,    /* E4M3 codes; fp32 scale per row of A and of W  */
     SPG_FMT_E4M3_TENSOR = 1, /* E4M3 codes; one fp32 scale per matrix         */
@@ -138,7 +138,7 @@ int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t
  *              (else SPG_EUNSUPPORTED)
  *   stride_* : batch strides (bytes for A/W codes, elements for out and
  *              residual); 0 broadcasts one matrix to every batch entry
- *              (AstrAI: "size-1 batches broadcast (stride 0)")
+ *              (AstrAI broadcasts batches of one through a zero stride)
  *   format   : SPG_FMT_*
  *   tscale_a, tscale_w : NVFP4 only, device fp32 [1] tensor scales
  */

@@ -21,12 +21,14 @@
  *       - maintainer review item 3 and the reply: the contract is the Op
  *         against an independent mathematical oracle.
  *  [P2] AstrAI commit log for csrc/kernels/fp8/gemm.cuh
- *       - "Benchmark: ... E4M3, NT pre-quantized": per-tensor scaled NT GEMM;
- *       - the two-primitive API (quantize + mm_fp8) with fp32-domain amax
- *         references; 3D operands through batch strides.
+ *       - its E4M3 benchmark entry: per-tensor scaled NT GEMM on
+ *         pre-quantized operands;
+ *       - an API of two primitives (quantize, then the FP8 GEMM), with
+ *         amax references computed in fp32; 3D operands through batch
+ *         strides.
  *  [P3] ninfer PR #160, "The NVFP4 TMA route reads activation scales as one
  *       tile": NVFP4 = E2M1 codes, one E4M3 scale per 16-element K group
- *       ("[BlockM tokens, 16 groups]" scale tiles), linear_add and
+ *       (scale tiles of a block of tokens by 16 groups), linear_add and
  *       linear_swiglu at T=4096.
  * The pages print no formulas for the scales.  Where they are silent this
  * file takes the plainest reading:
@@ -191,7 +193,7 @@ EXPORT float spo_amax_bf16(const uint16_t *x, int64_t rows, int64_t K, int64_t l
     return amax;
 }
 
-/* Per-tensor quantization ([P2] "E4M3, NT pre-quantized"; one scale per
+/* Per-tensor quantization ([P2], the per-tensor E4M3 benchmark; one scale per
  * matrix, per batch element for a batched operand).  x: batch matrices
  * [rows, K], matrix b at x + b*bstride, row stride K; q likewise with stride
  * rows*K per matrix; scale: fp32 [batch]. */

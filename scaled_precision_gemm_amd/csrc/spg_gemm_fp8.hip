@@ -1,7 +1,7 @@
 // FP8 E4M3 scaled GEMM for gfx950 with fused bf16 epilogues.
 //
 // out = epilogue(s_a * s_w * sum_k a_k w_k), A [M,K] and W [N,K] K-contiguous
-// (the NT layout of AstrAI's "E4M3, NT pre-quantized" benchmark), fp32
+// (the NT layout of AstrAI's per-tensor E4M3 benchmark), fp32
 // accumulation with the scales applied after it, as ninfer PR #167 states for
 // its row-scaled A8 GEMM (opening summary: same accumulator, scale
 // application, epilogue and output policies for the linear, linear_add and
