@@ -391,9 +391,10 @@ constexpr int kEpiRegionBytes = 4 * 4096;   // per workgroup
 // bounds checks or narrow-store paths, hence no per-store branches.
 // MI: 32-row A blocks per wave (4; 2 in a half-height tile, whose waves
 // hold acc[x][0..1] and cover token rows wm * 64 .. wm * 64 + 63).
-template <int EPI, bool FULL, int MI = 4>
+// GIVEN: wave_in is the caller's wave index; otherwise it is derived here.
+template <int EPI, bool FULL, int MI = 4, bool GIVEN = false>
 __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
-                                              const float *lds_sw, uint8_t *region)
+                                              const float *lds_sw, uint8_t *region, int wave_in)
 {
     constexpr bool SW = EPI == SPG_EPI_SWIGLU;
     constexpr int NP = SW ? 1 : 2;            // 64-column passes per 32-row block
@@ -402,7 +403,7 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
     const int lane = lane_id();
     // the wave index is uniform: keeping it (and every row / column bound
     // derived from it) in scalar registers keeps the pass branches uniform
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wave = GIVEN ? wave_in : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
     const EpiOut o = epi_out<EPI>(g, T);
     const bool vec16 = FULL || (((((uintptr_t)o.out) & 15) == 0) && ((g.ldo & 7) == 0));
@@ -531,22 +532,23 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
     }
 }
 
-// Fused epilogue of the whole tile (no split).
-template <int EPI, int MI = 4>
+// Fused epilogue of the whole tile (no split).  GIVEN, wave_in: as for
+// epilogue_impl.
+template <int EPI, int MI = 4, bool GIVEN = false>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
-                                         const float *lds_sw, uint8_t *region)
+                                         const float *lds_sw, uint8_t *region, int wave_in = 0)
 {
     constexpr bool SW = EPI == SPG_EPI_SWIGLU;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wave = GIVEN ? wave_in : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave >> 1, wn = wave & 1;
     const EpiOut o = epi_out<EPI>(g, T);
     const bool full = T.m0 + wm * (MI * 32) + MI * 32 <= g.M && T.c0 + (SW ? wn * 64 + 64 : wn * 128 + 128) <= o.nvalid &&
                       (((uintptr_t)o.out) & 15) == 0 && (g.ldo & 7) == 0 &&
                       (EPI != SPG_EPI_ADD || ((((uintptr_t)o.res) & 15) == 0 && (g.ldr & 7) == 0));
     if (full)
-        epilogue_impl<EPI, true, MI>(g, T, acc, lds_sa, lds_sw, region);
+        epilogue_impl<EPI, true, MI, GIVEN>(g, T, acc, lds_sa, lds_sw, region, wave_in);
     else
-        epilogue_impl<EPI, false, MI>(g, T, acc, lds_sa, lds_sw, region);
+        epilogue_impl<EPI, false, MI, GIVEN>(g, T, acc, lds_sa, lds_sw, region, wave_in);
 }
 
 }  // namespace gemm
