@@ -71,6 +71,14 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, v4i rsrc
                  :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
+// 4 bytes per lane from rsrc + voff + soff into LDS at lds_base + 4 * lane
+// (same rules as dma16).
+__device__ __forceinline__ void dma4(uint32_t lds_base, uint32_t voff, v4i rsrc, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

@@ -76,7 +76,12 @@ template <int EPI, int SMODE, bool SPLIT, int AM = 4>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 {
     __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlot + kEpiRegionBytes];
-    __shared__ __attribute__((aligned(16))) float lds_scale[2][2][kBM];   // [tile parity][a / w][row]
+    // Row-wise SWIGLU copies the scale factors straight into LDS, into a ring
+    // of three buffers (see below); the other forms load them into registers
+    // a tile ahead and store them into two alternating buffers.
+    constexpr bool kScaleDma = !SPLIT && EPI == SPG_EPI_SWIGLU && SMODE == SPG_FMT_E4M3_ROW;
+    constexpr int kScaleBufs = kScaleDma ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) float lds_scale[kScaleBufs][2][kBM];   // [buffer][a / w][row]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -231,6 +236,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         }
     };
 
+    // Scale factors of tile T into lds_scale[buf] by direct copies (row-wise
+    // SWIGLU): tile row r = 64 wave + lane.  A: token row m0 + r (zero past
+    // M).  W: gate row n0 + r for r < 128, up row N/2 + n0 + r - 128 above
+    // (zero where n0 + (r mod 128) >= N/2); the same rows make_src copies.
+    // The lane offsets come from an opaque lane id, so nothing derived from
+    // threadIdx.x stays live (or spilled) across the tile loop.
+    auto issue_scales = [&](const Tile &T, int buf) {
+        const uint32_t ln = (uint32_t)lane_id();
+        const float *sa = (const float *)g.sa + (g.stride_a ? T.b * g.sa_bstride : 0) + T.m0;
+        const float *sw = (const float *)g.sw + (g.stride_w ? T.b * g.sw_bstride : 0);
+        const int64_t a_rows = max((int64_t)0, min((int64_t)kBM, g.M - T.m0));
+        const int64_t w_rows = max((int64_t)0, min((int64_t)128, Nh - T.n0));
+        const int64_t w_first = wave < 2 ? T.n0 : Nh + T.n0;
+        const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float *)&lds_scale[buf][0][wave * 64]);
+        const uint32_t lw = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float *)&lds_scale[buf][1][wave * 64]);
+        dma4(la, ((uint32_t)(wave * 64) + ln) * 4u, make_rsrc(sa, (uint32_t)(a_rows * 4)), 0);
+        dma4(lw, ((uint32_t)((wave & 1) * 64) + ln) * 4u, make_rsrc(sw + w_first, (uint32_t)(w_rows * 4)), 0);
+    };
+
     Tile Tc = tile_i(0), Tn = Tc;
     CopySrc sc = make_src(Tc), sn = sc;
     bool has_next = ntile > 1;
@@ -238,7 +264,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         Tn = tile_i(1);
         sn = make_src(Tn);
     }
-    stage_scales<EPI, SMODE>(g, Tc, lds_scale[0][0], lds_scale[0][1]);
+    if constexpr (kScaleDma) {
+        // tiles 0 and 1; both land before the first stage is published
+        issue_scales(Tc, 0);
+        if (has_next) issue_scales(Tn, 1);
+    } else {
+        stage_scales<EPI, SMODE>(g, Tc, lds_scale[0][0], lds_scale[0][1]);
+    }
 
     // One stage = 32 MFMAs (sub-step 0 from F0, sub-step 1 from F1) in a
     // fixed order, with the other work of the stage slotted between them so
@@ -312,12 +344,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
         // loading them next to this tile's output stores would make every
         // wave wait for its stores (and for the loads' own latency).
         float nsa = 0.0f, nsw = 0.0f;
-        if (i + 1 < ntile) scale_values<EPI, SMODE>(g, Tn, nsa, nsw);
+        if (!kScaleDma && i + 1 < ntile) scale_values<EPI, SMODE>(g, Tn, nsa, nsw);
         Acc acc;
         zero_acc(acc);
         for (int kt = 0; kt + 1 < nk; ++kt) stage(acc, kt, std::false_type{});
         if (nk > 0) stage(acc, nk - 1, std::true_type{});
 
+        if constexpr (kScaleDma) {
+            // The scales of tile i + 2 go into buffer (i + 2) mod 3 now, so
+            // their copies land while this epilogue runs.  That buffer last
+            // held tile i - 1's scales: every wave has passed a barrier of
+            // tile i (the one below when K is empty) since its epilogue of
+            // tile i - 1.  The copies are complete (by the stage waits, or the
+            // wait below) and published by a barrier before tile i + 2's
+            // epilogue reads them.
+            if (nk == 0) {
+                wait_vmem<0>();
+                block_barrier();
+            }
+            if (i + 2 < ntile) issue_scales(tile_i(i + 2), (i + 2) % 3);
+        }
         if (SPLIT) {
             splitk_store(g, Tc, split, acc);   // the slices are summed by splitk_reduce_kernel
         } else {
@@ -327,7 +373,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
             // vector memory counter also waits for the next tile's copies in
             // flight (measured: 1-2% of the 4096 x 34816 x 5120 product).  The
             // other epilogues measured slightly faster re-deriving it.
-            epilogue<EPI, 4, EPI == SPG_EPI_SWIGLU>(g, Tc, acc, lds_scale[i & 1][0], lds_scale[i & 1][1],
+            const int sb = kScaleDma ? i % 3 : i & 1;
+            epilogue<EPI, 4, EPI == SPG_EPI_SWIGLU>(g, Tc, acc, lds_scale[sb][0], lds_scale[sb][1],
                                                    &lds[2 * kSlot + wave * (kEpiRegionBytes / 4)], wave);
         }
         if (i + 1 < ntile) {
@@ -342,9 +389,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
             }
             // Every wave has passed this tile's barriers, so none still reads
             // the scales of tile i - 1 that share this buffer.
-            const int t = wave * 64 + lane_id();
-            lds_scale[(i + 1) & 1][0][t] = nsa;
-            lds_scale[(i + 1) & 1][1][t] = nsw;
+            if (!kScaleDma) {
+                const int t = wave * 64 + lane_id();
+                lds_scale[(i + 1) & 1][0][t] = nsa;
+                lds_scale[(i + 1) & 1][1][t] = nsw;
+            }
         }
     }
     wait_vmem<0>();   // no copy into LDS may still be in flight when the workgroup ends

@@ -6,6 +6,8 @@ exact fp64 result and S the scaled sum of |products|.  The oracle quantizes
 the bf16 inputs itself: no oracle input comes from the GPU.  Full-size
 workloads are checked on sampled rows x columns (tile edges included).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -269,6 +271,35 @@ def test_gemm_zero_weight_add_returns_residual_bitwise(spg):
     R16 = bf16_normal((300, 260), 1.0, 2)
     gpu = run_fp8(spg, A16, W16, "add", "e4m3_row", R16)
     assert np.array_equal(gpu, R16)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3_row", "e4m3_tensor"])
+@pytest.mark.parametrize("epi", ["store", "add", "swiglu"])
+def test_gemm_empty_k(spg, epi, fmt):
+    # K = 0 through the C ABI (the binding cannot pass the null data pointer
+    # of an empty torch tensor): every sum is empty, so the output is exactly
+    # zero (SWIGLU: silu(0) * 0) or the residual, bit for bit.  600 tiles:
+    # the persistent grid walks up to three per workgroup with no K stages
+    # between them.
+    M, N = 300, 76800
+    n_out = N // 2 if epi == "swiglu" else N
+    A = torch.zeros((M, 16), dtype=torch.uint8, device="cuda")
+    W = torch.zeros((N, 16), dtype=torch.uint8, device="cuda")
+    nsc = (M, N) if fmt == "e4m3_row" else (1, 1)
+    sa = torch.full((nsc[0],), 0.75, dtype=torch.float32, device="cuda")
+    sw = torch.full((nsc[1],), 1.5, dtype=torch.float32, device="cuda")
+    R16 = bf16_normal((M, n_out), 1.0, 41) if epi == "add" else None
+    res = dev(R16) if R16 is not None else None
+    out = torch.full((M, n_out), -1.0, dtype=torch.bfloat16, device="cuda")
+    d, e, _ = spg.make_desc(A, W, fmt, epi, out, res)
+    d.K = 0
+    assert spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), e) == 0
+    st = spg.lib.gemm_scaled(out.data_ptr(), A.data_ptr(), sa.data_ptr(), W.data_ptr(), sw.data_ptr(),
+                             res.data_ptr() if res is not None else None, e, ctypes.byref(d), None, 0,
+                             torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    gpu = host_u16(out)
+    assert np.array_equal(gpu, R16 if epi == "add" else np.zeros((M, n_out), np.uint16))
 
 
 def test_gemm_power_of_two_case_is_bitwise(spg):
