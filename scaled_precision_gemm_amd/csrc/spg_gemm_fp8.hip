@@ -340,9 +340,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     };
     for (int i = 0; i < ntile; ++i) {
         // The next tile's scale factors are loaded now, a whole tile before
-        // they are written to LDS: loads and stores retire in issue order, so
-        // loading them next to this tile's output stores would make every
-        // wave wait for its stores (and for the loads' own latency).
+        // they are written to LDS: loads and stores share the vector-memory
+        // counter, so loading them next to this tile's output stores would
+        // make every wave's wait for them wait for its stores too (and for
+        // the loads' own latency).
         float nsa = 0.0f, nsw = 0.0f;
         if (!kScaleDma && i + 1 < ntile) scale_values<EPI, SMODE>(g, Tn, nsa, nsw);
         Acc acc;
