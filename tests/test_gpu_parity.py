@@ -247,9 +247,12 @@ def test_gemm_fp8_small_shapes(spg, shape, epi, fmt):
 
 # extreme aspect ratios: many tiles along one dimension (more tiles than
 # compute units, so the persistent grid walks several per workgroup), and the
-# longest K the oracle's fp64 sums keep exact (2^16; split 8 ways along K)
+# longest K the oracle's fp64 sums keep exact (2^16; split 8 ways along K).
+# 513 x 65792 x 256 SWIGLU: 771 tiles of two K stages on the persistent
+# grid, three or four per workgroup, so every buffer of the row-wise SWIGLU
+# scale ring is used (and a last tile row of one token), checked in full.
 EXTREME = [((70000, 40, 256), "add"), ((3, 70000, 256), "store"), ((5, 80000, 64), "swiglu"),
-           ((40, 72, 65536), "store"), ((130, 264, 65536), "swiglu")]
+           ((513, 65792, 256), "swiglu"), ((40, 72, 65536), "store"), ((130, 264, 65536), "swiglu")]
 
 
 @pytest.mark.parametrize("shape,epi", EXTREME, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
