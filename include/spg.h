@@ -135,7 +135,12 @@ int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t
  *   lda, ldw : row strides of A and W in bytes of codes (NVFP4: bytes of
  *              packed codes, >= K/2); at most 2^23 (else SPG_EUNSUPPORTED)
  *   ldo, ldr : row strides of out and residual in bf16 elements; below 2^26
- *              (else SPG_EUNSUPPORTED)
+ *              (else SPG_EUNSUPPORTED).  ldr == 0 makes the residual one row
+ *              of N (N/2 never applies: ADD only) bf16 values added to every
+ *              token row: the bf16 bias epilogue (AstrAI commit log for
+ *              gemm.cuh, the commit fusing the bias: a raw bf16 bias added in
+ *              the epilogue after the operand scales, instead of a separate
+ *              elementwise add)
  *   stride_* : batch strides (bytes for A/W codes, elements for out and
  *              residual); 0 broadcasts one matrix to every batch entry
  *              (AstrAI broadcasts batches of one through a zero stride)
@@ -164,8 +169,10 @@ void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32
  *              E4M3_TENSOR: fp32 [batch] each (index 0 when broadcast);
  *              NVFP4: E4M3 block-scale planes [M, K/16] and [N, K/16],
  *              row-major (NVFP4 requires batch == 1)
- *   residual : bf16 [M, N], required for SPG_EPI_ADD, NULL otherwise; it may
- *              be the same buffer as out when ldr == ldo and strides match
+ *   residual : bf16 [M, N] (or one row [N] when ldr == 0), required for
+ *              SPG_EPI_ADD, NULL otherwise; it may be the same buffer as out
+ *              when ldr == ldo and strides match (never when ldr == 0:
+ *              SPG_EINVAL)
  *   epilogue : SPG_EPI_*; SWIGLU pairs W rows j (gate) and j + N/2 (up) and
  *              needs N even
  *   ws       : device workspace of at least gemm_scaled_workspace_bytes(d, epilogue)

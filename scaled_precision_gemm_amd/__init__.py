@@ -197,7 +197,11 @@ def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residua
     else:
         d.ldo = n_out
         d.stride_o = M * n_out if batch > 1 else 0
-    if residual is not None:
+    if residual is not None and residual.dim() == 1:
+        # one row [N]: a bias added to every token row of every batch entry
+        _need(residual.shape[0] == n_out and residual.stride(0) == 1, "a bias row must be contiguous [N]")
+        d.ldr, d.stride_r = 0, 0
+    elif residual is not None:
         r3 = residual if residual.dim() == 3 else residual.unsqueeze(0)
         d.ldr = r3.stride(1)
         d.stride_r = r3.stride(0) if r3.shape[0] > 1 else 0

@@ -52,7 +52,8 @@ int validate_desc(const spg_gemm_desc *d, int epi)
     if (d->lda > (INT64_C(1) << 23) || d->ldw > (INT64_C(1) << 23)) return SPG_EUNSUPPORTED;
     if ((d->stride_a & 15) || (d->stride_w & 15)) return SPG_EINVAL;
     if (d->ldo < nout) return SPG_EINVAL;
-    if (epi == SPG_EPI_ADD && d->ldr < nout) return SPG_EINVAL;
+    // ldr == 0: one bf16 row (a bias) added to every token row
+    if (epi == SPG_EPI_ADD && d->ldr != 0 && d->ldr < nout) return SPG_EINVAL;
     // tile ids are computed in 32-bit arithmetic
     {
         const int64_t tm = cdiv(d->M, kTile), tn = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
@@ -247,6 +248,7 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     if (!aligned2(out) || !aligned16(A) || !aligned16(W)) return SPG_EINVAL;
     if (epilogue == SPG_EPI_ADD) {
         if (!residual || !aligned2(residual)) return SPG_EINVAL;
+        if (d->ldr == 0 && residual == out) return SPG_EINVAL;   // the bias row would be overwritten
     } else if (residual) {
         return SPG_EINVAL;
     }

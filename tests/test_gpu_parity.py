@@ -543,8 +543,11 @@ def test_gemm_tail_split_sampled(spg, fmt, K):
     (4000, 4312, 1040, "add", "e4m3_row", 1),
     (3900, 8704, 1024, "swiglu", "e4m3_row", 1),
     (2048, 4352, 1024, "store", "e4m3_tensor", 2),
-], ids=["store", "add_ragged", "swiglu_ragged", "tensor_batch2"])
+    (4000, 4312, 1040, "bias", "e4m3_row", 1),
+], ids=["store", "add_ragged", "swiglu_ragged", "tensor_batch2", "bias_ragged"])
 def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
+    bias = epi == "bias"        # ADD with one bf16 row broadcast to every token row
+    epi = "add" if bias else epi
     plan = spg.gemm_plan(M, N, K, fmt, epi, batch=B)
     assert plan["tail_bm"] == 128 and plan["tail_tiles"] in (16, 32) and plan["tail_split"] == 1
     rng = np.random.default_rng(M + N + K)
@@ -552,11 +555,15 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
     W16 = bf16_normal((N, K), 0.02, 81)
     n_out = N // 2 if epi == "swiglu" else N
     R16 = bf16_normal((M, n_out), 1.0, 82) if epi == "add" else None
+    res = dev(R16) if R16 is not None else None
+    if bias:
+        row = bf16_normal((n_out,), 1.0, 83)
+        R16, res = np.broadcast_to(row, (M, n_out)), dev(row)
     A, W = dev(A16), dev(W16)
     if fmt == "e4m3_row":
         qa, sa = spg.quantize_rowwise(A)
         qw, sw = spg.quantize_rowwise(W)
-        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=dev(R16) if R16 is not None else None)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res)
     else:
         qa, sa = spg.quantize_tensor(A)
         qw, sw = spg.quantize_tensor(W)
@@ -590,6 +597,65 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
         D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
         y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, Rs)
         check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"half tail {M}x{N}x{K} {epi} {fmt} batch {b}")
+
+
+# ---------------------------------------------------------------------------
+# bf16 bias: the ADD epilogue with one residual row (row stride 0) added to
+# every token row - unsplit tiles, several tiles per persistent workgroup,
+# split-K with its reduction (many and few tokens), both FP8 scale forms and
+# NVFP4, and a batch sharing the bias.
+# ---------------------------------------------------------------------------
+
+BIAS = [((128, 256, 512), "e4m3_row", 1), ((300, 258, 1040), "e4m3_tensor", 1), ((17, 34, 48), "e4m3_row", 1),
+        ((2304, 7936, 256), "e4m3_row", 1), ((520, 1030, 2064), "e4m3_row", 1), ((16, 5120, 17408), "e4m3_row", 1),
+        ((96, 300, 512), "e4m3_tensor", 3), ((257, 300, 512), "nvfp4", 1), ((64, 64, 256), "nvfp4", 1)]
+
+
+@pytest.mark.parametrize("shape,fmt,B", BIAS, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_gemm_bias_row(spg, shape, fmt, B):
+    M, N, K = shape
+    A16 = bf16_normal((B, M, K) if B > 1 else (M, K), 1.0, 90 + M)
+    W16 = bf16_normal((N, K), 0.02, 91 + N)
+    row = bf16_normal((N,), 1.0, 92 + K)
+    A, W, bias = dev(A16), dev(W16), dev(row)
+    if fmt == "nvfp4":
+        qa, bsa, ta = spg.quantize_block16(A)
+        qw, bsw, tw = spg.quantize_block16(W)
+        out = spg.gemm_scaled(qa, bsa, qw, bsw, "add", residual=bias, fmt="nvfp4", tscale_a=ta, tscale_w=tw)
+    elif fmt == "e4m3_row":
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, "add", residual=bias)
+    else:
+        qa, sa = spg.quantize_tensor(A)
+        qw, sw = spg.quantize_tensor(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, "add", residual=bias, fmt="e4m3_tensor")
+    gpu = host_u16(out)
+    R16 = np.broadcast_to(row, (M, N))
+    for b in range(B):
+        Ab = A16[b] if B > 1 else A16
+        if fmt == "nvfp4":
+            ref = oracle_nvfp4(Ab, W16, "add", R16)
+        elif fmt == "e4m3_row":
+            ref = oracle_fp8(Ab, W16, "add", "e4m3_row", R16)
+        else:
+            # the batch's per-tensor scales: each entry's own amax
+            qa_o, sa_o = oracle.quantize_tensor(Ab)
+            qw_o, sw_o = oracle.quantize_tensor(W16)
+            D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+            y, S, o = oracle.epilogue("add", D, Da, sa_o[0], sw_o[0], R16)
+            ref = dict(y=y, S=S, out=o)
+        check_close(gpu[b] if B > 1 else gpu, ref["y"], ref["S"], f"bias {shape} {fmt} batch {b}")
+
+
+def test_gemm_bias_row_with_zero_weights_is_the_bias(spg):
+    # every product is zero: each output row is the bias, bit for bit, also
+    # through split-K (16 tokens over a long K) and its reduction
+    for M, N, K in [(300, 260, 256), (16, 520, 8192)]:
+        A16 = bf16_normal((M, K), 1.0, 7)
+        row = bf16_normal((N,), 1.0, 8)
+        gpu = run_fp8(spg, A16, np.zeros((N, K), np.uint16), "add", "e4m3_row", row)
+        assert np.array_equal(gpu, np.tile(row, (M, 1))), (M, N, K)
 
 
 # ---------------------------------------------------------------------------

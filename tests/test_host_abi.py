@@ -92,7 +92,7 @@ def test_desc_init_defaults(spg):
 @pytest.mark.parametrize("case", [
     "null_desc", "bad_format", "bad_epilogue", "k_not_16", "nvfp4_k_not_32", "lda_short", "lda_unaligned",
     "ldo_short", "swiglu_odd_n", "add_without_residual", "store_with_residual", "null_a", "misaligned_a",
-    "negative_m", "zero_batch", "nvfp4_no_tscale", "negative_stride",
+    "negative_m", "zero_batch", "nvfp4_no_tscale", "negative_stride", "ldr_short", "bias_row_in_place",
 ])
 def test_gemm_validation_errors(spg, case):
     d = desc(spg, 64, 64, 64, 0)
@@ -133,7 +133,21 @@ def test_gemm_validation_errors(spg, case):
         d = desc(spg, 64, 64, 64, 2)
     elif case == "negative_stride":
         d.stride_a = -16
+    elif case == "ldr_short":
+        epi, d.ldr, kw["res"] = 1, 32, FAKE2
+    elif case == "bias_row_in_place":
+        # ldr == 0 (one bias row) with the output as that row
+        epi, d.ldr, kw["res"] = 1, 0, FAKE
     assert call_gemm(spg, d, epi, **kw) == EINVAL
+
+
+def test_gemm_bias_row_is_a_valid_residual(spg):
+    # ldr == 0 passes validation (the plan and workspace queries accept it)
+    d = desc(spg, 64, 64, 64, 0)
+    d.ldr = 0
+    p = spg.Plan()
+    assert spg.lib.spg_gemm_plan(ctypes.byref(d), 1, 256, ctypes.byref(p)) == 0
+    assert spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), 1) == 0
 
 
 def test_gemm_nvfp4_batch_unsupported(spg):

@@ -104,6 +104,23 @@ def test_zero_weight_add_returns_residual_bitwise():
     assert np.all(res["S"] == 0)
 
 
+def test_bias_row_adds_to_every_token_row():
+    # the bf16 bias epilogue is the residual add with one row broadcast to
+    # every token row (AstrAI commit log for gemm.cuh, the commit fusing the
+    # bias): zero weights give the bias itself in every row, bit for bit, and
+    # otherwise y is the store result plus the bias value of the column
+    A16 = bf16_normal((8, 32), 1.0, 13)
+    bias = bf16_normal((12,), 1.0, 14)
+    R = np.broadcast_to(bias, (8, 12))
+    z = oracle.linear_e4m3_rowwise(A16, np.zeros((12, 32), np.uint16), "add", residual=R)
+    assert np.array_equal(z["out"], np.tile(bias, (8, 1)))
+    W16 = bf16_normal((12, 32), 0.02, 15)
+    b = oracle.linear_e4m3_rowwise(A16, W16, "add", residual=R)
+    st = oracle.linear_e4m3_rowwise(A16, W16, "store")
+    bias_f = (bias.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(b["y"], st["y"] + bias_f[None, :])
+
+
 def test_swiglu_matches_scipy_logistic_and_pairs_rows():
     A16 = bf16_normal((6, 64), 1.0, 11)
     W16 = bf16_normal((10, 64), 0.02, 12)
