@@ -77,7 +77,7 @@ def gemm_bytes(wl) -> int:
         ab = wl.M * wl.K
         wb = wl.N * wl.K
     out = 2 * wl.M * wl.n_out
-    res = 2 * wl.M * wl.n_out if wl.epilogue == "add" else 0
+    res = 2 * (1 if wl.bias else wl.M) * wl.n_out if wl.epilogue == "add" else 0
     return b * (ab + wb + out + res)
 
 
@@ -340,7 +340,12 @@ def cpu_baseline(wl, A16, W16, R16, budget_s: float):
 
     def step(rows):
         a = np.ascontiguousarray(A16[:rows])
-        r = np.ascontiguousarray(R16[:rows]) if R16 is not None else None
+        if R16 is None:
+            r = None
+        elif wl.bias:
+            r = np.broadcast_to(R16, (rows, wl.n_out))
+        else:
+            r = np.ascontiguousarray(R16[:rows])
         if wl.fmt == "e4m3_row":
             qa, sa = oracle.quantize_rowwise(a)
             D, Da = oracle.gemm_e4m3_sums(qa, Wq)
@@ -551,7 +556,7 @@ def main():
         "dtype": "f16" if wl.fmt == "nvfp4" else "fp8_e4m3",
         "data": "synthetic",
         "config": {
-            "workload": wl.name, "format": wl.fmt, "epilogue": wl.epilogue,
+            "workload": wl.name, "format": wl.fmt, "epilogue": "add (bf16 bias row)" if wl.bias else wl.epilogue,
             "M": wl.M, "N": wl.N, "K": wl.K, "batch": wl.batch,
             "step": "activation quantize + gemm_scaled (weights pre-quantized)",
             "buffer_sets": sets, "plan": plan,

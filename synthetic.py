@@ -49,6 +49,7 @@ class Workload:
     a_std: float = 1.0
     w_std: float = 0.02
     seed: int = 0
+    bias: bool = False  # "add" with one bf16 row [n_out] (a bias) instead of an [M, n_out] residual
 
     @property
     def n_out(self) -> int:
@@ -70,7 +71,7 @@ class Workload:
         W = bf16_normal(self.w_shape(), self.w_std, self.seed + 2)
         R = None
         if self.epilogue == "add":
-            R = bf16_normal((self.M, self.n_out), 1.0, self.seed + 3)
+            R = bf16_normal((self.n_out,) if self.bias else (self.M, self.n_out), 1.0, self.seed + 3)
         return A, W, R
 
 
@@ -91,4 +92,6 @@ WORKLOADS = {
     # the same two FP8 linears at 16 tokens (the narrow, weight-streaming route)
     "fp8_row_add_t16": Workload("fp8_row_add_t16", "e4m3_row", "add", 16, 5120, 17408, seed=600),
     "fp8_row_swiglu_t16": Workload("fp8_row_swiglu_t16", "e4m3_row", "swiglu", 16, 34816, 5120, seed=610),
+    # the T=4096 [N=5120, K=6144] linear in row-scaled FP8 with a fused bf16 bias row
+    "fp8_row_bias_t4096": Workload("fp8_row_bias_t4096", "e4m3_row", "add", 4096, 5120, 6144, seed=700, bias=True),
 }

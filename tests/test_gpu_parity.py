@@ -433,7 +433,7 @@ def sample(n, count, rng, tile=256):
 
 
 @pytest.mark.parametrize("name", ["fp8_row_add_t1024", "fp8_row_swiglu_t4096", "fp8_tensor_square_8192",
-                                  "fp8_tensor_bmm64_512", "nvfp4_add_t4096"])
+                                  "fp8_tensor_bmm64_512", "nvfp4_add_t4096", "fp8_row_bias_t4096"])
 def test_workload_full_size_sampled(spg, name):
     wl = WORKLOADS[name]
     rng = np.random.default_rng(99)
@@ -465,7 +465,8 @@ def test_workload_full_size_sampled(spg, name):
         rows = sample(wl.M, 40, rng)
         cols = sample(wl.n_out, 40, rng, tile=128 if wl.epilogue == "swiglu" else 256)
         wrows = np.concatenate([cols, cols + wl.N // 2]) if wl.epilogue == "swiglu" else cols
-        Rs = np.ascontiguousarray(R16[np.ix_(rows, cols)]) if R16 is not None else None
+        Rb = np.broadcast_to(R16, (wl.M, wl.n_out)) if wl.bias else R16
+        Rs = np.ascontiguousarray(Rb[np.ix_(rows, cols)]) if R16 is not None else None
         if wl.fmt == "e4m3_row":
             qa_o, sa_o = oracle.quantize_rowwise(np.ascontiguousarray(Ab[rows]))
             qw_o, sw_o = oracle.quantize_rowwise(np.ascontiguousarray(Wb[wrows]))
