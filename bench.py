@@ -36,11 +36,13 @@ DEFAULT_WORKLOAD = "fp8_row_swiglu_t4096"
 PEAK_TFLOPS = {"fp8": 5000.0, "f16": 2500.0}
 HBM_GBS = 8000.0
 
-# the kernels of one gemm_scaled call: the GEMM, its split-K reduction
+# the kernels of one gemm_scaled call (the GEMM, its split-K reduction) and
+# the planner that picks their launches (split, tail, grid), which changes
+# the traffic as much as the kernels do
 GEMM_SOURCES = {
-    "e4m3_row": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip"],
-    "e4m3_tensor": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip"],
-    "nvfp4": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h", "spg_splitk.hip"],
+    "e4m3_row": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip", "spg_api.hip"],
+    "e4m3_tensor": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip", "spg_api.hip"],
+    "nvfp4": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h", "spg_splitk.hip", "spg_api.hip"],
 }
 
 

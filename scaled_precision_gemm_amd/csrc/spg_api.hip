@@ -66,14 +66,38 @@ int validate_desc(const spg_gemm_desc *d, int epi)
     return SPG_OK;
 }
 
-// The split-K factor: when the output tiles fill less than half of the
-// compute units - or for up to 64 tokens, where the partial tiles hold only
-// those rows and the product streams its weights (more compute units stream
-// more of them at once) - pick the split s <= 8 (K / s >= 1024) that
-// minimises waves(tiles * s) / s, the wave-quantised time of the split work.
-int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk)
+// The split-K factor, when the output tiles fill less than half of the
+// compute units or the product has at most 64 tokens (its partial tiles
+// then hold only those rows, and it streams its weights: more compute units
+// stream more of them at once).  FP8 at up to 64 tokens with at most one
+// wave of tiles: the cost model below.  Otherwise the split s <= 8
+// (K / s >= 1024) that minimises waves(tiles * s) / s, the wave-quantised
+// time of the split work.  (With s <= 8 and K / s >= 1024 no slice is empty.)
+int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk, bool fp8)
 {
     if (tiles * 2 > units && M > 64) return 1;
+    if (M <= 64 && fp8 && tiles <= units) {
+        // Few-token FP8 products stream their weights, and a workgroup's fixed
+        // cost (pipeline fill, partial stores, its share of the reduction) is
+        // worth about eight 128-deep stages: minimise waves * (slice + 1024)
+        // over s <= 8 with slices of at least 1024.  Measured (16 tokens):
+        // 34816 x 5120 SwiGLU s = 1, 2, 3, 4, 5, 8, 10 -> 52.0, 58.6, 49.2,
+        // 53.8, 52.8, 58.2, 63.8 us (picks 3); 5120 x 17408 add s = 4, 6, 8,
+        // 12, 16 -> 39.1, 31.3, 28.1, 25-30, 33 us (picks 8: 12 was no faster
+        // on average over three A/B rounds and spread wider).
+        int best = 1;
+        double best_cost = (double)K + 1024.0;   // unsplit: one wave of tiles
+        for (int s = 2; s <= 8; ++s) {
+            const int64_t chunk = cdiv(cdiv(K, s), bk) * bk;
+            if (K / s < 1024) break;
+            const double cost = (double)cdiv(tiles * s, units) * ((double)chunk + 1024.0);
+            if (cost < best_cost - 1e-9) {
+                best_cost = cost;
+                best = s;
+            }
+        }
+        return best;
+    }
     int best = 1;
     double best_cost = 1.0;
     for (int s = 2; s <= 8; ++s) {
@@ -85,7 +109,6 @@ int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk)
             best = s;
         }
     }
-    (void)bk;
     return best;
 }
 
@@ -101,7 +124,7 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     const int64_t tiles_m = cdiv(d->M, kTile);
     const int64_t tiles_n = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
     p->tiles = tiles_m * tiles_n * d->batch;
-    p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->M, d->K, units, p->bk) : 1;
+    p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->M, d->K, units, p->bk, d->format != SPG_FMT_NVFP4) : 1;
     p->kernel = d->format == SPG_FMT_NVFP4 ? 1 : 0;
     p->tail_split = 1;
     p->tail_tiles = 0;

@@ -215,6 +215,16 @@ def test_plans_for_the_workloads(spg):
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (16 * 136, 1, 256)
     p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu", units=304)
     assert p["workgroups"] == 304
+    # 16 tokens: the weight-streaming cost model (waves * (slice + 1024))
+    # picks 3 slices for the SwiGLU (408 workgroups, 1.6 waves beat 2.7 at
+    # 5 slices) and keeps 8 for the down-projection (one wave of 160)
+    p = spg.gemm_plan(16, 34816, 5120, "e4m3_row", "swiglu")
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (136, 3, 408)
+    p = spg.gemm_plan(16, 5120, 17408, "e4m3_row", "add")
+    assert (p["tiles"], p["split_k"], p["workgroups"]) == (20, 8, 160)
+    # NVFP4 at 16 tokens keeps the wave-quantised model
+    p = spg.gemm_plan(16, 34816, 5120, "nvfp4", "swiglu")
+    assert p["split_k"] == 5
     p = spg.gemm_plan(128, 256, 512, "e4m3_row", "store")
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (1, 1, 1)
     p = spg.gemm_plan(512, 512, 512, "e4m3_tensor", "store", batch=64)
