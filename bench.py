@@ -157,21 +157,27 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
     # One gemm_scaled call is one to three dispatches (main tiles, a K-split
     # tail, its reduction); bench.py's events bracket the whole call.  The
     # timed steps are the last `--steps` calls of the traced run.
-    first = command.strip().splitlines()[0].split() if command.strip() else []
-    steps, warmup = 200, 150
-    for i, a in enumerate(first):
-        if a == "--steps":
-            steps = int(first[i + 1])
-        if a == "--warmup":
-            warmup = int(first[i + 1])
+    lines_ = command.strip().splitlines()
+
+    def run_counts(line):
+        """(timed steps, all gemm_scaled calls) of the bench run on command
+        line `line` (the bench's defaults where a flag is not given)."""
+        toks = lines_[line].split() if len(lines_) > line else []
+        val = {"--steps": 200, "--warmup": 10, "--settle-launches": 150}
+        for i, a in enumerate(toks[:-1]):
+            if a in val:
+                val[a] = int(toks[i + 1])
+        return val["--steps"], val["--steps"] + val["--warmup"] + val["--settle-launches"]
+
+    steps, n_calls = run_counts(0)
     timed_avg_us = None
     try:
         trace = _read_csv(_find(stats_dir, "kernel_trace.csv"))
         durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in
                 sorted(trace, key=lambda r: int(r["Start_Timestamp"]))
                 if "gemm_" in r["Kernel_Name"] or "splitk_reduce" in r["Kernel_Name"]]
-        per_call = len(durs) // (steps + warmup)
-        if per_call >= 1 and len(durs) == per_call * (steps + warmup):
+        per_call = len(durs) // n_calls
+        if per_call >= 1 and len(durs) == per_call * n_calls:
             timed_avg_us = float(np.sum(durs[-steps * per_call:])) / steps / 1e3
     except FileNotFoundError:
         pass
@@ -179,16 +185,7 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
     def per_call(d, counter, line):
         """Counter value of each gemm_scaled call (summed over its dispatches)
         and of the copy dispatches, from the run of command line `line`."""
-        calls = 4
-        toks = command.strip().splitlines()[line].split() if len(command.strip().splitlines()) > line else []
-        st = wu = None
-        for i, a in enumerate(toks):
-            if a == "--steps":
-                st = int(toks[i + 1])
-            if a == "--warmup":
-                wu = int(toks[i + 1])
-        if st is not None and wu is not None:
-            calls = st + wu
+        _, calls = run_counts(line)
         rows = sorted(_read_csv(_find(d, "counter_collection.csv")), key=lambda r: int(r["Dispatch_Id"]))
         vals = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter
                 and ("gemm_" in r["Kernel_Name"] or "splitk_reduce" in r["Kernel_Name"])]
@@ -212,19 +209,13 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
     if counters_dir:
         # duration-weighted over the dispatches of each call, median over the
         # timed calls (command line 4 names its --steps / --warmup)
-        toks = command.strip().splitlines()[3].split() if len(command.strip().splitlines()) > 3 else []
-        st, wu = 20, 100
-        for i, a in enumerate(toks):
-            if a == "--steps":
-                st = int(toks[i + 1])
-            if a == "--warmup":
-                wu = int(toks[i + 1])
+        st, n_all = run_counts(3)
         rows = sorted(_read_csv(_find(counters_dir, "counter_collection.csv")), key=lambda r: int(r["Dispatch_Id"]))
         util = {}
         for metric in ("MfmaUtil", "LdsUtil"):
             disp = [(float(r["Counter_Value"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows
                     if r["Counter_Name"] == metric and ("gemm_" in r["Kernel_Name"] or "splitk_reduce" in r["Kernel_Name"])]
-            k = max(1, len(disp) // (st + wu))
+            k = max(1, len(disp) // n_all)
             calls = [disp[i:i + k] for i in range(0, len(disp) - k + 1, k)][-st:]
             per_call = [sum(v * d for v, d in c) / max(1, sum(d for _, d in c)) for c in calls]
             util[metric] = float(np.median(per_call)) if per_call else None
@@ -386,11 +377,16 @@ def cpu_baseline(wl, A16, W16, R16, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    # MI355X's power controller throttles hard a few launches after an idle
-    # spell and needs ~100 launches (~60 ms) of this load to settle; the
-    # default warmup covers that so the timed steps see the sustained clock
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=150)
+    ap.add_argument("--warmup", type=int, default=10)
+    # MI355X's power controller throttles hard a few launches after an idle
+    # spell and needs ~100 launches (~60 ms) of this load to settle.  The
+    # settle phase runs before the warmup, is reported as its own field
+    # (settle_launches, settle_ms) and is never counted as warmup.
+    ap.add_argument("--settle-launches", type=int, default=150,
+                    help="steps run (and reported) before the warmup so the power controller settles")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the shader clock after each timed step")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--sets", type=int, default=3, help="rotating input/weight buffer sets")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -489,14 +485,28 @@ def main():
         del src, dst
 
     stream = torch.cuda.current_stream()
-    n_ev = max(args.warmup, args.steps)
+    n_ev = max(args.warmup, args.steps, args.settle_launches, 1)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
 
+    settle_ms = 0.0
+    if args.settle_launches > 0:
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for i in range(args.settle_launches):
+            ev[i][0].record()
+            step(i)
+            ev[i][2].record()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        settle_ms = s0.elapsed_time(s1)
     for i in range(args.warmup):
         ev[i][0].record()
         step(i)
         ev[i][2].record()
     torch.cuda.synchronize()
+    # shader clock right after each timed step's GEMM (one-wave probe, a few
+    # microseconds; it runs inside the timed region, after the GEMM's event)
+    clk = None if args.no_clock else torch.zeros((args.steps, 4), dtype=torch.int64, device="cuda")
 
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -507,6 +517,8 @@ def main():
         ev[i][0].record()
         step(i)
         ev[i][2].record()
+        if clk is not None:
+            spg.probe_clock(clk[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -541,9 +553,20 @@ def main():
         "algorithmic_bytes": alg_bytes,
         "flops_per_launch": flops,
         "launch_ms_avg": round(gemm_avg, 4),
+        "launch_ms_median": round(float(np.median(gemm_ms)), 4),
         "launch_ms_p10_p90": [round(float(np.percentile(gemm_ms, 10)), 4),
                               round(float(np.percentile(gemm_ms, 90)), 4)],
+        "frac_at_median": round((flops / (float(np.median(gemm_ms)) * 1e-3) / 1e12 / peak) if not hbm_bound else
+                                (alg_bytes / (float(np.median(gemm_ms)) * 1e-3) / 1e9 / HBM_GBS), 4),
     }
+    if clk is not None:
+        c = clk.cpu().numpy().astype(np.float64)
+        ghz = (c[:, 1] - c[:, 0]) / np.maximum(1.0, c[:, 3] - c[:, 2]) / 10.0
+        roofline["sclk_ghz_timed"] = {"median": round(float(np.median(ghz)), 3),
+                                      "min": round(float(ghz.min()), 3), "max": round(float(ghz.max()), 3)}
+        # the MFMA peak scaled to the clock the timed steps actually ran at
+        if not hbm_bound:
+            roofline["frac_of_peak_at_timed_sclk"] = round(achieved / (peak * float(np.median(ghz)) / 2.4), 4)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -551,6 +574,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_launches": args.settle_launches,
+        "settle_ms": round(settle_ms, 2),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

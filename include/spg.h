@@ -170,13 +170,16 @@ void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32
  *              NVFP4: E4M3 block-scale planes [M, K/16] and [N, K/16],
  *              row-major (NVFP4 requires batch == 1)
  *   residual : bf16 [M, N] (or one row [N] when ldr == 0), required for
- *              SPG_EPI_ADD, NULL otherwise; it may be the same buffer as out
- *              when ldr == ldo and strides match (never when ldr == 0:
- *              SPG_EINVAL)
+ *              SPG_EPI_ADD, NULL otherwise; it may be the output itself
+ *              (residual == out, ldr == ldo, stride_r == stride_o); any
+ *              other overlap of the two, a bias row inside the output
+ *              included, is SPG_EINVAL
  *   epilogue : SPG_EPI_*; SWIGLU pairs W rows j (gate) and j + N/2 (up) and
  *              needs N even
  *   ws       : device workspace of at least gemm_scaled_workspace_bytes(d, epilogue)
  *              (may be NULL when that is 0)
+ *   With batch > 1 the output entries must not overlap:
+ *   stride_o >= (M - 1) * ldo + n_out, else SPG_EINVAL.
  * Results: each element within 2^-8 |y| + 2^-12 S of the exact value y,
  * where S is the scaled sum of |products| (fp32 accumulation order is free).
  */
@@ -260,6 +263,14 @@ int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units, spg_plan 
  * ...), so the XOR of all sink words is the XOR of the whole buffer.
  */
 int spg_probe_mfma(int kind, int64_t iters, int32_t workgroups, float *sink, uint64_t *clocks, void *stream);
+
+/* spg_probe_clock: one wave reads the shader-clock counter and the 100 MHz
+ * reference counter around `spins` rounds of a dependent integer hash and
+ * writes them to clocks (device, 4 x uint64, same order as spg_probe_mfma).
+ * Enqueued right after a GEMM on its stream, it gives the shader clock the
+ * power controller had set for that GEMM.  SPG_EINVAL for spins < 1, a null
+ * or misaligned pointer. */
+int spg_probe_clock(int64_t spins, uint64_t *clocks, void *stream);
 int spg_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus

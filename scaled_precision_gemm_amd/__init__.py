@@ -16,9 +16,10 @@ import torch
 
 __all__ = [
     "quantize_rowwise", "quantize_tensor", "quantize_block16", "gemm_scaled",
-    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read", "lib", "LIB_PATH",
+    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read", "probe_clock",
+    "lib", "LIB_PATH",
     "FMT_E4M3_ROW", "FMT_E4M3_TENSOR", "FMT_NVFP4", "EPI_STORE", "EPI_ADD", "EPI_SWIGLU",
-    "SpgError",
+    "SpgError", "check_operands",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspg.so")
@@ -77,6 +78,7 @@ SIGNATURES = {
     "spg_gemm_plan": (ctypes.c_int, [ctypes.POINTER(GemmDesc), ctypes.c_int, _I32, ctypes.POINTER(Plan)]),
     "spg_probe_mfma": (ctypes.c_int, [ctypes.c_int, _I64, _I32, _P, _P, _P]),
     "spg_probe_read": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "spg_probe_clock": (ctypes.c_int, [_I64, _P, _P]),
 }
 
 
@@ -211,6 +213,64 @@ def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residua
     return d, epi, batched
 
 
+def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_a=None, tscale_w=None):
+    """Shapes, dtypes, strides and devices of a gemm_scaled call, checked
+    before anything reaches the library (raises ValueError).  The library
+    trusts the sizes it is given, so an output, residual or scale tensor
+    smaller than the descriptor says would be read or written out of
+    bounds."""
+    fmt = _FMT.get(fmt, fmt)
+    epi = _EPI.get(epilogue, epilogue)
+    _need(fmt in (FMT_E4M3_ROW, FMT_E4M3_TENSOR, FMT_NVFP4), f"unknown format {fmt}")
+    _need(epi in (EPI_STORE, EPI_ADD, EPI_SWIGLU), f"unknown epilogue {epilogue}")
+    _need(isinstance(A, torch.Tensor) and isinstance(W, torch.Tensor), "A and W must be tensors")
+    _need(A.dtype == torch.uint8 and W.dtype == torch.uint8, "A and W must be uint8 code tensors")
+    _need(A.dim() in (2, 3) and W.dim() in (2, 3), "A and W must be 2-D or 3-D")
+    _need(A.stride(-1) == 1 and W.stride(-1) == 1, "rows of A and W must be contiguous")
+    dev = A.device
+    for name, t in (("W", W), ("sa", sa), ("sw", sw), ("out", out), ("residual", residual),
+                    ("tscale_a", tscale_a), ("tscale_w", tscale_w)):
+        _need(t is None or (isinstance(t, torch.Tensor) and t.device == dev), f"{name} must be on {dev}")
+    Ab = A.shape[0] if A.dim() == 3 else 1
+    Wb = W.shape[0] if W.dim() == 3 else 1
+    batch = max(Ab, Wb)
+    _need(Ab in (1, batch) and Wb in (1, batch), "batch sizes of A and W must match or be 1")
+    batched = A.dim() == 3 or W.dim() == 3
+    M, N, Kc = A.shape[-2], W.shape[-2], A.shape[-1]
+    _need(W.shape[-1] == Kc, "A and W disagree on K")
+    n_out = N // 2 if epi == EPI_SWIGLU else N
+    _need(sa is not None and sw is not None, "sa and sw are required")
+    if fmt == FMT_E4M3_ROW:
+        _need(sa.dtype == torch.float32 and sw.dtype == torch.float32, "row scales must be fp32")
+        _need(sa.is_contiguous() and sa.numel() == Ab * M, f"sa must hold {Ab * M} fp32 row scales")
+        _need(sw.is_contiguous() and sw.numel() == Wb * N, f"sw must hold {Wb * N} fp32 row scales")
+    elif fmt == FMT_E4M3_TENSOR:
+        _need(sa.dtype == torch.float32 and sw.dtype == torch.float32, "tensor scales must be fp32")
+        _need(sa.is_contiguous() and sa.numel() == Ab, f"sa must hold {Ab} fp32 tensor scale(s)")
+        _need(sw.is_contiguous() and sw.numel() == Wb, f"sw must hold {Wb} fp32 tensor scale(s)")
+    else:
+        _need(not batched, "NVFP4 takes one product (2-D operands)")
+        _need(sa.dtype == torch.uint8 and sw.dtype == torch.uint8, "NVFP4 block scales are uint8 E4M3 codes")
+        _need(tuple(sa.shape) == (M, 2 * Kc // 16) and sa.is_contiguous(), "sa must be a contiguous [M, K/16] plane")
+        _need(tuple(sw.shape) == (N, 2 * Kc // 16) and sw.is_contiguous(), "sw must be a contiguous [N, K/16] plane")
+        for name, t in (("tscale_a", tscale_a), ("tscale_w", tscale_w)):
+            _need(t is not None and t.dtype == torch.float32 and t.numel() == 1, f"{name} must be one fp32 value")
+    if out is not None:
+        want = (batch, M, n_out) if batched else (M, n_out)
+        _need(out.dtype == torch.bfloat16, "out must be bf16")
+        _need(tuple(out.shape) == want, f"out must have shape {want}")
+        _need(out.stride(-1) == 1, "rows of out must be contiguous")
+    if epi == EPI_ADD:
+        _need(residual is not None, "the add epilogue needs a residual")
+        _need(residual.dtype == torch.bfloat16, "residual must be bf16")
+        _need(residual.stride(-1) == 1, "rows of the residual must be contiguous")
+        shapes = [(n_out,), (M, n_out)] + ([(batch, M, n_out), (1, M, n_out)] if batched else [])
+        _need(tuple(residual.shape) in shapes, f"residual must have one of the shapes {shapes}")
+    else:
+        _need(residual is None, "a residual is taken only by the add epilogue")
+    return fmt, epi
+
+
 def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
                 out=None, tscale_a=None, tscale_w=None, workspace=None):
     """out = epilogue(scale * A W^T) in bf16.
@@ -220,14 +280,13 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
     nvfp4: A uint8 [M,K/2], sa uint8 [M,K/16]; W [N,K/2], sw [N,K/16];
            tscale_a, tscale_w fp32 [1]
     """
+    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w)
+    _need(A.is_cuda, "operands must be CUDA tensors")
     d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w)
     n_out = d.N // 2 if epi == EPI_SWIGLU else d.N
     if out is None:
         shape = (d.batch, d.M, n_out) if batched else (d.M, n_out)
         out = torch.empty(shape, dtype=torch.bfloat16, device=A.device)
-    _need(out.dtype == torch.bfloat16, "out must be bf16")
-    if residual is not None:
-        _need(residual.dtype == torch.bfloat16, "residual must be bf16")
     nws = lib.gemm_scaled_workspace_bytes(ctypes.byref(d), epi)
     if nws > 0 and (workspace is None or workspace.numel() < nws):
         workspace = torch.empty((nws,), dtype=torch.uint8, device=A.device)
@@ -289,3 +348,12 @@ def probe_read(buf: torch.Tensor, workgroups: int):
     nbytes = buf.numel() * buf.element_size()
     _check(lib.spg_probe_read(_ptr(buf), nbytes, workgroups, _ptr(sink), _stream(buf)), "spg_probe_read")
     return sink
+
+
+def probe_clock(clocks: torch.Tensor, spins: int = 2000):
+    """Enqueue the clock probe on the current stream, writing four counters
+    into `clocks` (int64 CUDA tensor of 4 elements, e.g. a row of a larger
+    one): shader clock in GHz = (c[1] - c[0]) / (c[3] - c[2]) / 10."""
+    _need(clocks.dtype == torch.int64 and clocks.numel() == 4 and clocks.is_contiguous(),
+          "probe_clock: clocks must be 4 contiguous int64 values")
+    _check(lib.spg_probe_clock(spins, _ptr(clocks), _stream(clocks)), "spg_probe_clock")

@@ -269,9 +269,20 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     if (d->M == 0 || nout == 0) return SPG_OK;
     if (!out || !A || !W || !sa || !sw) return SPG_EINVAL;
     if (!aligned2(out) || !aligned16(A) || !aligned16(W)) return SPG_EINVAL;
+    // batch entries of the output must not overlap (several entries would
+    // write the same elements concurrently)
+    if (d->batch > 1 && d->stride_o < (d->M - 1) * d->ldo + nout) return SPG_EINVAL;
     if (epilogue == SPG_EPI_ADD) {
         if (!residual || !aligned2(residual)) return SPG_EINVAL;
-        if (d->ldr == 0 && residual == out) return SPG_EINVAL;   // the bias row would be overwritten
+        // The residual may be the output itself (read and rewritten by the
+        // same lane) only with the same element layout: same pointer, row
+        // stride and batch stride.  Any other overlap - including a bias row
+        // (ldr == 0) inside the output - is rejected.
+        const uintptr_t o0 = (uintptr_t)out, r0 = (uintptr_t)residual;
+        const uintptr_t o1 = o0 + 2 * (uintptr_t)((d->batch - 1) * d->stride_o + (d->M - 1) * d->ldo + nout);
+        const uintptr_t r1 = r0 + 2 * (uintptr_t)((d->batch - 1) * d->stride_r + (d->M - 1) * d->ldr + nout);
+        const bool same = r0 == o0 && d->ldr == d->ldo && d->stride_r == d->stride_o;
+        if (r0 < o1 && o0 < r1 && !same) return SPG_EINVAL;
     } else if (residual) {
         return SPG_EINVAL;
     }

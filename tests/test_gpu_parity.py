@@ -35,11 +35,9 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
 
 def check_close(gpu_bits, y, S, what):
     ok, excess = oracle.within_tolerance(gpu_bits, y, S)
-    exact = np.mean(gpu_bits == np.vectorize(oracle.bf16_from_f64, otypes=[np.uint16])(y)) if y.size < 300000 else None
     bad = np.argwhere(~ok)
     assert ok.all(), (f"{what}: {len(bad)} of {ok.size} outside the bound; worst excess {excess.max():.3g} "
                       f"at {bad[:5].tolist()}")
-    return exact
 
 
 # ---------------------------------------------------------------------------
@@ -116,6 +114,44 @@ def test_quantize_rowwise_every_amax_exponent(spg, K):
         qto, sto = oracle.quantize_tensor(x[i:i + 1])
         assert np.array_equal(st.cpu().numpy().view(np.uint32), sto.view(np.uint32))
         assert np.array_equal(qt.cpu().numpy(), qto)
+
+
+def _every_amax_rows(a_lo, a_hi):
+    """Rows [amax, every bf16 x with |x| <= amax] for the positive finite
+    bf16 amax patterns a_lo .. a_hi - 1 (positive bf16 bit patterns order as
+    their values), zero-padded to a common multiple of 16."""
+    a = np.arange(a_lo, a_hi, dtype=np.int32)[:, None]
+    K = int(-(-(2 * (a_hi - 1) + 3) // 16) * 16)
+    i = np.arange(K, dtype=np.int32)[None, :]
+    x = np.where(i == 0, a, 0)
+    x = np.where((i >= 1) & (i <= a + 1), i - 1, x)
+    x = np.where((i >= a + 2) & (i <= 2 * a + 2), 0x8000 | (i - a - 2), x)
+    return x.astype(np.uint16)
+
+
+# chunk boundaries over the 32639 positive finite bf16 amax patterns, spaced
+# so each chunk holds about the same number of (amax, x) pairs
+_AMAX_EDGES = [1] + [int(0x7F80 * np.sqrt(k / 8.0)) for k in range(1, 8)] + [0x7F80]
+
+
+@pytest.mark.parametrize("chunk", range(8))
+def test_quantize_rowwise_every_amax_times_every_x(spg, chunk):
+    # exhaustive over the division-free encoder: every positive finite bf16
+    # amax (so every scale the row-wise quantizer can form, subnormal ones
+    # and the 2^100-scaled path for amax < 2^-40 included) against every bf16
+    # value x with |x| <= amax, both signs; codes and scales bit for bit
+    a_lo, a_hi = _AMAX_EDGES[chunk], _AMAX_EDGES[chunk + 1]
+    print(f"amax patterns {a_lo:#06x} .. {a_hi - 1:#06x}", flush=True)
+    x = _every_amax_rows(a_lo, a_hi)
+    q, s = spg.quantize_rowwise(dev(x))
+    qo, so = oracle.quantize_rowwise(x)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    qg = q.cpu().numpy()
+    bad = np.argwhere(qg != qo)
+    assert len(bad) == 0, (f"{len(bad)} codes differ, first (row amax, x): "
+                           f"{[(int(x[r, 0]), int(x[r, c])) for r, c in bad[:5]]}")
+    del q, s
+    torch.cuda.empty_cache()
 
 
 def test_quantize_rowwise_zero_and_signed_zero_rows(spg):
@@ -243,6 +279,26 @@ def test_gemm_fp8_small_shapes(spg, shape, epi, fmt):
     ref = oracle_fp8(A16, W16, epi, fmt, R16)
     assert gpu.shape == ref["out"].shape
     check_close(gpu, ref["y"], ref["S"], f"{shape} {epi} {fmt}")
+
+
+def test_bound_rejects_planted_errors_on_a_gpu_output(spg):
+    # the acceptance check is not vacuous on real data: the 128 x 256 x 512
+    # store output of the GPU passes it, and the same output moved away from
+    # y by 2^-7 |y| + 2^-11 S (twice the bound) fails it wherever the bound
+    # is nonzero
+    wl = WORKLOADS["fp8_row_tiny"]
+    A16, W16, _ = wl.inputs()
+    gpu = run_fp8(spg, A16, W16, "store", "e4m3_row", None)
+    ref = oracle_fp8(A16, W16, "store", "e4m3_row", None)
+    check_close(gpu, ref["y"], ref["S"], "tiny store")
+    g = oracle.bf16_to_f64(gpu)
+    away = np.where(g >= ref["y"], 1.0, -1.0)
+    planted = g + away * (2.0 ** -7 * np.abs(ref["y"]) + 2.0 ** -11 * ref["S"])
+    bad = np.vectorize(oracle.bf16_from_f64, otypes=[np.uint16])(planted)
+    ok, _ = oracle.within_tolerance(bad, ref["y"], ref["S"])
+    assert not ok.any()
+    with pytest.raises(AssertionError):
+        check_close(bad, ref["y"], ref["S"], "planted")
 
 
 # extreme aspect ratios: many tiles along one dimension (more tiles than
@@ -432,6 +488,20 @@ def sample(n, count, rng, tile=256):
     return np.unique(np.clip(np.concatenate([edges, rest]), 0, n - 1))
 
 
+def sample_every_tile(n, rng, tile):
+    """Indices 0 .. n-1 with two in every tile of `tile` indices, one in each
+    half (so both 128-row halves of a half-height tile are hit), plus the
+    first and last index and the edges of the first tiles."""
+    picks = [0, n - 1] + [v for t in range(tile, n, tile) for v in (t - 1, t)][:8]
+    half = tile // 2
+    for t0 in range(0, n, tile):
+        lo_end = min(t0 + half, n)
+        picks.append(int(rng.integers(t0, lo_end)))
+        if lo_end < n:
+            picks.append(int(rng.integers(lo_end, min(t0 + tile, n))))
+    return np.unique(np.asarray(picks, np.int64))
+
+
 @pytest.mark.parametrize("name", ["fp8_row_add_t1024", "fp8_row_swiglu_t4096", "fp8_tensor_square_8192",
                                   "fp8_tensor_bmm64_512", "nvfp4_add_t4096", "fp8_row_bias_t4096"])
 def test_workload_full_size_sampled(spg, name):
@@ -457,13 +527,20 @@ def test_workload_full_size_sampled(spg, name):
     del A, W, R, qa, qw, out
     torch.cuda.empty_cache()
 
-    batches = [0, wl.batch // 2, wl.batch - 1] if wl.batch > 1 else [None]
+    batches = list(range(wl.batch)) if wl.batch > 1 else [None]
     for b in batches:
         Ab = A16[b] if b is not None else A16
         Wb = W16[b] if b is not None else W16
         g = gpu[b] if b is not None else gpu
-        rows = sample(wl.M, 40, rng)
-        cols = sample(wl.n_out, 40, rng, tile=128 if wl.epilogue == "swiglu" else 256)
+        # every 256-row tile row and every tile column (SwiGLU: 128 outputs)
+        # twice, one index in each half: with the persistent walk, the K-split
+        # tail and both halves of half-height tail tiles, every tile is hit
+        rows = sample_every_tile(wl.M, rng, 256)
+        cols = sample_every_tile(wl.n_out, rng, 128 if wl.epilogue == "swiglu" else 256)
+        tiles_m = -(-wl.M // 256)
+        tiles_n = -(-wl.n_out // (128 if wl.epilogue == "swiglu" else 256))
+        assert len(np.unique(rows // 256)) == tiles_m
+        assert len(np.unique(cols // (128 if wl.epilogue == "swiglu" else 256))) == tiles_n
         wrows = np.concatenate([cols, cols + wl.N // 2]) if wl.epilogue == "swiglu" else cols
         Rb = np.broadcast_to(R16, (wl.M, wl.n_out)) if wl.bias else R16
         Rs = np.ascontiguousarray(Rb[np.ix_(rows, cols)]) if R16 is not None else None

@@ -40,3 +40,16 @@ def test_probe_read_covers_the_buffer(spg, nbytes, wgs):
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     assert got == want
+
+
+def test_probe_clock(spg):
+    clk = torch.zeros((3, 4), dtype=torch.int64, device="cuda")
+    for i in range(3):
+        spg.probe_clock(clk[i], spins=2000 * (i + 1))
+    torch.cuda.synchronize()
+    c = clk.cpu().numpy().astype(np.float64)
+    assert np.all(c[:, 1] > c[:, 0]) and np.all(c[:, 3] > c[:, 2])
+    ghz = (c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]) / 10.0
+    assert np.all((ghz > 0.3) & (ghz < 3.5))
+    # longer spins take more shader cycles
+    assert c[2, 1] - c[2, 0] > c[0, 1] - c[0, 0]

@@ -64,7 +64,7 @@ def test_status_strings(spg):
 # ---------------------------------------------------------------------------
 P = ctypes.c_void_p
 FAKE = P(0x100000)
-FAKE2 = P(0x200000)
+FAKE2 = P(0x40000000000)     # far from FAKE: no overlap with any output here
 MIS = P(0x100001)
 EINVAL, EUNSUP, EWS = 1, 2, 3
 
@@ -93,6 +93,8 @@ def test_desc_init_defaults(spg):
     "null_desc", "bad_format", "bad_epilogue", "k_not_16", "nvfp4_k_not_32", "lda_short", "lda_unaligned",
     "ldo_short", "swiglu_odd_n", "add_without_residual", "store_with_residual", "null_a", "misaligned_a",
     "negative_m", "zero_batch", "nvfp4_no_tscale", "negative_stride", "ldr_short", "bias_row_in_place",
+    "in_place_other_ldr", "in_place_other_batch_stride", "residual_overlaps_out", "bias_row_inside_out",
+    "output_batches_overlap", "output_broadcast",
 ])
 def test_gemm_validation_errors(spg, case):
     d = desc(spg, 64, 64, 64, 0)
@@ -138,7 +140,33 @@ def test_gemm_validation_errors(spg, case):
     elif case == "bias_row_in_place":
         # ldr == 0 (one bias row) with the output as that row
         epi, d.ldr, kw["res"] = 1, 0, FAKE
+    elif case == "in_place_other_ldr":
+        # residual == out but read with another row stride
+        epi, d.ldr, d.ldo, kw["res"] = 1, 64, 128, FAKE
+    elif case == "in_place_other_batch_stride":
+        d.batch, d.stride_a, d.stride_o, d.stride_r = 2, 64 * 64, 64 * 64, 64 * 128
+        epi, kw["res"] = 1, FAKE
+    elif case == "residual_overlaps_out":
+        # residual starts one row inside the output
+        epi, kw["res"] = 1, P(FAKE.value + 2 * 64)
+    elif case == "bias_row_inside_out":
+        epi, d.ldr, kw["res"] = 1, 0, P(FAKE.value + 2 * 64 * 10)
+    elif case == "output_batches_overlap":
+        d.batch, d.stride_a, d.stride_o = 2, 64 * 64, 64 * 63
+    elif case == "output_broadcast":
+        d.batch, d.stride_a, d.stride_o = 2, 64 * 64, 0
     assert call_gemm(spg, d, epi, **kw) == EINVAL
+
+
+def test_gemm_in_place_and_disjoint_residuals_pass_validation(spg):
+    # exactly aliased (same pointer, row and batch stride) and disjoint
+    # residuals get past validation: with no device the call then fails at
+    # the launch (SPG_EHIP) or, given a GPU, runs; never SPG_EINVAL
+    d = desc(spg, 64, 64, 64, 0)
+    assert call_gemm(spg, d, 1, res=FAKE) != EINVAL
+    assert call_gemm(spg, d, 1, res=P(FAKE.value + 2 * 64 * 64)) != EINVAL
+    d.batch, d.stride_a, d.stride_o, d.stride_r = 2, 64 * 64, 64 * 64, 64 * 64
+    assert call_gemm(spg, d, 1, res=FAKE) != EINVAL
 
 
 def test_gemm_bias_row_is_a_valid_residual(spg):
