@@ -146,6 +146,13 @@ int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t
  *              (AstrAI broadcasts batches of one through a zero stride)
  *   format   : SPG_FMT_*
  *   tscale_a, tscale_w : NVFP4 only, device fp32 [1] tensor scales
+ *   clock_probe : optional (NULL by default), device, 4 x uint64.  When
+ *              set, thread 0 of the first workgroup of the call's main GEMM
+ *              launch stores the shader-clock counter when the kernel
+ *              starts and ends (clock_probe[0], [1]) and the 100 MHz
+ *              reference counter at the same points ([2], [3]): the shader
+ *              clock the kernel ran at is (c1 - c0) / (c3 - c2) * 100 MHz.
+ *              A measurement aid only; results do not depend on it.
  */
 typedef struct spg_gemm_desc {
     int64_t M, N, K, batch;
@@ -155,6 +162,7 @@ typedef struct spg_gemm_desc {
     int32_t reserved;
     const float *tscale_a;
     const float *tscale_w;
+    uint64_t *clock_probe;
 } spg_gemm_desc;
 
 /* Zero every field, set batch = 1 and the dense strides for M, N, K. */
@@ -264,13 +272,6 @@ int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units, spg_plan 
  */
 int spg_probe_mfma(int kind, int64_t iters, int32_t workgroups, float *sink, uint64_t *clocks, void *stream);
 
-/* spg_probe_clock: one wave reads the shader-clock counter and the 100 MHz
- * reference counter around `spins` rounds of a dependent integer hash and
- * writes them to clocks (device, 4 x uint64, same order as spg_probe_mfma).
- * Enqueued right after a GEMM on its stream, it gives the shader clock the
- * power controller had set for that GEMM.  SPG_EINVAL for spins < 1, a null
- * or misaligned pointer. */
-int spg_probe_clock(int64_t spins, uint64_t *clocks, void *stream);
 int spg_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus

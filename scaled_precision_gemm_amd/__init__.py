@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "quantize_rowwise", "quantize_tensor", "quantize_block16", "gemm_scaled",
-    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read", "probe_clock",
+    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read",
     "lib", "LIB_PATH",
     "FMT_E4M3_ROW", "FMT_E4M3_TENSOR", "FMT_NVFP4", "EPI_STORE", "EPI_ADD", "EPI_SWIGLU",
     "SpgError", "check_operands",
@@ -44,6 +44,7 @@ class GemmDesc(ctypes.Structure):
         ("stride_o", ctypes.c_int64), ("stride_r", ctypes.c_int64),
         ("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("tscale_a", ctypes.c_void_p), ("tscale_w", ctypes.c_void_p),
+        ("clock_probe", ctypes.c_void_p),
     ]
 
 
@@ -78,7 +79,6 @@ SIGNATURES = {
     "spg_gemm_plan": (ctypes.c_int, [ctypes.POINTER(GemmDesc), ctypes.c_int, _I32, ctypes.POINTER(Plan)]),
     "spg_probe_mfma": (ctypes.c_int, [ctypes.c_int, _I64, _I32, _P, _P, _P]),
     "spg_probe_read": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
-    "spg_probe_clock": (ctypes.c_int, [_I64, _P, _P]),
 }
 
 
@@ -272,17 +272,25 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
 
 
 def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
-                out=None, tscale_a=None, tscale_w=None, workspace=None):
+                out=None, tscale_a=None, tscale_w=None, workspace=None, clock_probe=None):
     """out = epilogue(scale * A W^T) in bf16.
 
     e4m3_row: A uint8 [M,K], sa fp32 [M]; W uint8 [N,K], sw fp32 [N]
     e4m3_tensor: A [B,M,K] or [M,K], sa fp32 [B]; W likewise, sw fp32 [B]
     nvfp4: A uint8 [M,K/2], sa uint8 [M,K/16]; W [N,K/2], sw [N,K/16];
            tscale_a, tscale_w fp32 [1]
+    clock_probe: optional int64 tensor of 4 elements on the same device; the
+           main GEMM launch records its clock counters there (see
+           spg_gemm_desc.clock_probe): shader clock in GHz =
+           (c[1] - c[0]) / (c[3] - c[2]) / 10
     """
     check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w)
     _need(A.is_cuda, "operands must be CUDA tensors")
     d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w)
+    if clock_probe is not None:
+        _need(clock_probe.dtype == torch.int64 and clock_probe.numel() == 4 and clock_probe.is_contiguous()
+              and clock_probe.device == A.device, "clock_probe must be 4 contiguous int64 values on A's device")
+        d.clock_probe = clock_probe.data_ptr()
     n_out = d.N // 2 if epi == EPI_SWIGLU else d.N
     if out is None:
         shape = (d.batch, d.M, n_out) if batched else (d.M, n_out)
@@ -349,11 +357,3 @@ def probe_read(buf: torch.Tensor, workgroups: int):
     _check(lib.spg_probe_read(_ptr(buf), nbytes, workgroups, _ptr(sink), _stream(buf)), "spg_probe_read")
     return sink
 
-
-def probe_clock(clocks: torch.Tensor, spins: int = 2000):
-    """Enqueue the clock probe on the current stream, writing four counters
-    into `clocks` (int64 CUDA tensor of 4 elements, e.g. a row of a larger
-    one): shader clock in GHz = (c[1] - c[0]) / (c[3] - c[2]) / 10."""
-    _need(clocks.dtype == torch.int64 and clocks.numel() == 4 and clocks.is_contiguous(),
-          "probe_clock: clocks must be 4 contiguous int64 values")
-    _check(lib.spg_probe_clock(spins, _ptr(clocks), _stream(clocks)), "spg_probe_clock")

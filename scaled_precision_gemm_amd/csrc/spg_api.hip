@@ -291,6 +291,7 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     } else if (!aligned4(sa) || !aligned4(sw)) {
         return SPG_EINVAL;
     }
+    if (((uintptr_t)d->clock_probe & 7u) != 0) return SPG_EINVAL;
 
     spg_plan p;
     make_plan(d, epilogue, device_units(), &p);
@@ -340,7 +341,9 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     };
     spg_plan pm = p;
     pm.tiles = g.tile_count;
+    g.clocks = d->clock_probe;
     hipError_t e = launch(g, pm);
+    g.clocks = nullptr;                // the clock record covers the main launch only
     if (e == hipSuccess && p.tail_tiles > 0 && p.tail_bm < kTile) {
         // the tail: the last tail_tiles tiles as half-height tiles
         GemmArgs gt = g;
@@ -423,3 +426,4 @@ SPG_EXPORT int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t 
                                            amax_parts(rows * K), (hipStream_t)stream);
     return e == hipSuccess ? SPG_OK : SPG_EHIP;
 }
+

@@ -117,7 +117,22 @@ struct GemmArgs {
     int64_t tiles_m, tiles_n;         // output tiles per product
     int64_t tile_begin, tile_count;   // the tiles this launch computes (of batch*tiles_m*tiles_n)
     FastDiv div_per, div_span, div_gm_last;   // by tiles_m*tiles_n, 8*tiles_n, tiles_m % 8
+    uint64_t *clocks;                 // optional clock record (spg_gemm_desc.clock_probe), else null
 };
+
+// Optional clock record of the main GEMM launch: thread 0 of workgroup 0
+// stores the shader-clock counter and the 100 MHz reference counter when the
+// kernel starts (which = 0) and ends (which = 1), at clocks[which] and
+// clocks[2 + which].  Plain vector stores; nothing is kept live in between.
+__device__ __forceinline__ void clock_mark(uint64_t *clocks, int which)
+{
+    if (clocks != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+        const uint64_t t = __builtin_amdgcn_s_memtime();
+        const uint64_t r = __builtin_amdgcn_s_memrealtime();
+        __builtin_nontemporal_store(t, clocks + which);
+        __builtin_nontemporal_store(r, clocks + 2 + which);
+    }
+}
 
 inline FastDiv make_fastdiv(uint32_t d)
 {

@@ -224,6 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlotF];
     __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
     __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+    clock_mark(g.clocks, 0);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -384,9 +385,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
 
     if (SPLIT) {
         splitk_store(g, T, wi.split, acc);       // the slices are summed by splitk_reduce_kernel
+        clock_mark(g.clocks, 1);
         return;
     }
     epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // slots free after the barrier
+    clock_mark(g.clocks, 1);
 }
 
 template <int EPI>

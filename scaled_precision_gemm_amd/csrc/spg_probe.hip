@@ -14,10 +14,6 @@
 //  * HBM read: a grid-stride stream of 16-byte loads over a buffer larger
 //    than the last-level cache, folded with XOR into one word per thread (the
 //    folded words are checkable against the buffer).
-//  * Clock: one wave reads both counters around a short dependent VALU spin,
-//    enqueued right after a GEMM so that it sees the clock the power
-//    controller set for that GEMM (it reacts over milliseconds, the spin
-//    takes a few microseconds).
 #include "spg_common.h"
 
 namespace spg {
@@ -120,34 +116,11 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const v4i *__
     sink[tid] = x;
 }
 
-__global__ __launch_bounds__(64) void probe_clock_kernel(int64_t spins, uint64_t *clocks)
-{
-    const uint64_t t0 = __builtin_amdgcn_s_memtime();
-    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-    uint32_t x = threadIdx.x;
-    for (int64_t i = 0; i < spins; ++i) x = mix32(x);
-    const uint64_t t1 = __builtin_amdgcn_s_memtime();
-    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
-    if (threadIdx.x == 0) {
-        clocks[0] = t0;
-        clocks[1] = t1;
-        clocks[2] = r0;
-        clocks[3] = r1 + (x == 0x12345678u ? 1u : 0u);   // keeps the spin live
-    }
-}
-
 }  // namespace
 
 }  // namespace spg
 
 using namespace spg;
-
-SPG_EXPORT int spg_probe_clock(int64_t spins, uint64_t *clocks, void *stream)
-{
-    if (spins < 1 || !clocks || ((uintptr_t)clocks & 7)) return SPG_EINVAL;
-    probe_clock_kernel<<<dim3(1), 64, 0, (hipStream_t)stream>>>(spins, clocks);
-    return hipGetLastError() == hipSuccess ? SPG_OK : SPG_EHIP;
-}
 
 SPG_EXPORT int spg_probe_mfma(int kind, int64_t iters, int32_t workgroups, float *sink, uint64_t *clocks,
                               void *stream)
