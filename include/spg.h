@@ -122,6 +122,21 @@ size_t quantize_block16_workspace_bytes(int64_t rows, int64_t K);
 int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale,
                      float *tscale, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * quantize_block16_noalloc - quantize_block16 for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as quantize_block16
+ * without the workspace: its scratch (the partial maxima of the tensor amax,
+ * at most 1024 x 4 bytes) is a static device array of 4 KiB that each GPU
+ * the library runs on holds until the process ends.  It calls no allocating
+ * routine.  Calls on one GPU share that array: calls that overlap in time on
+ * one GPU race (serialize them, e.g. on one stream).  SPG_EWORKSPACE if a
+ * size ever needed more partial maxima than the array holds (no size does
+ * today), SPG_EHIP if the array's device address cannot be obtained.
+ */
+int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale,
+                             float *tscale, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* GEMM                                                                      */
 /* ------------------------------------------------------------------------ */

@@ -71,6 +71,7 @@ SIGNATURES = {
     "quantize_tensor": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "quantize_block16_workspace_bytes": (_SZ, [_I64, _I64]),
     "quantize_block16": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "quantize_block16_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "spg_gemm_desc_init": (None, [ctypes.POINTER(GemmDesc), _I64, _I64, _I64, _I32]),
     "gemm_scaled_workspace_bytes": (_SZ, [ctypes.POINTER(GemmDesc), ctypes.c_int]),
     "gemm_scaled": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(GemmDesc), _P, _SZ, _P]),

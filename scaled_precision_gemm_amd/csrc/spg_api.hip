@@ -1,5 +1,8 @@
 // Exported C ABI (include/spg.h): argument validation, the tile / split-K
-// selector and kernel launches.  No allocation, no global mutable state.
+// selector and kernel launches.  No allocation.  The only global state is
+// the per-device address cache of the static scratch array used by
+// quantize_block16_noalloc (written once per device, read-only after).
+#include <atomic>
 #include <math.h>
 #include <string.h>
 
@@ -427,3 +430,62 @@ SPG_EXPORT int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t 
     return e == hipSuccess ? SPG_OK : SPG_EHIP;
 }
 
+// ---------------------------------------------------------------------------
+// quantize_block16_noalloc: quantize_block16 with its scratch in a static
+// device array, for callers that cannot allocate (code under graph capture,
+// tight serving loops).  The scratch holds the partial maxima of the tensor
+// amax pass: amax_parts() is at most 1024 per tensor, so 4 KiB serve every
+// size.  Each device holds its own copy of the array at its own address,
+// looked up once per device with hipGetSymbolAddress; the array's name is
+// never used as an address on the host.  Calls on one device share it, so
+// calls that overlap in time on one device race.  Every call writes each
+// partial it later reads, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int64_t kScratchWords = 1024;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+namespace {
+
+std::atomic<uintptr_t> g_scratch_ptr[kMaxDevices];
+
+// Address of this device's copy of `scratch` (the current device), or 0 on
+// failure.  Concurrent first calls compute the same address: the race is
+// benign.
+uint32_t *scratch_for_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    uintptr_t p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        p = (uintptr_t)ptr;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return (uint32_t *)p;
+}
+
+}  // namespace
+
+SPG_EXPORT int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale,
+                                        float *tscale, void *stream)
+{
+    if (rows < 0 || K < 0 || (K % 32)) return SPG_EINVAL;
+    if (rows == 0 || K == 0) return SPG_EINVAL;
+    if (!x || !q || !bscale || !tscale) return SPG_EINVAL;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(tscale)) return SPG_EINVAL;
+    const int64_t parts = amax_parts(rows * K);
+    if (parts > kScratchWords) return SPG_EWORKSPACE;   // beyond the static scratch (not reached today)
+    uint32_t *ws = scratch_for_current_device();
+    if (!ws) return SPG_EHIP;
+    hipError_t e = launch_quantize_block16((const uint16_t *)x, rows, K, q, bscale, tscale, ws, parts,
+                                           (hipStream_t)stream);
+    return e == hipSuccess ? SPG_OK : SPG_EHIP;
+}
