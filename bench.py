@@ -85,14 +85,15 @@ def gemm_bytes(wl) -> int:
 
 def quantize_bytes(wl) -> int:
     """Algorithmic bytes of the step's activation quantization: bf16 in, codes
-    and scales out (per-tensor and NVFP4 read the activations twice: a
-    partial-maximum pass, then the encode pass)."""
+    and scales out (read once: per-tensor FP8 reads the activations twice, a
+    partial-maximum pass and then the encode pass, but the minimum is one
+    read, and NVFP4 runs as a single launch at this size)."""
     elems = wl.batch * wl.M * wl.K
     if wl.fmt == "e4m3_row":
         return 3 * elems + 4 * wl.batch * wl.M
     if wl.fmt == "e4m3_tensor":
-        return 5 * elems + 4 * wl.batch
-    return 4 * elems + elems // 2 + elems // 16 + 4
+        return 3 * elems + 4 * wl.batch
+    return 2 * elems + elems // 2 + elems // 16 + 4
 
 
 def operator_bytes(M, N, K, n_out, residual: bool, fmt: str) -> int:
@@ -435,7 +436,7 @@ def main():
         elif wl.fmt == "e4m3_tensor":
             wq = spg.quantize_tensor(W)
         else:
-            wq = spg.quantize_block16(W)
+            wq = spg.quantize_block16(W, layout="blocked")
         acts.append(A)
         weights.append(wq)
         del W
@@ -464,10 +465,10 @@ def main():
             spg.gemm_scaled(q, s, w[0], w[1], wl.epilogue, fmt="e4m3_tensor", out=out, workspace=ws,
                             clock_probe=cp)
         else:
-            q, bs, t = spg.quantize_block16(A)
+            q, bs, t = spg.quantize_block16(A, layout="blocked")
             ev[i][1].record()
             spg.gemm_scaled(q, bs, w[0], w[1], wl.epilogue, residual=R, fmt="nvfp4", out=out,
-                            tscale_a=t, tscale_w=w[2], workspace=ws, clock_probe=cp)
+                            tscale_a=t, tscale_w=w[2], workspace=ws, clock_probe=cp, scale_layout="blocked")
 
     # workspace sized once by the library's own query, reused every step
     plan = spg.gemm_plan(wl.M, wl.N, wl.K, wl.fmt, wl.epilogue, batch=wl.batch)

@@ -69,6 +69,16 @@ enum {
     SPG_EPI_SWIGLU = 2   /* out[:, j] = bf16(silu(v[:, j]) * v[:, j + N/2])  */
 };
 
+/* ---- NVFP4 block-scale plane layouts ---------------------------------- */
+enum {
+    SPG_SCALES_ROW_MAJOR = 0, /* [rows, K/16], row-major                       */
+    SPG_SCALES_BLOCKED = 1,   /* GEMM-native: 4 KiB blocks of 256 rows x 16    */
+                              /* scale bytes (one 256-element K stage), blocks */
+                              /* ordered by row tile then stage; the last row  */
+                              /* tile padded to 256 rows with zero bytes       */
+    SPG_QUANT_SINGLE_LAUNCH = 0x100  /* flag for quantize_block16: one launch */
+};
+
 const char *spg_status_string(int status);
 
 /* ------------------------------------------------------------------------ */
@@ -113,21 +123,46 @@ int quantize_tensor(const void *x, int64_t batch, int64_t rows, int64_t K, int64
  *           gives signed zeros
  *   x      : bf16 [rows, K], row stride K
  *   q      : uint8 [rows, K/2]; element k in the low nibble when k is even
- *   bscale : uint8 E4M3 codes [rows, K/16], row-major
+ *   bscale : uint8 E4M3 codes.  scale_layout SPG_SCALES_ROW_MAJOR: [rows,
+ *            K/16] row-major.  SPG_SCALES_BLOCKED (K % 256 == 0): the plane
+ *            PR #160's quantizer writes for its GEMM - the scale of (row r,
+ *            group g) at ((r / 256) * (K / 256) + g / 16) * 4096 + (r % 256)
+ *            * 16 + g % 16, ceil(rows / 256) * 256 * K / 16 bytes in all,
+ *            padding rows zero; the NVFP4 GEMM copies each 4 KiB block with
+ *            whole-line loads
  *   tscale : fp32 [1], device
  *   ws     : device workspace of at least quantize_block16_workspace_bytes()
+ *            (any contents; the call clears what it uses)
  *   K % 32 == 0.
+ * Default: a partial-maximum pass, then an encode pass that reads the
+ * tensor again.  scale_layout | SPG_QUANT_SINGLE_LAUNCH requests the single
+ * launch (ninfer PR #160's single-launch quantizer, with the tensor amax
+ * published by last-block election as AstrAI's commit log publishes its
+ * scales): when the tensor fits in the registers of one resident grid,
+ * a cooperative launch (after a tiny clearing launch) reads it once, the
+ * last block to arrive forms the tensor scale and the others wait for it;
+ * otherwise the two passes run.  Results are identical.  Measured on MI355X
+ * at 4096 x 6144: two passes 39 us, single launch 70 us (the cooperative
+ * launch alone costs ~19 us, and the second read of a cache-resident tensor
+ * is cheap), so the single launch pays only where reading the activations
+ * twice costs more, e.g. when they do not stay in the last-level cache.
  */
 size_t quantize_block16_workspace_bytes(int64_t rows, int64_t K);
+/* The path quantize_block16 with SPG_QUANT_SINGLE_LAUNCH takes for [rows, K]
+ * on the current device: 1 = single launch, 2 = two passes (the tensor does
+ * not fit one resident grid); -1 for an invalid shape.  Host query. */
+int quantize_block16_path(int64_t rows, int64_t K);
 int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale,
-                     float *tscale, void *ws, size_t ws_bytes, void *stream);
+                     float *tscale, int scale_layout, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * quantize_block16_noalloc - quantize_block16 for callers that cannot
  * allocate: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same arguments and results as quantize_block16
  * without the workspace: its scratch (the partial maxima of the tensor amax,
- * at most 1024 x 4 bytes) is a static device array of 4 KiB that each GPU
+ * at most 1024 x 4 bytes, and the single-launch path's counters, flag and
+ * block maxima, cleared by the call) is a static device array of 10.4 KiB
+ * that each GPU
  * the library runs on holds until the process ends.  It calls no allocating
  * routine.  Calls on one GPU share that array: calls that overlap in time on
  * one GPU race (serialize them, e.g. on one stream).  SPG_EWORKSPACE if a
@@ -135,7 +170,7 @@ int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t
  * today), SPG_EHIP if the array's device address cannot be obtained.
  */
 int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale,
-                             float *tscale, void *stream);
+                             float *tscale, int scale_layout, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* GEMM                                                                      */
@@ -160,6 +195,8 @@ int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q,
  *              residual); 0 broadcasts one matrix to every batch entry
  *              (AstrAI broadcasts batches of one through a zero stride)
  *   format   : SPG_FMT_*
+ *   scale_layout : NVFP4 only, the layout of both block-scale planes
+ *              (SPG_SCALES_ROW_MAJOR, or SPG_SCALES_BLOCKED with K % 256 == 0)
  *   tscale_a, tscale_w : NVFP4 only, device fp32 [1] tensor scales
  *   clock_probe : optional (NULL by default), device, 4 x uint64.  When
  *              set, thread 0 of the first workgroup of the call's main GEMM
@@ -174,7 +211,7 @@ typedef struct spg_gemm_desc {
     int64_t lda, ldw, ldo, ldr;
     int64_t stride_a, stride_w, stride_o, stride_r;
     int32_t format;
-    int32_t reserved;
+    int32_t scale_layout;
     const float *tscale_a;
     const float *tscale_w;
     uint64_t *clock_probe;
@@ -190,8 +227,8 @@ void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32
  *   sa, sw   : E4M3_ROW: fp32 [M] and fp32 [N] (per batch entry: + b*M, b*N
  *              unless that operand's batch stride is 0);
  *              E4M3_TENSOR: fp32 [batch] each (index 0 when broadcast);
- *              NVFP4: E4M3 block-scale planes [M, K/16] and [N, K/16],
- *              row-major (NVFP4 requires batch == 1)
+ *              NVFP4: E4M3 block-scale planes [M, K/16] and [N, K/16] in
+ *              d->scale_layout (NVFP4 requires batch == 1)
  *   residual : bf16 [M, N] (or one row [N] when ldr == 0), required for
  *              SPG_EPI_ADD, NULL otherwise; it may be the output itself
  *              (residual == out, ldr == ldo, stride_r == stride_o); any

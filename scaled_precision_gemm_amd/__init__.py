@@ -19,13 +19,16 @@ __all__ = [
     "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read",
     "lib", "LIB_PATH",
     "FMT_E4M3_ROW", "FMT_E4M3_TENSOR", "FMT_NVFP4", "EPI_STORE", "EPI_ADD", "EPI_SWIGLU",
-    "SpgError", "check_operands",
+    "SpgError", "check_operands", "block16_scale_shape", "SCALES_ROW_MAJOR", "SCALES_BLOCKED", "QUANT_SINGLE_LAUNCH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspg.so")
 
 FMT_E4M3_ROW, FMT_E4M3_TENSOR, FMT_NVFP4 = 0, 1, 2
 EPI_STORE, EPI_ADD, EPI_SWIGLU = 0, 1, 2
+SCALES_ROW_MAJOR, SCALES_BLOCKED = 0, 1
+QUANT_SINGLE_LAUNCH = 0x100
+_LAYOUT = {"row": SCALES_ROW_MAJOR, "blocked": SCALES_BLOCKED}
 _EPI = {"store": EPI_STORE, "add": EPI_ADD, "swiglu": EPI_SWIGLU}
 _FMT = {"e4m3_row": FMT_E4M3_ROW, "e4m3_tensor": FMT_E4M3_TENSOR, "nvfp4": FMT_NVFP4}
 
@@ -42,7 +45,7 @@ class GemmDesc(ctypes.Structure):
         ("lda", ctypes.c_int64), ("ldw", ctypes.c_int64), ("ldo", ctypes.c_int64), ("ldr", ctypes.c_int64),
         ("stride_a", ctypes.c_int64), ("stride_w", ctypes.c_int64),
         ("stride_o", ctypes.c_int64), ("stride_r", ctypes.c_int64),
-        ("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("format", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
         ("tscale_a", ctypes.c_void_p), ("tscale_w", ctypes.c_void_p),
         ("clock_probe", ctypes.c_void_p),
     ]
@@ -70,8 +73,9 @@ SIGNATURES = {
     "quantize_tensor_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "quantize_tensor": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "quantize_block16_workspace_bytes": (_SZ, [_I64, _I64]),
-    "quantize_block16": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
-    "quantize_block16_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "quantize_block16_path": (ctypes.c_int, [_I64, _I64]),
+    "quantize_block16": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, ctypes.c_int, _P, _SZ, _P]),
+    "quantize_block16_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, ctypes.c_int, _P]),
     "spg_gemm_desc_init": (None, [ctypes.POINTER(GemmDesc), _I64, _I64, _I64, _I32]),
     "gemm_scaled_workspace_bytes": (_SZ, [ctypes.POINTER(GemmDesc), ctypes.c_int]),
     "gemm_scaled": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(GemmDesc), _P, _SZ, _P]),
@@ -146,18 +150,30 @@ def quantize_tensor(x: torch.Tensor):
     return q, s
 
 
-def quantize_block16(x: torch.Tensor):
+def block16_scale_shape(R: int, K: int, layout="row") -> tuple:
+    """Shape of the NVFP4 block-scale plane: [R, K/16] row-major, or the
+    blocked plane of ceil(R/256) row tiles x K/256 stages x 4096 bytes."""
+    if _LAYOUT.get(layout, layout) == SCALES_BLOCKED:
+        return ((R + 255) // 256, K // 256, 4096)
+    return (R, K // 16)
+
+
+def quantize_block16(x: torch.Tensor, layout="row", single_launch=False):
     """NVFP4: x bf16 [R, K] -> (codes uint8 [R, K/2], block scales uint8
-    [R, K/16] (E4M3), tensor scale fp32 [1])."""
+    (E4M3; [R, K/16] row-major, or the blocked plane of block16_scale_shape),
+    tensor scale fp32 [1]).  single_launch requests the one-launch quantizer
+    (same results)."""
     _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_cuda and x.is_contiguous(),
           "x must be a contiguous 2-D bf16 CUDA tensor")
+    lay = _LAYOUT.get(layout, layout)
     R, K = x.shape
     q = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
-    bs = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
+    bs = torch.empty(block16_scale_shape(R, K, lay), dtype=torch.uint8, device=x.device)
     t = torch.empty((1,), dtype=torch.float32, device=x.device)
     nws = lib.quantize_block16_workspace_bytes(R, K)
     ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device=x.device)
-    _check(lib.quantize_block16(_ptr(x), R, K, _ptr(q), _ptr(bs), _ptr(t), _ptr(ws), ws.numel(), _stream(x)),
+    flags = lay | (QUANT_SINGLE_LAUNCH if single_launch else 0)
+    _check(lib.quantize_block16(_ptr(x), R, K, _ptr(q), _ptr(bs), _ptr(t), flags, _ptr(ws), ws.numel(), _stream(x)),
            "quantize_block16")
     return q, bs, t
 
@@ -214,7 +230,8 @@ def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residua
     return d, epi, batched
 
 
-def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_a=None, tscale_w=None):
+def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_a=None, tscale_w=None,
+                   scale_layout="row"):
     """Shapes, dtypes, strides and devices of a gemm_scaled call, checked
     before anything reaches the library (raises ValueError).  The library
     trusts the sizes it is given, so an output, residual or scale tensor
@@ -252,8 +269,12 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
     else:
         _need(not batched, "NVFP4 takes one product (2-D operands)")
         _need(sa.dtype == torch.uint8 and sw.dtype == torch.uint8, "NVFP4 block scales are uint8 E4M3 codes")
-        _need(tuple(sa.shape) == (M, 2 * Kc // 16) and sa.is_contiguous(), "sa must be a contiguous [M, K/16] plane")
-        _need(tuple(sw.shape) == (N, 2 * Kc // 16) and sw.is_contiguous(), "sw must be a contiguous [N, K/16] plane")
+        lay = _LAYOUT.get(scale_layout, scale_layout)
+        _need(lay in (SCALES_ROW_MAJOR, SCALES_BLOCKED), f"unknown scale layout {scale_layout}")
+        _need(lay == SCALES_ROW_MAJOR or (2 * Kc) % 256 == 0, "blocked scale planes need K % 256 == 0")
+        sa_shape, sw_shape = block16_scale_shape(M, 2 * Kc, lay), block16_scale_shape(N, 2 * Kc, lay)
+        _need(tuple(sa.shape) == sa_shape and sa.is_contiguous(), f"sa must be a contiguous {sa_shape} plane")
+        _need(tuple(sw.shape) == sw_shape and sw.is_contiguous(), f"sw must be a contiguous {sw_shape} plane")
         for name, t in (("tscale_a", tscale_a), ("tscale_w", tscale_w)):
             _need(t is not None and t.dtype == torch.float32 and t.numel() == 1, f"{name} must be one fp32 value")
     if out is not None:
@@ -273,21 +294,23 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
 
 
 def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
-                out=None, tscale_a=None, tscale_w=None, workspace=None, clock_probe=None):
+                out=None, tscale_a=None, tscale_w=None, workspace=None, clock_probe=None, scale_layout="row"):
     """out = epilogue(scale * A W^T) in bf16.
 
     e4m3_row: A uint8 [M,K], sa fp32 [M]; W uint8 [N,K], sw fp32 [N]
     e4m3_tensor: A [B,M,K] or [M,K], sa fp32 [B]; W likewise, sw fp32 [B]
     nvfp4: A uint8 [M,K/2], sa uint8 [M,K/16]; W [N,K/2], sw [N,K/16];
-           tscale_a, tscale_w fp32 [1]
+           tscale_a, tscale_w fp32 [1]; scale_layout "row" or "blocked" (both
+           planes, as quantize_block16 wrote them)
     clock_probe: optional int64 tensor of 4 elements on the same device; the
            main GEMM launch records its clock counters there (see
            spg_gemm_desc.clock_probe): shader clock in GHz =
            (c[1] - c[0]) / (c[3] - c[2]) / 10
     """
-    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w)
+    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout)
     _need(A.is_cuda, "operands must be CUDA tensors")
     d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w)
+    d.scale_layout = _LAYOUT.get(scale_layout, scale_layout)
     if clock_probe is not None:
         _need(clock_probe.dtype == torch.int64 and clock_probe.numel() == 4 and clock_probe.is_contiguous()
               and clock_probe.device == A.device, "clock_probe must be 4 contiguous int64 values on A's device")

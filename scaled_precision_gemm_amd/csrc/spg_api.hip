@@ -46,9 +46,12 @@ int validate_desc(const spg_gemm_desc *d, int epi)
         if (d->K % 32) return SPG_EINVAL;
         if (d->lda < d->K / 2 || d->ldw < d->K / 2) return SPG_EINVAL;
         if (d->batch != 1) return SPG_EUNSUPPORTED;
+        if (d->scale_layout != SPG_SCALES_ROW_MAJOR && d->scale_layout != SPG_SCALES_BLOCKED) return SPG_EINVAL;
+        if (d->scale_layout == SPG_SCALES_BLOCKED && (d->K % 256)) return SPG_EINVAL;
     } else {
         if (d->K % 16) return SPG_EINVAL;
         if (d->lda < d->K || d->ldw < d->K) return SPG_EINVAL;
+        if (d->scale_layout != SPG_SCALES_ROW_MAJOR) return SPG_EINVAL;   // NVFP4 only
     }
     if ((d->lda & 15) || (d->ldw & 15)) return SPG_EINVAL;
     // a 256-row tile of codes must fit the 31-bit range of a buffer resource
@@ -327,6 +330,7 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.epilogue = epilogue;
     g.tscale_a = d->tscale_a;
     g.tscale_w = d->tscale_w;
+    g.scale_layout = d->format == SPG_FMT_NVFP4 ? d->scale_layout : SPG_SCALES_ROW_MAJOR;
     g.split_k = p.split_k;
     const int64_t unit_k = p.bk;
     g.k_chunk = p.split_k > 1 ? cdiv(cdiv(d->K, p.split_k), unit_k) * unit_k : (d->K > 0 ? d->K : 1);
@@ -413,19 +417,48 @@ SPG_EXPORT int quantize_tensor(const void *x, int64_t batch, int64_t rows, int64
 SPG_EXPORT size_t quantize_block16_workspace_bytes(int64_t rows, int64_t K)
 {
     if (rows < 0 || K < 0) return 0;
-    return (size_t)amax_parts(rows * K) * sizeof(uint32_t);
+    // the single-launch path's sync area, then the two-pass path's partial
+    // maxima
+    return (size_t)(kBlock16SyncWords + amax_parts(rows * K)) * sizeof(uint32_t);
 }
 
-SPG_EXPORT int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale, float *tscale,
-                                void *ws, size_t ws_bytes, void *stream)
+namespace {
+
+// Checks shared by quantize_block16 and quantize_block16_noalloc.
+int validate_block16(const void *x, int64_t rows, int64_t K, const uint8_t *q, const uint8_t *bscale,
+                     const float *tscale, int layout)
 {
     if (rows < 0 || K < 0 || (K % 32)) return SPG_EINVAL;
     if (rows == 0 || K == 0) return SPG_EINVAL;
+    if ((layout & ~SPG_QUANT_SINGLE_LAUNCH) != 0 && (layout & ~SPG_QUANT_SINGLE_LAUNCH) != SPG_SCALES_BLOCKED)
+        return SPG_EINVAL;
+    layout &= ~SPG_QUANT_SINGLE_LAUNCH;
+    if (layout == SPG_SCALES_BLOCKED && (K % 256)) return SPG_EINVAL;
     if (!x || !q || !bscale || !tscale) return SPG_EINVAL;
     if (!aligned16(x) || !aligned16(q) || !aligned4(tscale)) return SPG_EINVAL;
+    // group indices (padded rows x K/16) are 32-bit in the kernels
+    if (((rows + 255) / 256 * 256) * (K / 16) >= (INT64_C(1) << 31)) return SPG_EUNSUPPORTED;
+    return SPG_OK;
+}
+
+}  // namespace
+
+SPG_EXPORT int quantize_block16_path(int64_t rows, int64_t K)
+{
+    if (rows <= 0 || K <= 0 || (K % 32)) return -1;
+    return quantize_block16_single_launch(rows, K) ? 1 : 2;
+}
+
+SPG_EXPORT int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale, float *tscale,
+                                int scale_layout, void *ws, size_t ws_bytes, void *stream)
+{
+    const int v = validate_block16(x, rows, K, q, bscale, tscale, scale_layout);
+    if (v != SPG_OK) return v;
     const size_t need = quantize_block16_workspace_bytes(rows, K);
     if (!ws || ws_bytes < need || !aligned4(ws)) return SPG_EWORKSPACE;
-    hipError_t e = launch_quantize_block16((const uint16_t *)x, rows, K, q, bscale, tscale, (uint32_t *)ws,
+    hipError_t e = launch_quantize_block16((const uint16_t *)x, rows, K, q, bscale, tscale,
+                                           scale_layout & ~SPG_QUANT_SINGLE_LAUNCH,
+                                           (scale_layout & SPG_QUANT_SINGLE_LAUNCH) != 0, (uint32_t *)ws,
                                            amax_parts(rows * K), (hipStream_t)stream);
     return e == hipSuccess ? SPG_OK : SPG_EHIP;
 }
@@ -433,18 +466,20 @@ SPG_EXPORT int quantize_block16(const void *x, int64_t rows, int64_t K, uint8_t 
 // ---------------------------------------------------------------------------
 // quantize_block16_noalloc: quantize_block16 with its scratch in a static
 // device array, for callers that cannot allocate (code under graph capture,
-// tight serving loops).  The scratch holds the partial maxima of the tensor
-// amax pass: amax_parts() is at most 1024 per tensor, so 4 KiB serve every
-// size.  Each device holds its own copy of the array at its own address,
-// looked up once per device with hipGetSymbolAddress; the array's name is
-// never used as an address on the host.  Calls on one device share it, so
-// calls that overlap in time on one device race.  Every call writes each
-// partial it later reads, so nothing needs clearing between calls.
+// tight serving loops).  The scratch holds the single-launch path's sync
+// area (counters, flag and tensor scale, cleared by a small kernel at the
+// start of each call, and one maximum per block) and the two-pass path's
+// partial maxima: amax_parts() is at most 1024 per tensor, so 10.4 KiB serve
+// every size.  Each device holds its
+// own copy of the array at its own address, looked up once per device with
+// hipGetSymbolAddress; the array's name is never used as an address on the
+// host.  Calls on one device share it, so calls that overlap in time on one
+// device race.  Every call writes each partial it later reads.
 // ---------------------------------------------------------------------------
 
 namespace {
 
-constexpr int64_t kScratchWords = 1024;
+constexpr int64_t kScratchWords = kBlock16SyncWords + 1024;
 constexpr int kMaxDevices = 64;
 
 }  // namespace
@@ -475,17 +510,17 @@ uint32_t *scratch_for_current_device()
 }  // namespace
 
 SPG_EXPORT int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *bscale,
-                                        float *tscale, void *stream)
+                                        float *tscale, int scale_layout, void *stream)
 {
-    if (rows < 0 || K < 0 || (K % 32)) return SPG_EINVAL;
-    if (rows == 0 || K == 0) return SPG_EINVAL;
-    if (!x || !q || !bscale || !tscale) return SPG_EINVAL;
-    if (!aligned16(x) || !aligned16(q) || !aligned4(tscale)) return SPG_EINVAL;
+    const int v = validate_block16(x, rows, K, q, bscale, tscale, scale_layout);
+    if (v != SPG_OK) return v;
     const int64_t parts = amax_parts(rows * K);
-    if (parts > kScratchWords) return SPG_EWORKSPACE;   // beyond the static scratch (not reached today)
+    if (kBlock16SyncWords + parts > kScratchWords) return SPG_EWORKSPACE;   // beyond the static scratch (not reached today)
     uint32_t *ws = scratch_for_current_device();
     if (!ws) return SPG_EHIP;
-    hipError_t e = launch_quantize_block16((const uint16_t *)x, rows, K, q, bscale, tscale, ws, parts,
+    hipError_t e = launch_quantize_block16((const uint16_t *)x, rows, K, q, bscale, tscale,
+                                           scale_layout & ~SPG_QUANT_SINGLE_LAUNCH,
+                                           (scale_layout & SPG_QUANT_SINGLE_LAUNCH) != 0, ws, parts,
                                            (hipStream_t)stream);
     return e == hipSuccess ? SPG_OK : SPG_EHIP;
 }

@@ -98,6 +98,9 @@ struct FastDiv {
     uint32_t m, s;
 };
 
+// n / d for n < 2^31 with a FastDiv of d (multiply-high, add, shift).
+__device__ __forceinline__ uint32_t fdiv_q(uint32_t n, const FastDiv &f) { return (__umulhi(n, f.m) + n) >> f.s; }
+
 struct GemmArgs {
     void *out;
     const uint8_t *A;
@@ -118,6 +121,7 @@ struct GemmArgs {
     int64_t tile_begin, tile_count;   // the tiles this launch computes (of batch*tiles_m*tiles_n)
     FastDiv div_per, div_span, div_gm_last;   // by tiles_m*tiles_n, 8*tiles_n, tiles_m % 8
     uint64_t *clocks;                 // optional clock record (spg_gemm_desc.clock_probe), else null
+    int32_t scale_layout;             // NVFP4 block-scale planes: SPG_SCALES_ROW_MAJOR or _BLOCKED
 };
 
 // Optional clock record of the main GEMM launch: thread 0 of workgroup 0
@@ -151,8 +155,18 @@ hipError_t launch_quantize_tensor(const uint16_t *x, int64_t batch, int64_t rows
                                   int64_t bstride, uint8_t *q, float *scale, uint32_t *ws,
                                   int64_t parts, hipStream_t s);
 hipError_t launch_quantize_block16(const uint16_t *x, int64_t rows, int64_t K, uint8_t *q,
-                                   uint8_t *bscale, float *tscale, uint32_t *ws, int64_t parts,
-                                   hipStream_t s);
+                                   uint8_t *bscale, float *tscale, int layout, bool single_launch, uint32_t *ws,
+                                   int64_t parts, hipStream_t s);
+
+// Workspace of quantize_block16: the single-launch path's sync area (its
+// counters, flag and tensor scale on separate cache lines, then one maximum
+// per block) in the first kBlock16SyncWords words, then the two-pass path's
+// partial maxima.
+constexpr int64_t kMaxFusedBlocks = 1024;
+constexpr int64_t kBlock16SyncWords = 19 * 32 + kMaxFusedBlocks;
+
+// Whether quantize_block16 runs as one launch on the current device.
+bool quantize_block16_single_launch(int64_t rows, int64_t K);
 
 // Partial-maximum blocks used by the per-tensor amax pass.
 int64_t amax_parts(int64_t elems);

@@ -118,10 +118,7 @@ struct Tile {
 // Tiles of one product are rasterized in groups of kGroupM tile-rows,
 // column-major inside a group, so neighbouring tile ids share A panels
 // (same rows) and W panels (same columns) through the L2 of their XCD.
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f)
-{
-    return (__umulhi(n, f.m) + n) >> f.s;
-}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) { return fdiv_q(n, f); }
 
 // All in 32-bit scalar arithmetic (tile counts are below 2^31).
 template <int EPI>

@@ -257,14 +257,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     const uint8_t *SA = (const uint8_t *)g.sa, *SW = (const uint8_t *)g.sw;
     const v4i rs_a = make_rsrc(A + T.m0 * g.lda, (uint32_t)(a_rows * g.lda));
     const v4i rs_w = make_rsrc(W + w_first * g.ldw, (uint32_t)(w_rows * g.ldw));
-    const v4i rs_sa = make_rsrc(SA + T.m0 * G, (uint32_t)(a_rows * G));
-    const v4i rs_sw = make_rsrc(SW + w_first * G, (uint32_t)(w_rows * G));
+    // Scale planes.  Row-major: tile row r's 16 bytes of a stage at row
+    // stride K/16.  Blocked: the 16 bytes of physical row p for stage s at
+    // ((p / 256) * (K / 256) + s) * 4096 + (p % 256) * 16, so the 256 rows of
+    // a stage are 4 KiB of whole lines.  Rows past the matrix read zero (the
+    // range check) or the plane's zero padding; either way their codes are
+    // zero.
+    const bool blk = g.scale_layout == SPG_SCALES_BLOCKED;
+    const uint32_t sblk = (uint32_t)(g.K / 256) * 4096u;          // bytes of one row tile's blocks
+    const v4i rs_sa = blk ? make_rsrc(SA, (uint32_t)((g.M + 255) / 256) * sblk)
+                          : make_rsrc(SA + T.m0 * G, (uint32_t)(a_rows * G));
+    const v4i rs_sw = blk ? make_rsrc(SW, (uint32_t)((g.N + 255) / 256) * sblk)
+                          : make_rsrc(SW + w_first * G, (uint32_t)(w_rows * G));
     const uint32_t ra0 = (uint32_t)(wave * 64) + rib, rw0 = (uint32_t)((wave & 1) * 64) + rib;
     const uint32_t va_e = ra0 * (uint32_t)g.lda + c_even * 16u, va_o = ra0 * (uint32_t)g.lda + c_odd * 16u;
     const uint32_t vw_e = rw0 * (uint32_t)g.ldw + c_even * 16u, vw_o = rw0 * (uint32_t)g.ldw + c_odd * 16u;
     // scales: lane L of wave w copies the 16 bytes of tile row 64 w + L
-    const uint32_t vsa = (uint32_t)(wave * 64 + lane) * (uint32_t)G;
-    const uint32_t vsw = (uint32_t)((wave & 1) * 64 + lane) * (uint32_t)G;
+    const uint32_t pra = (uint32_t)T.m0 + (uint32_t)(wave * 64 + lane);                  // physical rows
+    const uint32_t prw = (uint32_t)w_first + (uint32_t)((wave & 1) * 64 + lane);
+    const uint32_t vsa = blk ? (pra >> 8) * sblk + (pra & 255u) * 16u : (uint32_t)(wave * 64 + lane) * (uint32_t)G;
+    const uint32_t vsw = blk ? (prw >> 8) * sblk + (prw & 255u) * 16u : (uint32_t)((wave & 1) * 64 + lane) * (uint32_t)G;
     const uint32_t lds_base =
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&lds[0];
 
@@ -272,7 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     auto issue_stage = [&](int kt) {
         const int slot = kt & 1;
         const uint32_t kc = (uint32_t)((k_begin + (int64_t)kt * kBKF) / 2);    // code byte offset
-        const uint32_t ks = (uint32_t)((k_begin + (int64_t)kt * kBKF) / 16);   // scale byte offset
+        const uint32_t ks = blk ? (uint32_t)((k_begin + (int64_t)kt * kBKF) / kBKF) * 4096u   // stage block
+                                : (uint32_t)((k_begin + (int64_t)kt * kBKF) / 16);             // scale byte offset
         const uint32_t sbase = lds_base + (uint32_t)(slot * kSlotF);
         const uint32_t soff_c = (uint32_t)__builtin_amdgcn_readfirstlane((int)kc);
         const uint32_t soff_s = (uint32_t)__builtin_amdgcn_readfirstlane((int)ks);

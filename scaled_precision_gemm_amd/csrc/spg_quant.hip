@@ -259,41 +259,195 @@ __global__ __launch_bounds__(kThreads) void quant_tensor_encode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 encode: one thread per 16-element group (two 16-byte loads, one
-// 8-byte code store, one scale byte).
+// NVFP4 encode of one 16-element group given the tensor scale t: the block
+// scale code b = E4M3(fl32(amax_g / fl32(6 t))), e = fl32(dec(b) t), and the
+// eight packed code bytes of E2M1(fl32(x / e)) (a zero e gives signed zeros).
+// Both NVFP4 quantize kernels use it, so their codes are identical.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void encode_group16(const uint4 &v0, const uint4 &v1, uint32_t gm, float t, float six_t,
+                                               uint2 &codes, uint32_t &b)
+{
+    b = 0;
+    if (t > 0.0f) b = encode_e4m3(__uint_as_float(gm << 16) / six_t);
+    const float e = decode_e4m3(b) * t;
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t c0, c1;
+        if (e > 0.0f) {
+            c0 = encode_e2m1(bf16_lo(w[i]) / e);
+            c1 = encode_e2m1(bf16_hi(w[i]) / e);
+        } else {
+            c0 = (w[i] >> 12) & 0x8u;
+            c1 = (w[i] >> 28) & 0x8u;
+        }
+        packed[i >> 2] |= (c0 | (c1 << 4)) << (8 * (i & 3));
+    }
+    codes = make_uint2(packed[0], packed[1]);
+}
+
+// Byte offset of block scale (row, group g) in the scale plane.  Row-major:
+// row * G + g.  Blocked (the layout the NVFP4 GEMM stages, ninfer PR #160's
+// quantizer writing the plane in the tile shape its GEMM reads): the scales of
+// 256 rows for one 256-element K stage (16 groups) form one contiguous 4 KiB
+// block, row-major inside it, blocks ordered by row tile, then stage; the
+// rows of a last, partial row tile are padded with zero bytes.
+__device__ __forceinline__ uint64_t scale_offset(uint32_t row, uint32_t g, uint32_t G, int layout)
+{
+    if (layout == SPG_SCALES_ROW_MAJOR) return (uint64_t)row * G + g;
+    return ((uint64_t)(row >> 8) * (G >> 4) + (g >> 4)) * 4096u + (row & 255u) * 16u + (g & 15u);
+}
+
+// Two-pass NVFP4, pass 2: fold the partial maxima into t, then one thread per
+// 16-element group (two 16-byte loads, one 8-byte code store, one scale
+// byte).  Work items past the tensor's groups (groups .. groups_pad) write
+// the zero scale bytes of the padding rows of a blocked plane.
 __global__ __launch_bounds__(kThreads) void quant_block16_encode_kernel(
-    const uint16_t *__restrict__ x, int64_t groups, const uint32_t *__restrict__ partial, int64_t parts,
-    uint8_t *__restrict__ q, uint8_t *__restrict__ bscale, float *__restrict__ tscale)
+    const uint16_t *__restrict__ x, int64_t groups, int64_t groups_pad, FastDiv div_g, uint32_t G, int layout,
+    const uint32_t *__restrict__ partial, int64_t parts, uint8_t *__restrict__ q, uint8_t *__restrict__ bscale,
+    float *__restrict__ tscale)
 {
     __shared__ uint32_t lds4[4];
     const uint32_t m = fold_partials(partial, parts, lds4);
     const float t = __uint_as_float(m << 16) / 2688.0f;
     const float six_t = 6.0f * t;
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = t;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups;
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups_pad;
          g += (int64_t)gridDim.x * kThreads) {
-        const uint4 v0 = ld16(x + g * 16), v1 = ld16(x + g * 16 + 8);
-        const uint32_t gm = max(amax8(v0), amax8(v1));
+        const uint32_t row = fdiv_q((uint32_t)g, div_g), col = (uint32_t)g - row * G;
         uint32_t b = 0;
-        if (t > 0.0f) b = encode_e4m3(__uint_as_float(gm << 16) / six_t);
-        const float e = decode_e4m3(b) * t;
-        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t c0, c1;
-            if (e > 0.0f) {
-                c0 = encode_e2m1(bf16_lo(w[i]) / e);
-                c1 = encode_e2m1(bf16_hi(w[i]) / e);
-            } else {
-                c0 = (w[i] >> 12) & 0x8u;
-                c1 = (w[i] >> 28) & 0x8u;
-            }
-            packed[i >> 2] |= (c0 | (c1 << 4)) << (8 * (i & 3));
+        if (g < groups) {
+            const uint4 v0 = ld16(x + g * 16), v1 = ld16(x + g * 16 + 8);
+            uint2 codes;
+            encode_group16(v0, v1, max(amax8(v0), amax8(v1)), t, six_t, codes, b);
+            *reinterpret_cast<uint2 *>(q + g * 8) = codes;
         }
-        *reinterpret_cast<uint2 *>(q + g * 8) = make_uint2(packed[0], packed[1]);
-        bscale[g] = (uint8_t)b;
+        bscale[scale_offset(row, col, G, layout)] = (uint8_t)b;
+    }
+}
+
+// Single-launch NVFP4 (every block resident: cooperative launch).  Each
+// thread loads GPT groups into registers and takes their maxima.  Each block
+// stores its maximum in its own slot and counts itself in; the block that
+// arrives last is elected, folds the slots into the tensor amax, forms t and
+// publishes it with a release flag; the others wait for the flag, then every
+// thread encodes its groups straight from registers, so the tensor is read
+// from memory once.  Device-scope atomics on one address serialize across
+// the XCDs (one counter for 768 blocks measured 135 us for the whole
+// quantize), so arrivals are counted in 16 sub-counters on separate cache
+// lines; the block completing a sub-counter counts into the top counter.
+// The sync area (zeroed by quant_sync_clear_kernel just before) holds the
+// 16 sub-counters, the top counter, the flag and t, one 128-byte line each;
+// the block maxima follow it.  A wait that runs past spin_limit polls (never
+// expected) gives up and publishes a NaN tensor scale instead of hanging.
+constexpr int kSubCounters = 16;
+constexpr int kLineWords = 32;                              // 128-byte lines
+constexpr int kSyncWords = (kSubCounters + 3) * kLineWords; // sub-counters, top, flag, t
+constexpr int kFusedThreads = 1024;
+
+__global__ __launch_bounds__(256) void quant_sync_clear_kernel(uint32_t *__restrict__ sync)
+{
+    for (int i = threadIdx.x; i < kSyncWords; i += 256) sync[i] = 0u;
+}
+
+template <int GPT>
+__global__ __launch_bounds__(kFusedThreads) void quant_block16_fused_kernel(
+    const uint16_t *__restrict__ x, int64_t groups, int64_t groups_pad, FastDiv div_g, uint32_t G, int layout,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ bscale, float *__restrict__ tscale, uint32_t *sync,
+    int64_t spin_limit)
+{
+    __shared__ uint32_t lds16[16];
+    __shared__ uint32_t t_bits;
+    uint32_t *const top = sync + kSubCounters * kLineWords;
+    uint32_t *const flag = top + kLineWords;
+    uint32_t *const tword = flag + kLineWords;
+    uint32_t *const slots = sync + kSyncWords;
+    const int64_t nthreads = (int64_t)gridDim.x * kFusedThreads;
+    const int64_t tid = (int64_t)blockIdx.x * kFusedThreads + threadIdx.x;
+    uint4 v[GPT][2];
+    uint32_t gm[GPT];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        const int64_t g = tid + (int64_t)i * nthreads;
+        if (g < groups) {
+            v[i][0] = ld16(x + g * 16);
+            v[i][1] = ld16(x + g * 16 + 8);
+        } else {
+            v[i][0] = v[i][1] = make_uint4(0, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        gm[i] = max(amax8(v[i][0]), amax8(v[i][1]));
+        m = max(m, gm[i]);
+    }
+    // block maximum: wave maxima through LDS
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) lds16[threadIdx.x >> 6] = m;
+    __syncthreads();
+    __shared__ uint32_t elected;
+    if (threadIdx.x == 0) {
+        uint32_t bm = 0;
+        for (int w = 0; w < kFusedThreads / 64; ++w) bm = max(bm, lds16[w]);
+        __hip_atomic_store(&slots[blockIdx.x], bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t nb = gridDim.x, j = blockIdx.x % kSubCounters;
+        const uint32_t in_j = (nb - j + kSubCounters - 1) / kSubCounters;     // blocks counted by sub-counter j
+        const uint32_t nsub = nb < (uint32_t)kSubCounters ? nb : (uint32_t)kSubCounters;
+        const uint32_t a = __hip_atomic_fetch_add(&sync[j * kLineWords], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        elected = a == in_j - 1u &&
+                  __hip_atomic_fetch_add(top, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == nsub - 1u;
+    }
+    __syncthreads();
+    if (elected) {
+        // every thread of the elected block folds at most one block maximum
+        // (gridDim.x <= 1024), then t is formed and published
+        uint32_t am = threadIdx.x < gridDim.x
+                          ? __hip_atomic_load(&slots[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : 0u;
+        am = wave_max_u32(am);
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0) lds16[threadIdx.x >> 6] = am;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 0; w < kFusedThreads / 64; ++w) am = max(am, lds16[w]);
+            const float t = __uint_as_float(am << 16) / 2688.0f;
+            __hip_atomic_store(tword, __float_as_uint(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (threadIdx.x == 0) {
+        // poll with relaxed loads (an acquire load per poll would also
+        // invalidate this XCD's caches each time), then acquire once
+        int64_t n = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u && n < spin_limit) {
+            __builtin_amdgcn_s_sleep(8);
+            ++n;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        t_bits = n < spin_limit ? __hip_atomic_load(tword, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0x7FC00000u;
+    }
+    __syncthreads();
+    const float t = __uint_as_float(t_bits);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = t;
+    if (t != t) return;                                      // gave up waiting: NaN published
+    const float six_t = 6.0f * t;
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        const int64_t g = tid + (int64_t)i * nthreads;
+        if (g < groups) {
+            uint2 codes;
+            uint32_t b;
+            encode_group16(v[i][0], v[i][1], gm[i], t, six_t, codes, b);
+            *reinterpret_cast<uint2 *>(q + g * 8) = codes;
+            const uint32_t row = fdiv_q((uint32_t)g, div_g);
+            bscale[scale_offset(row, (uint32_t)g - row * G, G, layout)] = (uint8_t)b;
+        }
+    }
+    for (int64_t g = groups + tid; g < groups_pad; g += nthreads) {   // padding rows of a blocked plane
+        const uint32_t row = fdiv_q((uint32_t)g, div_g);
+        bscale[scale_offset(row, (uint32_t)g - row * G, G, layout)] = 0;
     }
 }
 
@@ -354,17 +508,75 @@ hipError_t launch_quantize_tensor(const uint16_t *x, int64_t batch, int64_t rows
     return hipGetLastError();
 }
 
+namespace {
+
+// Single launch when the whole tensor fits in the registers of one resident
+// grid (GPT groups per thread); false (and nothing enqueued but the clear)
+// when it does not, or when the cooperative launch is refused.
+static_assert(kBlock16SyncWords >= kSyncWords + kMaxFusedBlocks, "sync area too small");
+
+// Blocks of the single-launch kernel for `groups` groups, or 0 when they
+// cannot all be resident at once on the current device.
+template <int GPT>
+int64_t fused_blocks(int64_t groups)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_block16_fused_kernel<GPT>, kFusedThreads, 0) !=
+            hipSuccess || per_cu <= 0)
+        return 0;
+    const int64_t need = (groups + (int64_t)kFusedThreads * GPT - 1) / ((int64_t)kFusedThreads * GPT);
+    return need <= (int64_t)cus * per_cu && need <= kMaxFusedBlocks ? need : 0;
+}
+
+template <int GPT>
+bool try_fused_block16(const uint16_t *x, int64_t groups, int64_t groups_pad, FastDiv div_g, uint32_t G, int layout,
+                       uint8_t *q, uint8_t *bscale, float *tscale, uint32_t *sync, hipStream_t s)
+{
+    const int64_t need = fused_blocks<GPT>(groups);
+    if (need == 0) return false;
+    quant_sync_clear_kernel<<<1, 256, 0, s>>>(sync);
+    if (hipGetLastError() != hipSuccess) return false;
+    int64_t spin_limit = INT64_C(1) << 22;
+    void *args[] = {(void *)&x, (void *)&groups, (void *)&groups_pad, (void *)&div_g, (void *)&G, (void *)&layout,
+                    (void *)&q, (void *)&bscale, (void *)&tscale, (void *)&sync, (void *)&spin_limit};
+    if (hipLaunchCooperativeKernel((const void *)quant_block16_fused_kernel<GPT>, dim3((unsigned)need),
+                                   dim3(kFusedThreads), args, 0, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+bool quantize_block16_single_launch(int64_t rows, int64_t K)
+{
+    const int64_t groups = rows * K / 16;
+    return fused_blocks<8>(groups) > 0;
+}
+
 hipError_t launch_quantize_block16(const uint16_t *x, int64_t rows, int64_t K, uint8_t *q,
-                                   uint8_t *bscale, float *tscale, uint32_t *ws, int64_t parts,
-                                   hipStream_t s)
+                                   uint8_t *bscale, float *tscale, int layout, bool single_launch, uint32_t *ws,
+                                   int64_t parts, hipStream_t s)
 {
     const int64_t elems = rows * K;
-    amax_partial_kernel<<<dim3((unsigned)parts, 1), kThreads, 0, s>>>(x, elems, elems, parts, ws);
+    const int64_t groups = elems / 16;
+    const uint32_t G = (uint32_t)(K / 16);
+    const int64_t rows_pad = layout == SPG_SCALES_BLOCKED ? (rows + 255) / 256 * 256 : rows;
+    const int64_t groups_pad = rows_pad * G;
+    const FastDiv div_g = make_fastdiv(G);
+    uint32_t *sync = ws, *partial = ws + kBlock16SyncWords;
+    if (single_launch && try_fused_block16<8>(x, groups, groups_pad, div_g, G, layout, q, bscale, tscale, sync, s))
+        return hipGetLastError();
+    // two passes: partial maxima, then fold and encode (reads the tensor again)
+    amax_partial_kernel<<<dim3((unsigned)parts, 1), kThreads, 0, s>>>(x, elems, elems, parts, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t groups = elems / 16;
-    const int64_t g = grid_for(groups, kThreads * 2, 4096);
-    quant_block16_encode_kernel<<<dim3((unsigned)g), kThreads, 0, s>>>(x, groups, ws, parts, q, bscale, tscale);
+    const int64_t g = grid_for(groups_pad, kThreads * 2, 4096);
+    quant_block16_encode_kernel<<<dim3((unsigned)g), kThreads, 0, s>>>(x, groups, groups_pad, div_g, G, layout, partial,
+                                                                      parts, q, bscale, tscale);
     return hipGetLastError();
 }
 

@@ -201,6 +201,37 @@ def test_quantize_block16_bitexact(spg, shape, std):
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
+def unblock_scales(plane: np.ndarray, R: int, K: int) -> np.ndarray:
+    """Row-major [R, K/16] view of a blocked NVFP4 scale plane (4 KiB blocks
+    of 256 rows x 16 scale bytes, by row tile then K stage) and its padding
+    rows."""
+    tiles, stages = plane.shape[0], plane.shape[1]
+    full = plane.reshape(tiles, stages, 256, 16).transpose(0, 2, 1, 3).reshape(tiles * 256, stages * 16)
+    return full[:R], full[R:]
+
+
+@pytest.mark.parametrize("shape,std", [((1, 256), 1.0), ((300, 512), 1.0), ((257, 1024), 0.02), ((4096, 6144), 1.0),
+                                       ((5120, 6144), 0.02), ((6144, 8448), 1.0)], ids=lambda v: str(v))
+def test_quantize_block16_blocked_layout(spg, shape, std):
+    # the blocked plane holds exactly the row-major scales, padding rows are
+    # zero, and codes and the tensor scale do not depend on the layout; the
+    # last shape is beyond one resident grid (the two-pass path)
+    R, K = shape
+    x16 = bf16_normal(shape, std, 3100 + R)
+    path = spg.lib.quantize_block16_path(R, K)
+    assert path == (2 if R * K > 40_000_000 else 1)
+    x = dev(x16)
+    qo, bso, to = oracle.quantize_block16(x16)
+    for single in (False, True):         # two passes; single launch where the tensor fits one grid
+        q, bs, t = spg.quantize_block16(x, layout="blocked", single_launch=single)
+        qr, bsr, tr = spg.quantize_block16(x, layout="row", single_launch=single)
+        plane, pad = unblock_scales(bs.cpu().numpy(), R, K)
+        assert t.cpu().numpy().view(np.uint32)[0] == np.float32(to).view(np.uint32) == tr.cpu().numpy().view(np.uint32)[0]
+        assert np.array_equal(plane, bso) and np.array_equal(bsr.cpu().numpy(), bso)
+        assert pad.size == ((-R) % 256) * (K // 16) and np.all(pad == 0)
+        assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(qr.cpu().numpy(), qo)
+
+
 def test_quantize_block16_every_bf16_value_in_unit_groups(spg):
     # tensor amax 2688 gives t = 1; a group led by 6 gets scale code 1.0,
     # so its other 15 values are encoded directly to E2M1
@@ -465,6 +496,25 @@ def test_gemm_nvfp4_stage256_shapes(spg, shape, epi):
     check_close(gpu, ref["y"], ref["S"], f"nvfp4 {shape} {epi}")
 
 
+# blocked scale planes (K a multiple of 256): ragged M and N (zero padding
+# rows), SwiGLU halves that are not multiples of 128 rows (up rows straddle
+# the plane's 256-row blocks), and a single tile split along K
+@pytest.mark.parametrize("epi", ["store", "add", "swiglu"])
+@pytest.mark.parametrize("shape", [(64, 64, 256), (257, 400, 512), (300, 520, 1024), (256, 256, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_nvfp4_blocked_scales(spg, shape, epi):
+    M, N, K = shape
+    A16 = bf16_normal((M, K), 1.0, 160 + M)
+    W16 = bf16_normal((N, K), 0.02, 161 + N)
+    R16 = bf16_normal((M, N), 1.0, 162) if epi == "add" else None
+    qa, bsa, ta = spg.quantize_block16(dev(A16), layout="blocked")
+    qw, bsw, tw = spg.quantize_block16(dev(W16), layout="blocked")
+    out = spg.gemm_scaled(qa, bsa, qw, bsw, epi, residual=dev(R16) if R16 is not None else None,
+                          fmt="nvfp4", tscale_a=ta, tscale_w=tw, scale_layout="blocked")
+    ref = oracle_nvfp4(A16, W16, epi, R16)
+    check_close(host_u16(out), ref["y"], ref["S"], f"nvfp4 blocked {shape} {epi}")
+
+
 def test_gemm_nvfp4_wide_scale_range(spg):
     # block scales spanning subnormal E4M3 codes exercise every decode path
     M, N, K = 96, 64, 512
@@ -519,9 +569,10 @@ def test_workload_full_size_sampled(spg, name):
         qw, sw = spg.quantize_tensor(W)
         out = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue, fmt="e4m3_tensor")
     else:
-        qa, sa, ta = spg.quantize_block16(A)
-        qw, sw, tw = spg.quantize_block16(W)
-        out = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue, residual=R, fmt="nvfp4", tscale_a=ta, tscale_w=tw)
+        qa, sa, ta = spg.quantize_block16(A, layout="blocked")
+        qw, sw, tw = spg.quantize_block16(W, layout="blocked")
+        out = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue, residual=R, fmt="nvfp4", tscale_a=ta, tscale_w=tw,
+                              scale_layout="blocked")
     torch.cuda.synchronize()
     gpu = host_u16(out)
     del A, W, R, qa, qw, out
@@ -889,8 +940,8 @@ def test_nvfp4_and_tensor_quantizers_and_gemm_with_guard_bands(spg, M, N, K):
         nws = spg.lib.quantize_block16_workspace_bytes(R, K)
         ws = torch.empty((max(nws, 16),), dtype=torch.uint8, device="cuda")
         q, bs, t = _interior(qbuf, G, R * K // 2), _interior(sbuf, G + 3, R * K // 16), _interior(tbuf, G // 4, 1)
-        st = spg.lib.quantize_block16(spg._ptr(x), R, K, spg._ptr(q), spg._ptr(bs), spg._ptr(t), spg._ptr(ws),
-                                      ws.numel(), spg._stream(x))
+        st = spg.lib.quantize_block16(spg._ptr(x), R, K, spg._ptr(q), spg._ptr(bs), spg._ptr(t), spg.SCALES_ROW_MAJOR,
+                                      spg._ptr(ws), ws.numel(), spg._stream(x))
         assert st == 0
         torch.cuda.synchronize()
         qo, bso, to = oracle.quantize_block16(x16)

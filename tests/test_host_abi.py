@@ -225,9 +225,34 @@ def test_quantizer_validation_errors(spg):
     assert L.quantize_tensor(FAKE, 2, 64, 64, 4000, FAKE, FAKE, FAKE, nws, None) == EINVAL  # bstride < rows*K
     assert L.quantize_tensor(FAKE, 0, 64, 64, 4096, FAKE, FAKE, FAKE, nws, None) == EINVAL
     nb = L.quantize_block16_workspace_bytes(64, 64)
-    assert L.quantize_block16(FAKE, 64, 48, FAKE, FAKE, FAKE, FAKE, nb, None) == EINVAL     # K % 32
-    assert L.quantize_block16(FAKE, 64, 64, FAKE, FAKE, FAKE, None, 0, None) == EWS
-    assert L.quantize_block16(FAKE, 64, 64, None, FAKE, FAKE, FAKE, nb, None) == EINVAL
+    assert nb >= 4 * (4 + 1)                     # election words + at least one partial
+    ROW, BLK = 0, 1
+    assert L.quantize_block16(FAKE, 64, 48, FAKE, FAKE, FAKE, ROW, FAKE, nb, None) == EINVAL     # K % 32
+    assert L.quantize_block16(FAKE, 64, 64, FAKE, FAKE, FAKE, ROW, None, 0, None) == EWS
+    assert L.quantize_block16(FAKE, 64, 64, None, FAKE, FAKE, ROW, FAKE, nb, None) == EINVAL
+    assert L.quantize_block16(FAKE, 64, 64, FAKE, FAKE, FAKE, 2, FAKE, nb, None) == EINVAL       # bad layout
+    assert L.quantize_block16(FAKE, 64, 64, FAKE, FAKE, FAKE, 0x200, FAKE, nb, None) == EINVAL   # unknown flag
+    assert L.quantize_block16(FAKE, 64, 224, FAKE, FAKE, FAKE, BLK, FAKE, nb, None) == EINVAL    # blocked: K % 256
+    assert L.quantize_block16_noalloc(FAKE, 64, 48, FAKE, FAKE, FAKE, ROW, None) == EINVAL
+    assert L.quantize_block16_noalloc(FAKE, 64, 224, FAKE, FAKE, FAKE, BLK, None) == EINVAL
+    assert L.quantize_block16_noalloc(MIS, 64, 64, FAKE, FAKE, FAKE, ROW, None) == EINVAL
+
+
+def test_gemm_scale_layout_validation(spg):
+    # blocked NVFP4 planes need K % 256 == 0; the field must be zero for FP8
+    d = desc(spg, 64, 64, 224, 2)
+    d.scale_layout = 1
+    assert call_gemm(spg, d) == EINVAL
+    d = desc(spg, 64, 64, 256, 2)
+    d.scale_layout = 3
+    assert call_gemm(spg, d) == EINVAL
+    d = desc(spg, 64, 64, 64, 0)
+    d.scale_layout = 1
+    assert call_gemm(spg, d) == EINVAL
+    d = desc(spg, 64, 64, 256, 2)
+    d.scale_layout = 1
+    p = spg.Plan()
+    assert spg.lib.spg_gemm_plan(ctypes.byref(d), 0, 256, ctypes.byref(p)) == 0
 
 
 # ---------------------------------------------------------------------------
