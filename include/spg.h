@@ -274,7 +274,11 @@ int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t
 /*
  * The plan gemm_scaled would launch for `d` on a device with `units` compute
  * units: tile shape, K-split, the number of workgroups and the tail (split
- * along K, or run as half-height tiles).
+ * along K, or run as half-height tiles).  For unsplit FP8 products of more
+ * than 64 tokens the tile geometry (256 x 256, or 128 x 256 over the whole
+ * product) is chosen with the route model above: factor 1 for 256 x 256,
+ * 1.9 for 128 x 256 (measured), the 256 x 256 route's partial last round
+ * replaced by its tail.
  * Returns SPG_OK or the validation error gemm_scaled would return.  The
  * workspace holds one fp32 256x256 partial tile per split tile and slice.
  */
@@ -286,7 +290,8 @@ typedef struct spg_plan {
                              /* the tail) * split_k, or at most one per       */
                              /* compute unit when the FP8 kernel runs an      */
                              /* unsplit product persistently                  */
-    int32_t kernel;          /* internal kernel id                            */
+    int32_t kernel;          /* 0: FP8 256 x 256 tiles; 1: NVFP4; 2: FP8      */
+                             /* 128 x 256 tiles (bm = 128) over the product   */
     int32_t tail_split;      /* > 1: the last tail_tiles tiles run in a second */
                              /* launch split tail_split ways along K (whole   */
                              /* rounds of tiles stay unsplit), else 1         */

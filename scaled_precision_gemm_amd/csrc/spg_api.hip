@@ -118,6 +118,33 @@ int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk, bool fp
     return best;
 }
 
+// The route model of ninfer PR #167 ("Routing"): a route's cost is its
+// waves (ceil(tiles / (units * per_unit))) times the work one unit carries
+// through a wave (per_unit * bm * bn), times one calibrated factor per route.
+double route_cost(const spg_route_candidate &c, int64_t M, int64_t N, int64_t batch, int32_t units)
+{
+    if (c.bm <= 0 || c.bn <= 0 || c.per_unit <= 0 || units <= 0) return INFINITY;
+    const int64_t tiles = batch * cdiv(M, c.bm) * cdiv(N, c.bn);
+    const int64_t slots = (int64_t)units * c.per_unit;
+    return c.factor * (double)cdiv(tiles, slots) * (double)c.per_unit * (double)c.bm * (double)c.bn;
+}
+
+// The two FP8 tile geometries, in that model, for MI355X (256 compute units,
+// one workgroup each: both kernels use most of the LDS):
+//   256 x 256 tiles (persistent kernel), factor 1;
+//   128 x 256 tiles (the half-height kernel, one tile per workgroup): a half
+//   tile still copies the whole 256-row W panel, 3/4 of a full tile's copy
+//   bytes for 1/2 of its MFMAs, and the copies (L2 to LDS) are what bounds
+//   these kernels.  Measured over whole products a half tile takes ~0.95 of a
+//   full tile's time (384 x 43008 x 4096: 0.101 ms in 128-row tiles against
+//   0.093 ms in 256-row tiles with a half-height tail; 640 x 26624 x 4096:
+//   0.098 against 0.088 ms), i.e. factor 1.9 on its half-size work.
+// So 128-row tiles are taken only where 256-row tiles would leave half of
+// each tile empty (65 to 128 tokens in one round); everywhere else the full
+// geometry wins.
+constexpr spg_route_candidate kFullTile = {256, 256, 1, 1.0};
+constexpr spg_route_candidate kHalfTile = {128, 256, 1, 1.9};
+
 void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
 {
     memset(p, 0, sizeof(*p));
@@ -177,6 +204,30 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
             }
         }
     }
+    // Geometry (FP8, unsplit, more than 64 tokens): the full route's cost in
+    // the PR #167 model, its partial last round replaced by the tail chosen
+    // above, against the half-height geometry over the whole product.
+    if (p->kernel == 0 && p->split_k == 1 && d->M > 64 && d->K > 0 && p->tiles > 0) {
+        const int64_t Nw = tiles_n * kTile;   // tile columns in W rows (SWIGLU: 128 gate + 128 up each)
+        double full = route_cost(kFullTile, d->M, Nw, d->batch, units);
+        if (p->tail_tiles > 0) {
+            const double rate = 9.6e12, t_tile = 2.0 * kTile * kTile * (double)d->K / rate;
+            const double tail = p->tail_bm < kTile ? 0.55 * t_tile + 5e-6
+                                                   : t_tile / p->tail_split + 2.0 * (double)p->tail_tiles *
+                                                     p->tail_split * kTile * kTile * 4.0 / 4e12 + 10e-6;
+            full += (tail / t_tile - 1.0) * kFullTile.bm * kFullTile.bn;
+        }
+        const double half = route_cost(kHalfTile, d->M, Nw, d->batch, units);
+        if (half < full) {
+            p->kernel = 2;                    // the half-height kernel over every tile
+            p->bm = (int32_t)(kTile / 2);
+            p->tail_tiles = 0;
+            p->tail_split = 1;
+            p->tail_bm = (int32_t)kTile;
+            p->workgroups = 2 * p->tiles;     // two 128-row halves per 256-row tile
+            return;
+        }
+    }
     const int64_t main_tiles = p->tiles - p->tail_tiles;
     // The FP8 kernel runs unsplit products with two or more K stages
     // persistently: one workgroup per compute unit walking its tiles.
@@ -225,11 +276,7 @@ SPG_EXPORT void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64
 
 SPG_EXPORT double spg_route_cost(const spg_route_candidate *c, int64_t M, int64_t N, int64_t batch, int32_t units)
 {
-    if (!c || c->bm <= 0 || c->bn <= 0 || c->per_unit <= 0 || units <= 0) return INFINITY;
-    const int64_t tiles = batch * cdiv(M, c->bm) * cdiv(N, c->bn);
-    const int64_t slots = (int64_t)units * c->per_unit;
-    const int64_t waves = cdiv(tiles, slots);
-    return c->factor * (double)waves * (double)c->per_unit * (double)c->bm * (double)c->bn;
+    return c ? route_cost(*c, M, N, batch, units) : INFINITY;
 }
 
 SPG_EXPORT int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t N, int64_t batch,
@@ -349,7 +396,8 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     spg_plan pm = p;
     pm.tiles = g.tile_count;
     g.clocks = d->clock_probe;
-    hipError_t e = launch(g, pm);
+    // the half-height geometry over every tile, or the planned main launch
+    hipError_t e = p.kernel == 2 ? launch_gemm_fp8_half(g, s) : launch(g, pm);
     g.clocks = nullptr;                // the clock record covers the main launch only
     if (e == hipSuccess && p.tail_tiles > 0 && p.tail_bm < kTile) {
         // the tail: the last tail_tiles tiles as half-height tiles

@@ -410,12 +410,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 }
 
 // ---------------------------------------------------------------------------
-// Half-height tiles for a short last round.  When the tiles leave a last
-// round that fills at most half of the compute units (4096 x 34816 x 5120
-// SwiGLU: 2176 tiles = 8.5 rounds of 256), those tiles run in a second launch
-// as 128 x 256 halves, one per workgroup, so the round is spread over every
-// compute unit and takes about half as long; unlike a K split this needs no
-// partial tiles and no reduction.
+// Half-height tiles (128 x 256), one per workgroup.  Two uses: a short last
+// round (when the tiles leave a last round that fills at most half of the
+// compute units - 4096 x 34816 x 5120 SwiGLU: 2176 tiles = 8.5 rounds of 256
+// - those tiles run in a second launch as 128 x 256 halves, so the round is
+// spread over every compute unit and takes about half as long; unlike a K
+// split this needs no partial tiles and no reduction), and the whole product
+// when the planner's route model prefers 128-row tiles (M just past a
+// multiple of 256).  A half whose rows all lie past M returns at once.
 //
 // Same data path as the full kernel (direct-to-LDS copies of 128-byte row
 // segments, the same swizzle, W fragments first), with the A side halved:
@@ -445,6 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
     __shared__ __attribute__((aligned(2048))) uint8_t lds[kSlotsH * kSlotH];
     __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
     __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+    clock_mark(g.clocks, 0);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -610,6 +613,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
     lds_sw[tid] = vw;
     block_barrier();
     epilogue<EPI, 2>(g, T, acc, lds_sa, lds_sw, &lds[wave * (kEpiRegionBytes / 4)]);
+    clock_mark(g.clocks, 1);
 }
 
 template <int EPI>

@@ -278,8 +278,9 @@ def test_plans_for_the_workloads(spg):
     # NVFP4 at 16 tokens keeps the wave-quantised model
     p = spg.gemm_plan(16, 34816, 5120, "nvfp4", "swiglu")
     assert p["split_k"] == 5
+    # 128 tokens, one tile: the 128 x 256 geometry, two half tiles (one empty)
     p = spg.gemm_plan(128, 256, 512, "e4m3_row", "store")
-    assert (p["tiles"], p["split_k"], p["workgroups"]) == (1, 1, 1)
+    assert (p["tiles"], p["split_k"], p["workgroups"], p["bm"]) == (1, 1, 2, 128)
     p = spg.gemm_plan(512, 512, 512, "e4m3_tensor", "store", batch=64)
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (256, 1, 256)
     p = spg.gemm_plan(8192, 8192, 8192, "e4m3_tensor", "store")
@@ -382,3 +383,45 @@ def test_probe_validation_errors(spg):
     assert spg.lib.spg_probe_read(buf, 1000, 1, buf, None) == 1          # not a multiple of 16
     assert spg.lib.spg_probe_read(P(0x10008), 1024, 1, buf, None) == 1   # source not 16-byte aligned
     assert spg.lib.spg_probe_read(buf, 1024, 0, buf, None) == 1
+
+
+# ---------------------------------------------------------------------------
+# the MI355X plan: tile geometry (ninfer PR #167's route model, recalibrated
+# for 256 compute units: 256 x 256 factor 1, 128 x 256 factor 1.9), split-K,
+# tails; the decisions for the benchmark workloads and the cases where the
+# 128-row geometry is taken
+# ---------------------------------------------------------------------------
+MI355X_PLANS = [
+    # (M, N, K, fmt, epi, batch) -> (kernel, bm, split_k, tail_tiles, tail_split, tail_bm)
+    ((128, 256, 512, "e4m3_row", "store", 1), (2, 128, 1, 0, 1, 256)),       # 65-128 tokens: 128-row tiles
+    ((96, 34816, 5120, "e4m3_row", "swiglu", 1), (2, 128, 1, 0, 1, 256)),
+    ((257, 300, 160, "e4m3_row", "store", 1), (2, 128, 1, 0, 1, 256)),
+    ((1024, 5120, 17408, "e4m3_row", "add", 1), (0, 256, 3, 0, 1, 256)),    # 80 tiles: K split 3
+    ((4096, 34816, 5120, "e4m3_row", "swiglu", 1), (0, 256, 1, 128, 1, 128)),  # 8.5 rounds: half-height tail
+    ((4096, 5120, 6144, "e4m3_row", "add", 1), (0, 256, 1, 64, 1, 128)),
+    ((384, 43008, 4096, "e4m3_row", "store", 1), (0, 256, 1, 80, 1, 128)),
+    ((4096, 5120, 6144, "nvfp4", "add", 1), (1, 256, 1, 64, 4, 256)),        # NVFP4: K-split tail
+    ((8192, 8192, 8192, "e4m3_tensor", "store", 1), (0, 256, 1, 0, 1, 256)),
+    ((512, 512, 512, "e4m3_tensor", "store", 64), (0, 256, 1, 0, 1, 256)),
+    ((16, 5120, 17408, "e4m3_row", "add", 1), (0, 256, 8, 0, 1, 256)),       # few tokens: split model
+    ((16, 34816, 5120, "e4m3_row", "swiglu", 1), (0, 256, 3, 0, 1, 256)),
+]
+
+
+@pytest.mark.parametrize("case,want", MI355X_PLANS, ids=lambda v: "x".join(map(str, v[:3])) if len(v) == 6 and isinstance(v[3], str) else None)
+def test_mi355x_plan_decisions(spg, case, want):
+    M, N, K, fmt, epi, b = case
+    p = spg.gemm_plan(M, N, K, fmt, epi, batch=b, units=256)
+    assert (p["kernel"], p["bm"], p["split_k"], p["tail_tiles"], p["tail_split"], p["tail_bm"]) == want
+
+
+def test_geometry_costs_follow_the_route_model(spg):
+    # the planner's two candidates priced by the exported PR #167 model: at
+    # 384 tokens the 128-row tiles waste nothing but cost 1.9 per unit of
+    # work, at 128 tokens the 256-row tiles waste half of every tile
+    full, half = (256, 256, 1, 1.0), (128, 256, 1, 1.9)
+    assert spg.route_cost(*full, 384, 43008, 1, 256) == 2 * 256 * 256
+    assert spg.route_cost(*half, 384, 43008, 1, 256) == 1.9 * 2 * 128 * 256
+    assert spg.route_cost(*half, 128, 34816, 1, 256) < spg.route_cost(*full, 128, 34816, 1, 256)
+    assert spg.route_select([full, half], 128, 34816, 1, 256) == 1
+    assert spg.route_select([full, half], 4096, 34816, 1, 256) == 0
