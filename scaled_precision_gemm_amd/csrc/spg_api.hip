@@ -79,10 +79,10 @@ int validate_desc(const spg_gemm_desc *d, int epi)
 // wave of tiles: the cost model below.  Otherwise the split s <= 8
 // (K / s >= 1024) that minimises waves(tiles * s) / s, the wave-quantised
 // time of the split work.  (With s <= 8 and K / s >= 1024 no slice is empty.)
-int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk, bool fp8)
+int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk, bool streaming)
 {
     if (tiles * 2 > units && M > 64) return 1;
-    if (M <= 64 && fp8 && tiles <= units) {
+    if (M <= 64 && streaming && tiles <= units) {
         // Few-token FP8 products stream their weights, and a workgroup's fixed
         // cost (pipeline fill, partial stores, its share of the reduction) is
         // worth about eight 128-deep stages: minimise waves * (slice + 1024)
@@ -96,6 +96,7 @@ int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk, bool fp
         for (int s = 2; s <= 8; ++s) {
             const int64_t chunk = cdiv(cdiv(K, s), bk) * bk;
             if (K / s < 1024) break;
+            if ((int64_t)(s - 1) * chunk >= K) continue;   // a slice would be empty
             const double cost = (double)cdiv(tiles * s, units) * ((double)chunk + 1024.0);
             if (cost < best_cost - 1e-9) {
                 best_cost = cost;
@@ -108,6 +109,7 @@ int choose_split(int64_t tiles, int64_t M, int64_t K, int units, int bk, bool fp
     double best_cost = 1.0;
     for (int s = 2; s <= 8; ++s) {
         if (K / s < 1024) break;
+        if ((int64_t)(s - 1) * (cdiv(cdiv(K, s), bk) * bk) >= K) continue;   // a slice would be empty
         const double waves = (double)cdiv(tiles * s, units);
         const double cost = waves / s;
         if (cost < best_cost - 1e-9) {
@@ -157,7 +159,10 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
     const int64_t tiles_m = cdiv(d->M, kTile);
     const int64_t tiles_n = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
     p->tiles = tiles_m * tiles_n * d->batch;
-    p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->M, d->K, units, p->bk, d->format != SPG_FMT_NVFP4) : 1;
+    // few-token products (both formats stream their weights) take the
+    // weight-streaming split model when NVFP4 runs its fast path
+    const bool streaming = d->format != SPG_FMT_NVFP4 || p->bk == 256;
+    p->split_k = (p->tiles > 0 && d->K > 0) ? choose_split(p->tiles, d->M, d->K, units, p->bk, streaming) : 1;
     p->kernel = d->format == SPG_FMT_NVFP4 ? 1 : 0;
     p->tail_split = 1;
     p->tail_tiles = 0;
@@ -341,6 +346,8 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     }
     if (d->format == SPG_FMT_NVFP4) {
         if (!d->tscale_a || !d->tscale_w || !aligned4(d->tscale_a) || !aligned4(d->tscale_w)) return SPG_EINVAL;
+        // blocked planes are read only by the fast path, which copies 16-byte pieces
+        if (d->scale_layout == SPG_SCALES_BLOCKED && (!aligned16(sa) || !aligned16(sw))) return SPG_EINVAL;
     } else if (!aligned4(sa) || !aligned4(sw)) {
         return SPG_EINVAL;
     }

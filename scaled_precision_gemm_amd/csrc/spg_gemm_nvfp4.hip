@@ -218,7 +218,11 @@ constexpr int kCodeOp = kBM * 128;              // code bytes per operand per st
 constexpr int kScaleOp = kBM * 16;              // scale bytes per operand per stage: 4 KiB
 constexpr int kSlotF = 2 * (kCodeOp + kScaleOp);   // [A codes][W codes][A scales][W scales]
 
-template <int EPI, bool SPLIT>
+// AM: A blocks per wave that take part (4 in general).  Products of at most
+// 32 (64) tokens have only their first 32 (64) tile rows, so AM = 1 (2)
+// leaves out the code reads, decodes and MFMAs of the empty A blocks: a stage
+// is then paced by the weights (their copies and decode), as for FP8.
+template <int EPI, bool SPLIT, int AM = 4>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs g)
 {
     __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlotF];
@@ -344,12 +348,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
         uint2 code[2][8];
         h2 bs[2][8];
         uint4 fr[2][8];                                // decoded fragments of the current / next k-step
+        // fragment f takes part unless it is an A block past AM
+        auto live = [](int f) { return f >= 4 || f < AM; };
 #pragma unroll
-        for (int f = 0; f < 8; ++f) code[0][f] = read_code(0, f);
+        for (int f = 0; f < 8; ++f)
+            if (live(f)) code[0][f] = read_code(0, f);
 #pragma unroll
-        for (int f = 0; f < 8; ++f) bs[0][f] = scale_of(0, f);
+        for (int f = 0; f < 8; ++f)
+            if (live(f)) bs[0][f] = scale_of(0, f);
 #pragma unroll
-        for (int f = 0; f < 8; ++f) fr[0][f] = decode8_cvt(code[0][f].x, bs[0][f]);
+        for (int f = 0; f < 8; ++f)
+            if (live(f)) fr[0][f] = decode8_cvt(code[0][f].x, bs[0][f]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -360,18 +369,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int y = j >> 2, x = j & 3;
-                    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fr[fc][4 + x]),
-                                                                     __builtin_bit_cast(v8h, fr[fc][y]), acc[x][y], 0, 0, 0);
+                    if (y < AM)
+                        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fr[fc][4 + x]),
+                                                                         __builtin_bit_cast(v8h, fr[fc][y]), acc[x][y],
+                                                                         0, 0, 0);
+                    const int f = j >> 1;
                     if (d == 0) {
-                        if ((j & 1) == 0) fr[fn][j >> 1] = decode8_cvt(code[cb][j >> 1].y, bs[cb][j >> 1]);
+                        if ((j & 1) == 0 && live(f)) fr[fn][f] = decode8_cvt(code[cb][f].y, bs[cb][f]);
                         if (j == 1 && c + 1 < 8) {
 #pragma unroll
-                            for (int f = 0; f < 8; ++f) code[nb][f] = read_code(c + 1, f);
+                            for (int ff = 0; ff < 8; ++ff)
+                                if (live(ff)) code[nb][ff] = read_code(c + 1, ff);
                         }
-                        if ((j & 1) == 1 && c + 1 < 8) bs[nb][j >> 1] = scale_of(c + 1, j >> 1);
+                        if ((j & 1) == 1 && c + 1 < 8 && live(f)) bs[nb][f] = scale_of(c + 1, f);
                     } else if (c + 1 < 8) {
                         if (j == 0) wait_lds();
-                        if ((j & 1) == 0) fr[fn][j >> 1] = decode8_cvt(code[nb][j >> 1].x, bs[nb][j >> 1]);
+                        if ((j & 1) == 0 && live(f)) fr[fn][f] = decode8_cvt(code[nb][f].x, bs[nb][f]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -413,8 +426,16 @@ hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
     // 16-byte aligned (rows are, since K / 16 is then a multiple of 16)
     const bool fast = p.bk == kBKF && (((uintptr_t)g.sa | (uintptr_t)g.sw) & 15) == 0;
     if (fast) {
-        if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true><<<grid, kThreads, 0, s>>>(g);
-        else gemm_nvfp4_kernel<EPI, false><<<grid, kThreads, 0, s>>>(g);
+        if (g.M <= 32) {
+            if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true, 1><<<grid, kThreads, 0, s>>>(g);
+            else gemm_nvfp4_kernel<EPI, false, 1><<<grid, kThreads, 0, s>>>(g);
+        } else if (g.M <= 64) {
+            if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true, 2><<<grid, kThreads, 0, s>>>(g);
+            else gemm_nvfp4_kernel<EPI, false, 2><<<grid, kThreads, 0, s>>>(g);
+        } else {
+            if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true><<<grid, kThreads, 0, s>>>(g);
+            else gemm_nvfp4_kernel<EPI, false><<<grid, kThreads, 0, s>>>(g);
+        }
     } else {
         gemm_nvfp4_general_kernel<EPI><<<grid, kThreads, 0, s>>>(g);
     }

@@ -92,6 +92,9 @@ WORKLOADS = {
     # the same two FP8 linears at 16 tokens (the narrow, weight-streaming route)
     "fp8_row_add_t16": Workload("fp8_row_add_t16", "e4m3_row", "add", 16, 5120, 17408, seed=600),
     "fp8_row_swiglu_t16": Workload("fp8_row_swiglu_t16", "e4m3_row", "swiglu", 16, 34816, 5120, seed=610),
+    # the NVFP4 [N=5120, K=6144] linear and the [34816, 5120] gate/up at 16 tokens
+    "nvfp4_add_t16": Workload("nvfp4_add_t16", "nvfp4", "add", 16, 5120, 6144, seed=620),
+    "nvfp4_swiglu_t16": Workload("nvfp4_swiglu_t16", "nvfp4", "swiglu", 16, 34816, 5120, seed=630),
     # the T=4096 [N=5120, K=6144] linear in row-scaled FP8 with a fused bf16 bias row
     "fp8_row_bias_t4096": Workload("fp8_row_bias_t4096", "e4m3_row", "add", 4096, 5120, 6144, seed=700, bias=True),
 }

@@ -832,6 +832,30 @@ def test_gemm_narrow_batched_broadcast_and_deterministic(spg):
         check_close(out1[b], y, S, f"narrow batch {b}")
 
 
+NARROW_NVFP4 = [((1, 64, 256), "store", "row"), ((5, 200, 1024), "add", "blocked"),
+                ((16, 2060, 512), "swiglu", "row"), ((31, 520, 2048), "store", "blocked"),
+                ((16, 5120, 6144), "add", "blocked"), ((16, 34816, 5120), "swiglu", "blocked"),
+                ((33, 300, 1024), "store", "row"), ((64, 2048, 4096), "add", "blocked"),
+                ((7, 400, 512), "swiglu", "row"), ((48, 520, 1056), "store", "row")]
+
+
+@pytest.mark.parametrize("shape,epi,layout", NARROW_NVFP4, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_gemm_nvfp4_narrow(spg, shape, epi, layout):
+    # few tokens on the NVFP4 path: one (<= 32 tokens) or two (<= 64) active
+    # A blocks per wave, the weight-streaming K split, both scale-plane
+    # layouts (K = 1056: the general path, row-major only)
+    M, N, K = shape
+    A16 = bf16_normal((M, K), 1.0, 170 + M)
+    W16 = bf16_normal((N, K), 0.02, 171 + N)
+    R16 = bf16_normal((M, N), 1.0, 172) if epi == "add" else None
+    qa, bsa, ta = spg.quantize_block16(dev(A16), layout=layout)
+    qw, bsw, tw = spg.quantize_block16(dev(W16), layout=layout)
+    out = spg.gemm_scaled(qa, bsa, qw, bsw, epi, residual=dev(R16) if R16 is not None else None,
+                          fmt="nvfp4", tscale_a=ta, tscale_w=tw, scale_layout=layout)
+    ref = oracle_nvfp4(A16, W16, epi, R16)
+    check_close(host_u16(out), ref["y"], ref["S"], f"nvfp4 narrow {shape} {epi} {layout}")
+
+
 # ---------------------------------------------------------------------------
 # padded leading dimensions: codes with row strides above K, output and
 # residual with row strides above N (odd element strides for the bf16 ones);

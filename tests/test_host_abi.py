@@ -275,9 +275,19 @@ def test_plans_for_the_workloads(spg):
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (136, 3, 408)
     p = spg.gemm_plan(16, 5120, 17408, "e4m3_row", "add")
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (20, 8, 160)
-    # NVFP4 at 16 tokens keeps the wave-quantised model
+    # NVFP4 at 16 tokens (fast path, K % 256 == 0) takes the weight-streaming
+    # model too; with K % 256 != 0 (general path) the wave-quantised one
     p = spg.gemm_plan(16, 34816, 5120, "nvfp4", "swiglu")
+    assert (p["split_k"], p["workgroups"]) == (3, 408)
+    p = spg.gemm_plan(16, 34816, 5152, "nvfp4", "swiglu")
     assert p["split_k"] == 5
+    # no K slice is ever empty
+    for K in (8448, 9472, 12544, 14080):
+        for fmt in ("nvfp4", "e4m3_row"):
+            p = spg.gemm_plan(16, 5120, K, fmt, "add")
+            s, bk = p["split_k"], p["bk"]
+            chunk = -(-(-(-K // s)) // bk) * bk
+            assert (s - 1) * chunk < K, (K, fmt, s)
     # 128 tokens, one tile: the 128 x 256 geometry, two half tiles (one empty)
     p = spg.gemm_plan(128, 256, 512, "e4m3_row", "store")
     assert (p["tiles"], p["split_k"], p["workgroups"], p["bm"]) == (1, 1, 2, 128)
