@@ -60,7 +60,7 @@ def _load():
         "spo_gemm_e4m3": (None, [c_p, c_i64, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_p]),
         "spo_gemm_nvfp4": (None, [c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_p, c_p]),
         "spo_epilogue": (None, [ctypes.c_int, c_p, c_p, c_i64, c_i64, c_p, c_p, c_p, c_i64,
-                                c_p, c_p, c_p]),
+                                c_p, c_p, c_p, c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -219,8 +219,19 @@ def gemm_nvfp4_sums(Aq, As, Wq, Ws):
     return D, Da
 
 
-def epilogue(epi, D, Dabs, ascale, wscale, residual=None):
-    """Apply scales and the epilogue in fp64; returns (y, S, out_bf16_bits)."""
+def bias_e4m3(codes: np.ndarray, scale) -> np.ndarray:
+    """A bias stored as E4M3 codes with one fp32 scale, dequantized: the exact
+    fp64 values dec(code) * scale (AstrAI commit log, the commit fusing the
+    bias: a non-null bias scale means FP8 storage dequantized in the
+    epilogue)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return E4M3_TABLE[c] * np.float64(np.float32(scale))
+
+
+def epilogue(epi, D, Dabs, ascale, wscale, residual=None, bias=None):
+    """Apply scales and the epilogue in fp64; returns (y, S, out_bf16_bits).
+    ADD takes a bf16 residual [M, Nout] and/or `bias`, fp64 values [Nout]
+    added to every row after the operand scales, before the one rounding."""
     epi = EPILOGUES.get(epi, epi)
     D = np.ascontiguousarray(D, np.float64)
     Dabs = np.ascontiguousarray(Dabs, np.float64)
@@ -230,28 +241,34 @@ def epilogue(epi, D, Dabs, ascale, wscale, residual=None):
     if epi == SWIGLU:
         assert Nw % 2 == 0
     Nout = Nw // 2 if epi == SWIGLU else Nw
+    rp, ldr, bp = None, 0, None
     if epi == ADD:
-        r = _u16(residual)
-        assert r.shape == (M, Nout)
-        rp, ldr = _p(r), Nout
+        assert residual is not None or bias is not None
+        if residual is not None:
+            r = _u16(residual)
+            assert r.shape == (M, Nout)
+            rp, ldr = _p(r), Nout
+        if bias is not None:
+            b = np.ascontiguousarray(bias, np.float64)
+            assert b.shape == (Nout,)
+            bp = _p(b)
     else:
-        assert residual is None
-        rp, ldr = None, 0
+        assert residual is None and bias is None
     y = np.empty((M, Nout), np.float64)
     S = np.empty((M, Nout), np.float64)
     out = np.empty((M, Nout), np.uint16)
-    _lib.spo_epilogue(int(epi), _p(D), _p(Dabs), M, Nw, _p(a), _p(w), rp, ldr,
+    _lib.spo_epilogue(int(epi), _p(D), _p(Dabs), M, Nw, _p(a), _p(w), rp, ldr, bp,
                       _p(y), _p(S), _p(out))
     return y, S, out
 
 
-def linear_e4m3_rowwise(A_bf16, W_bf16, epi, residual=None):
+def linear_e4m3_rowwise(A_bf16, W_bf16, epi, residual=None, bias=None):
     """Whole path, row-scaled FP8: quantize both operands per row, exact GEMM,
     scales, epilogue.  Returns dict with codes, scales, y, S, out."""
     Aq, sa = quantize_rowwise(A_bf16)
     Wq, sw = quantize_rowwise(W_bf16)
     D, Da = gemm_e4m3_sums(Aq, Wq)
-    y, S, out = epilogue(epi, D, Da, sa, sw, residual)
+    y, S, out = epilogue(epi, D, Da, sa, sw, residual, bias)
     return dict(Aq=Aq, sa=sa, Wq=Wq, sw=sw, y=y, S=S, out=out)
 
 

@@ -359,14 +359,18 @@ static double silu_prime(double z)
  * D, Dabs: [M, Nw] (row stride Nw); ascale[M], wscale[Nw] are the fp32 scales
  * as doubles (per-tensor and NVFP4 tensor scales are passed replicated).
  * STORE:  y = sa_i sw_j D_ij                        (Nout = Nw)
- * ADD:    y = sa_i sw_j D_ij + r_ij                 (Nout = Nw)
+ * ADD:    y = sa_i sw_j D_ij + r_ij + b_j           (Nout = Nw)
  * SWIGLU: y = silu(v_ij) v_i,j+Nw/2, v = sa sw D    (Nout = Nw/2)
+ * r (bf16 bits, row stride ldr) and b (fp64 [Nout], a bias already
+ * dequantized) may each be NULL (taken as zero).  The bias enters after the
+ * operand scales and before the one rounding to bf16 (AstrAI commit log, the
+ * commit fusing the bias into the GEMM epilogue).
  * y, tol_S: [M, Nout]; out: bf16 bits of y, rounded once from fp64.
  * tol_S is the error scale S of the acceptance bound |gpu - y| <=
  * 2^-8 |y| + 2^-12 S: S = |sa sw| Dabs, first-order propagated for SWIGLU. */
 EXPORT void spo_epilogue(int epi, const double *D, const double *Dabs, int64_t M, int64_t Nw,
                          const double *ascale, const double *wscale,
-                         const uint16_t *residual, int64_t ldr,
+                         const uint16_t *residual, int64_t ldr, const double *bias,
                          double *y, double *tol_S, uint16_t *out)
 {
     const int64_t Nout = (epi == SPO_SWIGLU) ? Nw / 2 : Nw;
@@ -386,7 +390,8 @@ EXPORT void spo_epilogue(int epi, const double *D, const double *Dabs, int64_t M
                 double v = ascale[i] * wscale[j] * D[i * Nw + j];
                 S = fabs(ascale[i] * wscale[j]) * Dabs[i * Nw + j];
                 yv = v;
-                if (epi == SPO_ADD) yv += (double)spo_bf16_to_f32(residual[i * ldr + j]);
+                if (epi == SPO_ADD && residual) yv += (double)spo_bf16_to_f32(residual[i * ldr + j]);
+                if (epi == SPO_ADD && bias) yv += bias[j];
             }
             y[i * Nout + j] = yv;
             tol_S[i * Nout + j] = S;

@@ -121,6 +121,65 @@ def test_bias_row_adds_to_every_token_row():
     assert np.array_equal(b["y"], st["y"] + bias_f[None, :])
 
 
+def _bf16_val(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_e4m3_bias_values_by_hand():
+    # E4M3 bias codes times one fp32 scale (AstrAI commit log, the commit
+    # fusing the bias: FP8 bias storage dequantized in the epilogue).  Code
+    # values worked by hand: sign, 4 exponent bits (bias 7), 3 mantissa bits.
+    codes = np.array([0x38, 0xB8, 0x3C, 0x44, 0x7E, 0xFE, 0x08, 0x01, 0x00, 0x80], np.uint8)
+    want = np.array([1.0, -1.0, 1.5, 3.0, 448.0, -448.0, 2.0 ** -6, 2.0 ** -9, 0.0, -0.0])
+    assert np.array_equal(oracle.bias_e4m3(codes, 1.0), want)
+    assert np.array_equal(oracle.bias_e4m3(codes, 0.75), want * 0.75)
+    # the scale is taken as fp32: 0.1 becomes float32(0.1), not the double
+    assert oracle.bias_e4m3(np.array([0x38], np.uint8), 0.1)[0] == float(np.float32(0.1))
+
+
+def test_e4m3_bias_with_zero_weights_is_its_nearest_bf16():
+    # zero weights: every row of the output is bf16(dec(code) * scale), one
+    # rounding of the exact product (checked against both bf16 neighbours)
+    A16 = bf16_normal((6, 32), 1.0, 21)
+    rng = np.random.default_rng(22)
+    codes = rng.choice(FINITE, size=(12,)).astype(np.uint8)
+    scale = np.float32(1.0 / 3.0)
+    exact = E4[codes] * np.float64(scale)
+    z = oracle.linear_e4m3_rowwise(A16, np.zeros((12, 32), np.uint16), "add",
+                                   bias=oracle.bias_e4m3(codes, scale))
+    assert np.array_equal(z["out"], np.tile(z["out"][0], (6, 1)))
+    got = z["out"][0]
+    err = np.abs(_bf16_val(got) - exact)
+    for nb in (got.astype(np.int64) + 1, got.astype(np.int64) - 1):
+        nb_val = _bf16_val((nb & 0xFFFF).astype(np.uint16))
+        assert np.all(err <= np.abs(nb_val - exact))
+    assert np.array_equal(np.signbit(_bf16_val(got)) | (exact == 0), np.signbit(exact) | (exact == 0))
+
+
+def test_e4m3_bias_adds_after_the_operand_scales():
+    # with weights: y is the store result plus the dequantized bias of the
+    # column (not scaled by sa sw, not indexed by row), in fp64 exactly; a
+    # bias made by row-quantizing a bf16 row is that row within E4M3's
+    # half-ulp (2^-4 relative, or 2^-10 of the row's scale for subnormals)
+    A16 = bf16_normal((8, 64), 1.0, 23)
+    W16 = bf16_normal((12, 64), 0.02, 24)
+    row = bf16_normal((12,), 0.5, 25)
+    bq, bs = oracle.quantize_rowwise(row[None, :])
+    b = oracle.bias_e4m3(bq[0], bs[0])
+    rv = _bf16_val(row)
+    assert np.all(np.abs(b - rv) <= 2.0 ** -4 * np.abs(rv) + 2.0 ** -10 * float(bs[0]))
+    res = oracle.linear_e4m3_rowwise(A16, W16, "add", bias=b)
+    st = oracle.linear_e4m3_rowwise(A16, W16, "store")
+    assert np.array_equal(res["y"], st["y"] + b[None, :])
+    assert np.array_equal(res["S"], st["S"])
+    # a bias of exact bf16 values (scale 1) equals the bf16 bias row
+    c1 = np.array([0x38, 0xC0, 0x30, 0x01, 0x7E, 0x00, 0xB4, 0x4A, 0x3A, 0x22, 0x9F, 0x5C], np.uint8)
+    row1 = f32_to_bf16_bits(E4[c1].astype(np.float32))
+    r1 = oracle.linear_e4m3_rowwise(A16, W16, "add", residual=np.broadcast_to(row1, (8, 12)))
+    b1 = oracle.linear_e4m3_rowwise(A16, W16, "add", bias=oracle.bias_e4m3(c1, 1.0))
+    assert np.array_equal(r1["out"], b1["out"]) and np.array_equal(r1["y"], b1["y"])
+
+
 def test_swiglu_matches_scipy_logistic_and_pairs_rows():
     A16 = bf16_normal((6, 64), 1.0, 11)
     W16 = bf16_normal((10, 64), 0.02, 12)
