@@ -205,6 +205,16 @@ int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q,
  *              reference counter at the same points ([2], [3]): the shader
  *              clock the kernel ran at is (c1 - c0) / (c3 - c2) * 100 MHz.
  *              A measurement aid only; results do not depend on it.
+ *   bias_scale : optional (NULL by default), device, one fp32 value.  When
+ *              set, the ADD epilogue's one-row residual (ldr == 0, a bias)
+ *              holds E4M3 codes, N bytes per batch entry (stride_r in bytes),
+ *              and bias j enters as dec(code_j) * bias_scale, formed in fp32
+ *              after the operand scales and before the one rounding to bf16;
+ *              one scale serves every batch entry.  NULL keeps the raw bf16
+ *              bias row (AstrAI commit log, the commit fusing the bias into
+ *              the GEMM epilogue: a null bias scale means a bf16 bias, a
+ *              non-null one FP8 storage dequantized in the epilogue).  Set
+ *              with any other epilogue or with ldr != 0: SPG_EINVAL.
  */
 typedef struct spg_gemm_desc {
     int64_t M, N, K, batch;
@@ -215,6 +225,7 @@ typedef struct spg_gemm_desc {
     const float *tscale_a;
     const float *tscale_w;
     uint64_t *clock_probe;
+    const float *bias_scale;
 } spg_gemm_desc;
 
 /* Zero every field, set batch = 1 and the dense strides for M, N, K. */
@@ -229,11 +240,12 @@ void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32
  *              E4M3_TENSOR: fp32 [batch] each (index 0 when broadcast);
  *              NVFP4: E4M3 block-scale planes [M, K/16] and [N, K/16] in
  *              d->scale_layout (NVFP4 requires batch == 1)
- *   residual : bf16 [M, N] (or one row [N] when ldr == 0), required for
- *              SPG_EPI_ADD, NULL otherwise; it may be the output itself
- *              (residual == out, ldr == ldo, stride_r == stride_o); any
- *              other overlap of the two, a bias row inside the output
- *              included, is SPG_EINVAL
+ *   residual : bf16 [M, N] (or one row [N] when ldr == 0; E4M3 codes [N]
+ *              when d->bias_scale is set), required for SPG_EPI_ADD, NULL
+ *              otherwise; it may be the output itself (residual == out,
+ *              ldr == ldo, stride_r == stride_o); any other overlap of the
+ *              two, a bias row inside the output included, is SPG_EINVAL,
+ *              and so is a bias scale inside the output
  *   epilogue : SPG_EPI_*; SWIGLU pairs W rows j (gate) and j + N/2 (up) and
  *              needs N even
  *   ws       : device workspace of at least gemm_scaled_workspace_bytes(d, epilogue)

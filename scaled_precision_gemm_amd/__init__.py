@@ -47,7 +47,7 @@ class GemmDesc(ctypes.Structure):
         ("stride_o", ctypes.c_int64), ("stride_r", ctypes.c_int64),
         ("format", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
         ("tscale_a", ctypes.c_void_p), ("tscale_w", ctypes.c_void_p),
-        ("clock_probe", ctypes.c_void_p),
+        ("clock_probe", ctypes.c_void_p), ("bias_scale", ctypes.c_void_p),
     ]
 
 
@@ -231,7 +231,7 @@ def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residua
 
 
 def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_a=None, tscale_w=None,
-                   scale_layout="row"):
+                   scale_layout="row", bias_scale=None):
     """Shapes, dtypes, strides and devices of a gemm_scaled call, checked
     before anything reaches the library (raises ValueError).  The library
     trusts the sizes it is given, so an output, residual or scale tensor
@@ -247,7 +247,7 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
     _need(A.stride(-1) == 1 and W.stride(-1) == 1, "rows of A and W must be contiguous")
     dev = A.device
     for name, t in (("W", W), ("sa", sa), ("sw", sw), ("out", out), ("residual", residual),
-                    ("tscale_a", tscale_a), ("tscale_w", tscale_w)):
+                    ("tscale_a", tscale_a), ("tscale_w", tscale_w), ("bias_scale", bias_scale)):
         _need(t is None or (isinstance(t, torch.Tensor) and t.device == dev), f"{name} must be on {dev}")
     Ab = A.shape[0] if A.dim() == 3 else 1
     Wb = W.shape[0] if W.dim() == 3 else 1
@@ -282,7 +282,14 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
         _need(out.dtype == torch.bfloat16, "out must be bf16")
         _need(tuple(out.shape) == want, f"out must have shape {want}")
         _need(out.stride(-1) == 1, "rows of out must be contiguous")
-    if epi == EPI_ADD:
+    if bias_scale is not None:
+        # an E4M3 bias row: uint8 codes [N], one fp32 scale
+        _need(epi == EPI_ADD, "a bias scale is taken only by the add epilogue")
+        _need(bias_scale.dtype == torch.float32 and bias_scale.numel() == 1, "bias_scale must be one fp32 value")
+        _need(residual is not None and residual.dtype == torch.uint8 and residual.dim() == 1
+              and residual.shape[0] == n_out and residual.stride(0) == 1,
+              f"with a bias scale the residual must be contiguous uint8 E4M3 codes [{n_out}]")
+    elif epi == EPI_ADD:
         _need(residual is not None, "the add epilogue needs a residual")
         _need(residual.dtype == torch.bfloat16, "residual must be bf16")
         _need(residual.stride(-1) == 1, "rows of the residual must be contiguous")
@@ -294,7 +301,8 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
 
 
 def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
-                out=None, tscale_a=None, tscale_w=None, workspace=None, clock_probe=None, scale_layout="row"):
+                out=None, tscale_a=None, tscale_w=None, workspace=None, clock_probe=None, scale_layout="row",
+                bias_scale=None):
     """out = epilogue(scale * A W^T) in bf16.
 
     e4m3_row: A uint8 [M,K], sa fp32 [M]; W uint8 [N,K], sw fp32 [N]
@@ -306,8 +314,12 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
            main GEMM launch records its clock counters there (see
            spg_gemm_desc.clock_probe): shader clock in GHz =
            (c[1] - c[0]) / (c[3] - c[2]) / 10
+    bias_scale: optional fp32 [1] on the same device; with "add" and a
+           residual of uint8 E4M3 codes [N], the bias added to every row is
+           dec(code) * bias_scale (see spg_gemm_desc.bias_scale); without it
+           a 1-D residual is a bf16 bias row
     """
-    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout)
+    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale)
     _need(A.is_cuda, "operands must be CUDA tensors")
     d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w)
     d.scale_layout = _LAYOUT.get(scale_layout, scale_layout)
@@ -315,6 +327,8 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
         _need(clock_probe.dtype == torch.int64 and clock_probe.numel() == 4 and clock_probe.is_contiguous()
               and clock_probe.device == A.device, "clock_probe must be 4 contiguous int64 values on A's device")
         d.clock_probe = clock_probe.data_ptr()
+    if bias_scale is not None:
+        d.bias_scale = bias_scale.data_ptr()
     n_out = d.N // 2 if epi == EPI_SWIGLU else d.N
     if out is None:
         shape = (d.batch, d.M, n_out) if batched else (d.M, n_out)

@@ -58,8 +58,10 @@ int validate_desc(const spg_gemm_desc *d, int epi)
     if (d->lda > (INT64_C(1) << 23) || d->ldw > (INT64_C(1) << 23)) return SPG_EUNSUPPORTED;
     if ((d->stride_a & 15) || (d->stride_w & 15)) return SPG_EINVAL;
     if (d->ldo < nout) return SPG_EINVAL;
-    // ldr == 0: one bf16 row (a bias) added to every token row
+    // ldr == 0: one row (a bias) added to every token row; a bias scale
+    // (E4M3 bias codes) only with such a row
     if (epi == SPG_EPI_ADD && d->ldr != 0 && d->ldr < nout) return SPG_EINVAL;
+    if (d->bias_scale && (epi != SPG_EPI_ADD || d->ldr != 0)) return SPG_EINVAL;
     // tile ids are computed in 32-bit arithmetic
     {
         const int64_t tm = cdiv(d->M, kTile), tn = epi == SPG_EPI_SWIGLU ? cdiv(nout, kTile / 2) : cdiv(d->N, kTile);
@@ -330,17 +332,24 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     // batch entries of the output must not overlap (several entries would
     // write the same elements concurrently)
     if (d->batch > 1 && d->stride_o < (d->M - 1) * d->ldo + nout) return SPG_EINVAL;
+    const uintptr_t o0 = (uintptr_t)out;
+    const uintptr_t o1 = o0 + 2 * (uintptr_t)((d->batch - 1) * d->stride_o + (d->M - 1) * d->ldo + nout);
     if (epilogue == SPG_EPI_ADD) {
-        if (!residual || !aligned2(residual)) return SPG_EINVAL;
+        const bool codes = d->bias_scale != nullptr;   // E4M3 bias row: 1-byte elements
+        if (!residual || (!codes && !aligned2(residual))) return SPG_EINVAL;
         // The residual may be the output itself (read and rewritten by the
         // same lane) only with the same element layout: same pointer, row
         // stride and batch stride.  Any other overlap - including a bias row
         // (ldr == 0) inside the output - is rejected.
-        const uintptr_t o0 = (uintptr_t)out, r0 = (uintptr_t)residual;
-        const uintptr_t o1 = o0 + 2 * (uintptr_t)((d->batch - 1) * d->stride_o + (d->M - 1) * d->ldo + nout);
-        const uintptr_t r1 = r0 + 2 * (uintptr_t)((d->batch - 1) * d->stride_r + (d->M - 1) * d->ldr + nout);
-        const bool same = r0 == o0 && d->ldr == d->ldo && d->stride_r == d->stride_o;
+        const uintptr_t r0 = (uintptr_t)residual;
+        const uintptr_t r1 = r0 + (codes ? 1 : 2) * (uintptr_t)((d->batch - 1) * d->stride_r + (d->M - 1) * d->ldr + nout);
+        const bool same = !codes && r0 == o0 && d->ldr == d->ldo && d->stride_r == d->stride_o;
         if (r0 < o1 && o0 < r1 && !same) return SPG_EINVAL;
+        if (codes) {
+            // read by every workgroup while others write the output
+            const uintptr_t b0 = (uintptr_t)d->bias_scale;
+            if (!aligned4(d->bias_scale) || (b0 < o1 && o0 < b0 + 4)) return SPG_EINVAL;
+        }
     } else if (residual) {
         return SPG_EINVAL;
     }
@@ -385,6 +394,8 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.tscale_a = d->tscale_a;
     g.tscale_w = d->tscale_w;
     g.scale_layout = d->format == SPG_FMT_NVFP4 ? d->scale_layout : SPG_SCALES_ROW_MAJOR;
+    g.bias_mode = epilogue == SPG_EPI_ADD && d->ldr == 0 ? (d->bias_scale ? 2 : 1) : 0;
+    g.bias_scale = d->bias_scale;
     g.split_k = p.split_k;
     const int64_t unit_k = p.bk;
     g.k_chunk = p.split_k > 1 ? cdiv(cdiv(d->K, p.split_k), unit_k) * unit_k : (d->K > 0 ? d->K : 1);

@@ -122,6 +122,8 @@ struct GemmArgs {
     FastDiv div_per, div_span, div_gm_last;   // by tiles_m*tiles_n, 8*tiles_n, tiles_m % 8
     uint64_t *clocks;                 // optional clock record (spg_gemm_desc.clock_probe), else null
     int32_t scale_layout;             // NVFP4 block-scale planes: SPG_SCALES_ROW_MAJOR or _BLOCKED
+    int32_t bias_mode;                // ADD: 0 a residual matrix, 1 a bf16 bias row, 2 an E4M3 bias row
+    const float *bias_scale;          // bias_mode 2: the bias row's fp32 scale
 };
 
 // Optional clock record of the main GEMM launch: thread 0 of workgroup 0

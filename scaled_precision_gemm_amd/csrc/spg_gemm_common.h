@@ -240,6 +240,23 @@ __device__ __forceinline__ void stage_scales(const GemmArgs &g, const Tile &T, f
     lds_sw[threadIdx.x] = vw;
 }
 
+// Bias of output column col (< N) of batch entry b, for the ADD epilogue
+// with a bias row: the bf16 value (bias_mode 1), or the E4M3 code times the
+// bias scale, dequantized in fp32 (bias_mode 2; AstrAI commit log, the
+// commit fusing the bias: FP8 bias storage dequantized after the operand
+// scaling).
+__device__ __forceinline__ float bias_at(const GemmArgs &g, int64_t b, int64_t col)
+{
+    const int64_t off = (g.stride_r ? b * g.stride_r : 0) + col;
+    if (g.bias_mode == 1) return __uint_as_float((uint32_t)g.residual[off] << 16);
+    return decode_e4m3(((const uint8_t *)g.residual)[off]) * *g.bias_scale;
+}
+
+// LDS floats a kernel with epilogue EPI provides for the bias of a bias row:
+// 128 columns per wave (ADD), else a placeholder.
+template <int EPI>
+constexpr int bias_words() { return EPI == SPG_EPI_ADD ? 4 * 128 : 4; }
+
 // Split-K, part 1: every K slice stores its fp32 partial tile and stops; a
 // second kernel (splitk_reduce_kernel) sums the slices once all have
 // finished - the kernel boundary orders the stores before the loads, so no
@@ -294,13 +311,14 @@ __device__ __forceinline__ EpiOut epi_out(const GemmArgs &g, const Tile &T)
     o.res = g.residual ? g.residual + (g.stride_r ? T.b * g.stride_r : 0) : nullptr;
     o.nvalid = EPI == SPG_EPI_SWIGLU ? g.N / 2 : g.N;
     o.vec = ((((uintptr_t)o.out) & 7) == 0) && ((g.ldo & 3) == 0);
-    if (EPI == SPG_EPI_ADD) o.vec = o.vec && ((((uintptr_t)o.res) & 7) == 0) && ((g.ldr & 3) == 0);
+    if (EPI == SPG_EPI_ADD && g.bias_mode == 0) o.vec = o.vec && ((((uintptr_t)o.res) & 7) == 0) && ((g.ldr & 3) == 0);
     return o;
 }
 
 // Fused epilogue of one 32x32 block straight from registers:
 //   v = acc * lds_sa[token row] * lds_sw[W row]
-//   STORE: bf16(v); ADD: bf16(v + residual), one rounding of the fp32 sum;
+//   STORE: bf16(v); ADD: bf16(v + residual), one rounding of the fp32 sum
+//   (a bias row: v + the bias of the column, dequantized in fp32);
 //   SWIGLU: bf16(silu(gate) * up), gate from `a`, up from `up` (same layout)
 // Lane l writes token row wm * 128 + y * 32 + l % 32 of the tile and, per
 // register group q, the four output columns at W-tile row
@@ -319,10 +337,20 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
     const float sa = lds_sa[rl];
     uint16_t *orow = o.out + row * g.ldo;
     const uint16_t *rrow = EPI == SPG_EPI_ADD ? o.res + row * g.ldr : nullptr;
+    const bool brow = EPI == SPG_EPI_ADD && g.bias_mode != 0;
 
-    // residual first, so its loads are in flight during the arithmetic
+    // residual (or bias) first, so its loads are in flight during the
+    // arithmetic
     uint2 rv[4];
-    if (EPI == SPG_EPI_ADD) {
+    float bv[EPI == SPG_EPI_ADD ? 4 : 1][4];
+    if (EPI == SPG_EPI_ADD && brow) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t col = T.c0 + w0 + q * 8 + khalf * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[EPI == SPG_EPI_ADD ? q : 0][j] = col + j < o.nvalid ? bias_at(g, T.b, col + j) : 0.0f;
+        }
+    } else if (EPI == SPG_EPI_ADD) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t col = T.c0 + w0 + q * 8 + khalf * 4;
@@ -354,7 +382,10 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
                 v[j] = a[e] * sa * sw[j];
             }
         }
-        if (EPI == SPG_EPI_ADD) {
+        if (EPI == SPG_EPI_ADD && brow) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] += bv[EPI == SPG_EPI_ADD ? q : 0][j];
+        } else if (EPI == SPG_EPI_ADD) {
             v[0] += bf16_lo(rv[q].x);
             v[1] += bf16_hi(rv[q].x);
             v[2] += bf16_lo(rv[q].y);
@@ -387,6 +418,9 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
 //  2. every lane forms v = acc * lds_sa * lds_sw (+ residual read back from
 //     the region in fp32, one rounding; SWIGLU silu(gate) * up) and writes the
 //     bf16 results in place (8 bytes per register group);
+//     BIAS (ADD with a bias row): step 1 is skipped; each wave first stages
+//     the fp32 biases of its 128 columns in its own 512 bytes of lds_bias,
+//     and step 2 adds the bias of the column;
 //  3. the region leaves as 16-byte chunks of whole 128-byte row segments.
 // `region` is this wave's 4 KiB, 16-byte aligned, used by nothing else.
 constexpr int kEpiRegionBytes = 4 * 4096;   // per workgroup
@@ -397,10 +431,11 @@ constexpr int kEpiRegionBytes = 4 * 4096;   // per workgroup
 // MI: 32-row A blocks per wave (4; 2 in a half-height tile, whose waves
 // hold acc[x][0..1] and cover token rows wm * 64 .. wm * 64 + 63).
 // GIVEN: wave_in is the caller's wave index; otherwise it is derived here.
-template <int EPI, bool FULL, int MI = 4, bool GIVEN = false>
+template <int EPI, bool FULL, int MI = 4, bool GIVEN = false, bool BIAS = false>
 __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
-                                              const float *lds_sw, uint8_t *region, int wave_in)
+                                              const float *lds_sw, float *lds_bias, uint8_t *region, int wave_in)
 {
+    static_assert(!BIAS || EPI == SPG_EPI_ADD, "a bias row belongs to the ADD epilogue");
     constexpr bool SW = EPI == SPG_EPI_SWIGLU;
     constexpr int NP = SW ? 1 : 2;            // 64-column passes per 32-row block
     // opaque to the optimizer: lane-derived offsets are recomputed per call
@@ -412,7 +447,7 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, khalf = lane >> 5;
     const EpiOut o = epi_out<EPI>(g, T);
     const bool vec16 = FULL || (((((uintptr_t)o.out) & 15) == 0) && ((g.ldo & 7) == 0));
-    const bool rvec = FULL || (EPI == SPG_EPI_ADD && ((((uintptr_t)o.res) & 15) == 0) && ((g.ldr & 7) == 0));
+    const bool rvec = FULL || (EPI == SPG_EPI_ADD && !BIAS && ((((uintptr_t)o.res) & 15) == 0) && ((g.ldr & 7) == 0));
     auto phys = [](int r, int c) -> int { return c ^ ((r >> 1) & 7); };
     const int rr = lane >> 3, rc = lane & 7;  // row-order lane position: 8 rows x 8 chunks
     // 32-bit element offsets inside a 32-row block (ldo, ldr < 2^26)
@@ -421,19 +456,31 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
     // every scale factor this lane needs, read from LDS before any region
     // write (the compiler cannot move LDS reads across LDS writes it cannot
     // prove disjoint, so reading them per element would wait on each)
+    // (BIAS: the column scales are read with the biases, next to their use,
+    // which keeps the epilogue within the registers the tile loop leaves)
+    float *const bias_w = lds_bias + (BIAS ? wave * 128 : 0);   // this wave's columns wn * 128 ..
+    if (BIAS) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t c = T.c0 + wn * 128 + h * 64 + lane;
+            bias_w[h * 64 + lane] = c < o.nvalid ? bias_at(g, T.b, c) : 0.0f;
+        }
+    }
     constexpr int NX = SW ? 2 : 4;
     float sa_r[MI];
-    v4f sw_r[NX][4], swu_r[SW ? 2 : 1][4];
+    v4f sw_r[BIAS ? 1 : NX][4], swu_r[SW ? 2 : 1][4];
 #pragma unroll
     for (int y = 0; y < MI; ++y) sa_r[y] = lds_sa[wm * (MI * 32) + y * 32 + l32];
+    if (!BIAS) {
 #pragma unroll
-    for (int x = 0; x < NX; ++x)
+        for (int x = 0; x < NX; ++x)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int wl = wtile_row0<EPI>(wn, x) + q * 8 + khalf * 4;
-            sw_r[x][q] = *reinterpret_cast<const v4f *>(lds_sw + wl);
-            if (SW) swu_r[x & 1][q] = *reinterpret_cast<const v4f *>(lds_sw + 128 + wl);
-        }
+            for (int q = 0; q < 4; ++q) {
+                const int wl = wtile_row0<EPI>(wn, x) + q * 8 + khalf * 4;
+                sw_r[BIAS ? 0 : x][q] = *reinterpret_cast<const v4f *>(lds_sw + wl);
+                if (SW) swu_r[x & 1][q] = *reinterpret_cast<const v4f *>(lds_sw + 128 + wl);
+            }
+    }
 
 #pragma unroll
     for (int y = 0; y < MI; ++y) {
@@ -452,7 +499,7 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
             uint16_t *const obase = o.out + row0 * g.ldo + col0;   // uniform
 
             // 1. residual block -> region
-            if (EPI == SPG_EPI_ADD) {
+            if (EPI == SPG_EPI_ADD && !BIAS) {
                 const uint16_t *const rbase = o.res + row0 * g.ldr + col0;
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
@@ -481,7 +528,9 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
                 const int x = SW ? xx : p * 2 + xx;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const v4f sw = sw_r[x][q];
+                    const int wl = wtile_row0<EPI>(wn, x) + q * 8 + khalf * 4;
+                    const v4f sw = BIAS ? *reinterpret_cast<const v4f *>(lds_sw + wl) : sw_r[BIAS ? 0 : x][q];
+                    const v4f bias = BIAS ? *reinterpret_cast<const v4f *>(bias_w + (wl - wn * 128)) : v4f{};
                     const v4f swu = SW ? swu_r[x & 1][q] : v4f{};
                     uint2 *dst = reinterpret_cast<uint2 *>(region + l32 * 128 + phys(l32, xx * 4 + q) * 16 + khalf * 8);
                     float v[4];
@@ -496,7 +545,10 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
                             v[j] = acc[x][y][e] * sa * sw[j];
                         }
                     }
-                    if (EPI == SPG_EPI_ADD) {
+                    if (BIAS) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) v[j] += bias[j];
+                    } else if (EPI == SPG_EPI_ADD) {
                         const uint2 rv = *dst;
                         v[0] += bf16_lo(rv.x);
                         v[1] += bf16_hi(rv.x);
@@ -538,22 +590,33 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
 }
 
 // Fused epilogue of the whole tile (no split).  GIVEN, wave_in: as for
-// epilogue_impl.
+// epilogue_impl.  lds_bias: bias_words<EPI>() floats of LDS, 128 per wave,
+// used by nothing else (ADD with a bias row; untouched otherwise).
 template <int EPI, int MI = 4, bool GIVEN = false>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
-                                         const float *lds_sw, uint8_t *region, int wave_in = 0)
+                                         const float *lds_sw, float *lds_bias, uint8_t *region, int wave_in = 0)
 {
     constexpr bool SW = EPI == SPG_EPI_SWIGLU;
     const int wave = GIVEN ? wave_in : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave >> 1, wn = wave & 1;
     const EpiOut o = epi_out<EPI>(g, T);
+    const bool brow = EPI == SPG_EPI_ADD && g.bias_mode != 0;
     const bool full = T.m0 + wm * (MI * 32) + MI * 32 <= g.M && T.c0 + (SW ? wn * 64 + 64 : wn * 128 + 128) <= o.nvalid &&
                       (((uintptr_t)o.out) & 15) == 0 && (g.ldo & 7) == 0 &&
-                      (EPI != SPG_EPI_ADD || ((((uintptr_t)o.res) & 15) == 0 && (g.ldr & 7) == 0));
+                      (EPI != SPG_EPI_ADD || brow || ((((uintptr_t)o.res) & 15) == 0 && (g.ldr & 7) == 0));
+    if constexpr (EPI == SPG_EPI_ADD) {
+        if (brow) {
+            if (full)
+                epilogue_impl<EPI, true, MI, GIVEN, true>(g, T, acc, lds_sa, lds_sw, lds_bias, region, wave_in);
+            else
+                epilogue_impl<EPI, false, MI, GIVEN, true>(g, T, acc, lds_sa, lds_sw, lds_bias, region, wave_in);
+            return;
+        }
+    }
     if (full)
-        epilogue_impl<EPI, true, MI, GIVEN>(g, T, acc, lds_sa, lds_sw, region, wave_in);
+        epilogue_impl<EPI, true, MI, GIVEN>(g, T, acc, lds_sa, lds_sw, lds_bias, region, wave_in);
     else
-        epilogue_impl<EPI, false, MI, GIVEN>(g, T, acc, lds_sa, lds_sw, region, wave_in);
+        epilogue_impl<EPI, false, MI, GIVEN>(g, T, acc, lds_sa, lds_sw, lds_bias, region, wave_in);
 }
 
 }  // namespace gemm

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
     constexpr bool kScaleDma = !SPLIT && EPI == SPG_EPI_SWIGLU && SMODE == SPG_FMT_E4M3_ROW;
     constexpr int kScaleBufs = kScaleDma ? 3 : 2;
     __shared__ __attribute__((aligned(16))) float lds_scale[kScaleBufs][2][kBM];   // [buffer][a / w][row]
+    __shared__ __attribute__((aligned(16))) float lds_bias[bias_words<EPI>()];
     clock_mark(g.clocks, 0);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
             // flight (measured: 1-2% of the 4096 x 34816 x 5120 product).  The
             // other epilogues measured slightly faster re-deriving it.
             const int sb = kScaleDma ? i % 3 : i & 1;
-            epilogue<EPI, 4, EPI == SPG_EPI_SWIGLU>(g, Tc, acc, lds_scale[sb][0], lds_scale[sb][1],
+            epilogue<EPI, 4, EPI == SPG_EPI_SWIGLU>(g, Tc, acc, lds_scale[sb][0], lds_scale[sb][1], lds_bias,
                                                    &lds[2 * kSlot + wave * (kEpiRegionBytes / 4)], wave);
         }
         if (i + 1 < ntile) {
@@ -447,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
     __shared__ __attribute__((aligned(2048))) uint8_t lds[kSlotsH * kSlotH];
     __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
     __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+    __shared__ __attribute__((aligned(16))) float lds_bias[bias_words<EPI>()];
     clock_mark(g.clocks, 0);
 
     const int tid = threadIdx.x;
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
     lds_sa[tid] = va;
     lds_sw[tid] = vw;
     block_barrier();
-    epilogue<EPI, 2>(g, T, acc, lds_sa, lds_sw, &lds[wave * (kEpiRegionBytes / 4)]);
+    epilogue<EPI, 2>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[wave * (kEpiRegionBytes / 4)]);
     clock_mark(g.clocks, 1);
 }
 

@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const G
     auto lds_ab = [&](int st, int op) -> uint8_t * { return &lds[(st * 2 + op) * kStageBytes]; };
     __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
     __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+    __shared__ __attribute__((aligned(16))) float lds_bias[bias_words<EPI>()];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const G
         splitk_store(g, T, split, acc);   // the slices are summed by splitk_reduce_kernel
         return;
     }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
+    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
 }
 
 // Decode for the fast path, with the hardware conversions.  Every E4M3
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlotF];
     __shared__ __attribute__((aligned(16))) float lds_sa[kBM];
     __shared__ __attribute__((aligned(16))) float lds_sw[kBN];
+    __shared__ __attribute__((aligned(16))) float lds_bias[bias_words<EPI>()];
     clock_mark(g.clocks, 0);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
         clock_mark(g.clocks, 1);
         return;
     }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, &lds[(threadIdx.x >> 6) * 4096]);   // slots free after the barrier
+    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 4096]);   // slots free after the barrier
     clock_mark(g.clocks, 1);
 }
 

@@ -37,6 +37,8 @@ def test_valid_call_reaches_the_device_check():
         call(row_args(epilogue="add", residual=t((N,), torch.bfloat16)))
     with pytest.raises(ValueError, match="CUDA"):
         call(row_args(epilogue="swiglu", out=t((M, N // 2), torch.bfloat16)))
+    with pytest.raises(ValueError, match="CUDA"):
+        call(row_args(epilogue="add", residual=t((N,), torch.uint8), bias_scale=t((1,), torch.float32)))
 
 
 @pytest.mark.parametrize("case,match", [
@@ -56,6 +58,11 @@ def test_valid_call_reaches_the_device_check():
     ("other_device", "must be on meta"),
     ("a_strided", "rows of A and W"),
     ("k_mismatch", "disagree on K"),
+    ("bias_scale_for_store", "bias scale is taken only by the add"),
+    ("bias_scale_with_bf16_row", "E4M3 codes"),
+    ("bias_scale_with_matrix", "E4M3 codes"),
+    ("bias_scale_two_values", "bias_scale must be one fp32 value"),
+    ("codes_without_bias_scale", "residual must be bf16"),
 ])
 def test_bad_calls_raise_before_the_library(case, match):
     a = row_args()
@@ -95,5 +102,15 @@ def test_bad_calls_raise_before_the_library(case, match):
         a["A"] = t((K, M), torch.uint8).t()
     elif case == "k_mismatch":
         a["W"] = t((N, K + 16), torch.uint8)
+    elif case == "bias_scale_for_store":
+        a.update(bias_scale=t((1,), torch.float32))
+    elif case == "bias_scale_with_bf16_row":
+        a.update(epilogue="add", residual=t((N,), torch.bfloat16), bias_scale=t((1,), torch.float32))
+    elif case == "bias_scale_with_matrix":
+        a.update(epilogue="add", residual=t((M, N), torch.uint8), bias_scale=t((1,), torch.float32))
+    elif case == "bias_scale_two_values":
+        a.update(epilogue="add", residual=t((N,), torch.uint8), bias_scale=t((2,), torch.float32))
+    elif case == "codes_without_bias_scale":
+        a.update(epilogue="add", residual=t((N,), torch.uint8))
     with pytest.raises(ValueError, match=match):
         call(a)

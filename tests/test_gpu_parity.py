@@ -673,10 +673,12 @@ def test_gemm_tail_split_sampled(spg, fmt, K):
     (3900, 8704, 1024, "swiglu", "e4m3_row", 1),
     (2048, 4352, 1024, "store", "e4m3_tensor", 2),
     (4000, 4312, 1040, "bias", "e4m3_row", 1),
-], ids=["store", "add_ragged", "swiglu_ragged", "tensor_batch2", "bias_ragged"])
+    (4000, 4312, 1040, "bias8", "e4m3_row", 1),
+], ids=["store", "add_ragged", "swiglu_ragged", "tensor_batch2", "bias_ragged", "e4m3_bias_ragged"])
 def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
+    bias8 = epi == "bias8"      # ADD with an E4M3 bias row and its scale
     bias = epi == "bias"        # ADD with one bf16 row broadcast to every token row
-    epi = "add" if bias else epi
+    epi = "add" if (bias or bias8) else epi
     plan = spg.gemm_plan(M, N, K, fmt, epi, batch=B)
     assert plan["tail_bm"] == 128 and plan["tail_tiles"] in (16, 32) and plan["tail_split"] == 1
     rng = np.random.default_rng(M + N + K)
@@ -685,14 +687,18 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
     n_out = N // 2 if epi == "swiglu" else N
     R16 = bf16_normal((M, n_out), 1.0, 82) if epi == "add" else None
     res = dev(R16) if R16 is not None else None
+    bscale, bvals = None, None
     if bias:
         row = bf16_normal((n_out,), 1.0, 83)
         R16, res = np.broadcast_to(row, (M, n_out)), dev(row)
+    if bias8:
+        res, bscale, bvals = e4m3_bias(spg, bf16_normal((n_out,), 1.0, 84))
+        R16 = None
     A, W = dev(A16), dev(W16)
     if fmt == "e4m3_row":
         qa, sa = spg.quantize_rowwise(A)
         qw, sw = spg.quantize_rowwise(W)
-        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res, bias_scale=bscale)
     else:
         qa, sa = spg.quantize_tensor(A)
         qw, sw = spg.quantize_tensor(W)
@@ -724,7 +730,7 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
             qa_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(Ab[rows]), sa_o)
             qw_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(W16[wrows]), sw_o)
         D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
-        y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, Rs)
+        y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, Rs, None if bvals is None else bvals[cols])
         check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"half tail {M}x{N}x{K} {epi} {fmt} batch {b}")
 
 
@@ -785,6 +791,94 @@ def test_gemm_bias_row_with_zero_weights_is_the_bias(spg):
         row = bf16_normal((N,), 1.0, 8)
         gpu = run_fp8(spg, A16, np.zeros((N, K), np.uint16), "add", "e4m3_row", row)
         assert np.array_equal(gpu, np.tile(row, (M, 1))), (M, N, K)
+
+
+# ---------------------------------------------------------------------------
+# FP8 bias: the bias row stored as E4M3 codes with one fp32 scale (made by
+# the row quantizer from a bf16 row), dequantized in the epilogue after the
+# operand scales (AstrAI commit log, the commit fusing the bias).  The same
+# routes as the bf16 bias row: 256- and 128-row tiles, persistent
+# workgroups, split-K and its reduction, per-tensor batches, NVFP4.
+# ---------------------------------------------------------------------------
+
+def e4m3_bias(spg, row16):
+    """(codes uint8 [N], scale fp32 [1]) on the device, and the oracle's
+    dequantized values for the same row (the codes checked equal).  The
+    device quantizer takes rows of a multiple of 16 values: the row is
+    padded with zeros, which leave its amax, scale and codes unchanged."""
+    n = row16.shape[0]
+    padded = np.zeros((1, (n + 15) // 16 * 16), np.uint16)
+    padded[0, :n] = row16
+    q, s = spg.quantize_rowwise(dev(padded))
+    q_o, s_o = oracle.quantize_rowwise(row16[None, :])
+    assert np.array_equal(q.cpu().numpy()[:, :n], q_o) and s.cpu().numpy()[0] == s_o[0]
+    return q[0, :n].contiguous(), s, oracle.bias_e4m3(q_o[0], s_o[0])
+
+
+@pytest.mark.parametrize("shape,fmt,B", BIAS, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_gemm_e4m3_bias_row(spg, shape, fmt, B):
+    M, N, K = shape
+    A16 = bf16_normal((B, M, K) if B > 1 else (M, K), 1.0, 190 + M)
+    W16 = bf16_normal((N, K), 0.02, 191 + N)
+    row = bf16_normal((N,), 0.5, 192 + K)
+    codes, bscale, bvals = e4m3_bias(spg, row)
+    A, W = dev(A16), dev(W16)
+    if fmt == "nvfp4":
+        qa, bsa, ta = spg.quantize_block16(A)
+        qw, bsw, tw = spg.quantize_block16(W)
+        out = spg.gemm_scaled(qa, bsa, qw, bsw, "add", residual=codes, fmt="nvfp4", tscale_a=ta, tscale_w=tw,
+                              bias_scale=bscale)
+    elif fmt == "e4m3_row":
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, "add", residual=codes, bias_scale=bscale)
+    else:
+        qa, sa = spg.quantize_tensor(A)
+        qw, sw = spg.quantize_tensor(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, "add", residual=codes, fmt="e4m3_tensor", bias_scale=bscale)
+    gpu = host_u16(out)
+    for b in range(B):
+        Ab = A16[b] if B > 1 else A16
+        if fmt == "nvfp4":
+            qa_o, bsa_o, ta_o = oracle.quantize_block16(Ab)
+            qw_o, bsw_o, tw_o = oracle.quantize_block16(W16)
+            D, Da = oracle.gemm_nvfp4_sums(qa_o, bsa_o, qw_o, bsw_o)
+            y, S, _ = oracle.epilogue("add", D, Da, ta_o, tw_o, bias=bvals)
+        else:
+            if fmt == "e4m3_row":
+                qa_o, sa_o = oracle.quantize_rowwise(Ab)
+                qw_o, sw_o = oracle.quantize_rowwise(W16)
+            else:
+                qa_o, sa_o = oracle.quantize_tensor(Ab)
+                qw_o, sw_o = oracle.quantize_tensor(W16)
+                sa_o, sw_o = sa_o[0], sw_o[0]
+            D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+            y, S, _ = oracle.epilogue("add", D, Da, sa_o, sw_o, bias=bvals)
+        check_close(gpu[b] if B > 1 else gpu, y, S, f"e4m3 bias {shape} {fmt} batch {b}")
+
+
+def test_gemm_e4m3_bias_with_zero_weights_is_the_bias(spg):
+    # zero weights: every row is the dequantized bias.  With a power-of-two
+    # bias scale dec(code) * scale is exact in fp32, so the output is the
+    # oracle's one rounding bit for bit - also through a 128-row tile
+    # product, the persistent kernel and split-K with its reduction
+    rng = np.random.default_rng(5)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    for M, N, K in [(300, 260, 256), (2304, 520, 128), (16, 520, 8192)]:
+        A16 = bf16_normal((M, K), 1.0, 9)
+        codes = rng.choice(finite, size=(N,)).astype(np.uint8)
+        scale = np.float32(2.0 ** -7)
+        A = dev(A16)
+        qa, sa = spg.quantize_rowwise(A)
+        qw = torch.zeros((N, K), dtype=torch.uint8, device="cuda")
+        sw = torch.ones((N,), dtype=torch.float32, device="cuda")
+        out = spg.gemm_scaled(qa, sa, qw, sw, "add", residual=torch.from_numpy(codes).cuda(),
+                              bias_scale=torch.tensor([scale], device="cuda"))
+        gpu = host_u16(out)
+        # the oracle's epilogue on zero sums (a -0 bias gives +0 after the add)
+        _, _, want = oracle.epilogue("add", np.zeros((1, N)), np.zeros((1, N)), 1.0, 1.0,
+                                     bias=oracle.bias_e4m3(codes, scale))
+        assert np.array_equal(gpu, np.tile(want, (M, 1))), (M, N, K)
 
 
 # ---------------------------------------------------------------------------

@@ -94,7 +94,8 @@ def test_desc_init_defaults(spg):
     "ldo_short", "swiglu_odd_n", "add_without_residual", "store_with_residual", "null_a", "misaligned_a",
     "negative_m", "zero_batch", "nvfp4_no_tscale", "negative_stride", "ldr_short", "bias_row_in_place",
     "in_place_other_ldr", "in_place_other_batch_stride", "residual_overlaps_out", "bias_row_inside_out",
-    "output_batches_overlap", "output_broadcast",
+    "output_batches_overlap", "output_broadcast", "bias_scale_with_store", "bias_scale_with_matrix_residual",
+    "bias_scale_misaligned", "bias_scale_inside_out", "e4m3_bias_row_inside_out",
 ])
 def test_gemm_validation_errors(spg, case):
     d = desc(spg, 64, 64, 64, 0)
@@ -155,6 +156,17 @@ def test_gemm_validation_errors(spg, case):
         d.batch, d.stride_a, d.stride_o = 2, 64 * 64, 64 * 63
     elif case == "output_broadcast":
         d.batch, d.stride_a, d.stride_o = 2, 64 * 64, 0
+    elif case == "bias_scale_with_store":
+        d.bias_scale = FAKE2.value
+    elif case == "bias_scale_with_matrix_residual":
+        # an E4M3 bias is one row (ldr == 0), never a residual matrix
+        epi, kw["res"], d.bias_scale = 1, FAKE2, FAKE2.value + 4096
+    elif case == "bias_scale_misaligned":
+        epi, d.ldr, kw["res"], d.bias_scale = 1, 0, FAKE2, FAKE2.value + 4098
+    elif case == "bias_scale_inside_out":
+        epi, d.ldr, kw["res"], d.bias_scale = 1, 0, FAKE2, FAKE.value + 256
+    elif case == "e4m3_bias_row_inside_out":
+        epi, d.ldr, kw["res"], d.bias_scale = 1, 0, P(FAKE.value + 2 * 64 * 63 + 1), FAKE2.value
     assert call_gemm(spg, d, epi, **kw) == EINVAL
 
 
@@ -176,6 +188,21 @@ def test_gemm_bias_row_is_a_valid_residual(spg):
     p = spg.Plan()
     assert spg.lib.spg_gemm_plan(ctypes.byref(d), 1, 256, ctypes.byref(p)) == 0
     assert spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), 1) == 0
+
+
+def test_gemm_e4m3_bias_row_passes_validation(spg):
+    # E4M3 bias codes are single bytes: any address outside the output, even
+    # an odd one, with a 4-byte aligned scale outside the output, gets past
+    # validation (SPG_EHIP without a device, never SPG_EINVAL); the byte just
+    # past the output's last element is outside it
+    d = desc(spg, 64, 64, 64, 0)
+    d.ldr, d.bias_scale = 0, FAKE2.value
+    assert call_gemm(spg, d, 1, res=P(FAKE2.value + 4097)) != EINVAL
+    assert call_gemm(spg, d, 1, res=P(FAKE.value + 2 * 64 * 64)) != EINVAL
+    d.bias_scale = FAKE.value + 2 * 64 * 64
+    assert call_gemm(spg, d, 1, res=FAKE2) != EINVAL
+    p = spg.Plan()
+    assert spg.lib.spg_gemm_plan(ctypes.byref(d), 1, 256, ctypes.byref(p)) == 0
 
 
 def test_gemm_nvfp4_batch_unsupported(spg):
