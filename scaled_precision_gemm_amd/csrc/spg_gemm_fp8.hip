@@ -437,6 +437,7 @@ constexpr int kHalfRows = 128;                     // A rows of a half tile
 constexpr int kOpAh = kHalfRows * kBK;             // A bytes of one stage: 16 KiB
 constexpr int kSlotH = kOpAh + kOp;                // A + W of one stage: 48 KiB
 constexpr int kSlotsH = 3;
+static_assert(4 * 16384 <= kSlotsH * kSlotH, "the epilogue's staged regions fit in the freed slots");
 
 struct FragsH {
     uint4 a[2][2], b[4][2];
@@ -614,7 +615,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
     lds_sa[tid] = va;
     lds_sw[tid] = vw;
     block_barrier();
-    epilogue<EPI, 2>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[wave * (kEpiRegionBytes / 4)]);
+    // 16 KiB per wave of the freed slots: one region per pass
+    epilogue<EPI, 2, false, true>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[wave * 16384]);
     clock_mark(g.clocks, 1);
 }
 

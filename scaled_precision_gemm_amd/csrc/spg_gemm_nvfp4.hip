@@ -185,6 +185,16 @@ __device__ __forceinline__ h2 scale_pair(uint32_t word, uint32_t sel)
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(word, word, sel), 1.0f, false);
 }
 
+// Pairs 2 H and 2 H + 1 of decode8_cvt: half of a fragment's decode, so that
+// the decode of the next k-step spreads evenly over the MFMAs of this one.
+template <int H>
+__device__ __forceinline__ uint2 decode4_cvt(uint32_t w, h2 s)
+{
+    const h2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0.0078125f, 2 * H) * s;
+    const h2 r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0.0078125f, 2 * H + 1) * s;
+    return make_uint2(__builtin_bit_cast(uint32_t, r0), __builtin_bit_cast(uint32_t, r1));
+}
+
 __device__ __forceinline__ uint4 decode8_cvt(uint32_t w, h2 s)
 {
     const h2 r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 0.0078125f, 0) * s;
@@ -218,6 +228,7 @@ constexpr int kBKF = 256;                       // K elements per stage
 constexpr int kCodeOp = kBM * 128;              // code bytes per operand per stage: 32 KiB
 constexpr int kScaleOp = kBM * 16;              // scale bytes per operand per stage: 4 KiB
 constexpr int kSlotF = 2 * (kCodeOp + kScaleOp);   // [A codes][W codes][A scales][W scales]
+static_assert(4 * 32768 <= 2 * kSlotF, "the epilogue's staged regions fit in the freed slots");
 
 // AM: A blocks per wave that take part (4 in general).  Products of at most
 // 32 (64) tokens have only their first 32 (64) tile rows, so AM = 1 (2)
@@ -325,10 +336,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
     // decode and LDS work of the next k-step slotted between the MFMAs of the
     // current one (one wave per SIMD: the MFMA pipe idles whenever the wave
     // stops to wait for LDS or to decode):
-    //   k-step (c, 0): after MFMA j (j even) decode fragment j/2 of (c, 1);
-    //                  after MFMA 1 read chunk c + 1's codes; after MFMA j
-    //                  (j odd) prepare one block scale of chunk c + 1
-    //   k-step (c, 1): after MFMA j decode fragment j/2 of (c + 1, 0)
+    //   k-step (c, 0): after MFMA j decode half j % 2 of fragment j/2 of
+    //                  (c, 1); after MFMA 1 read chunk c + 1's codes; after
+    //                  MFMA j (j odd) prepare one block scale of chunk c + 1
+    //   k-step (c, 1): after MFMA j decode half j % 2 of fragment j/2 of
+    //                  (c + 1, 0)
+    // Four VALU instructions follow every MFMA.  (Whole fragments after the
+    // even MFMAs only - eight, then none - measured 10.7K cycles per stage
+    // against 9.7K: the MFMA waits whenever the instructions between two of
+    // them outlast its 32 cycles.)
     // Fragments 0..3 are the A blocks y, 4..7 the W blocks x.
     auto compute = [&](int slot) {
         const uint8_t *base = &lds[slot * kSlotF];
@@ -375,18 +391,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
                         acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fr[fc][4 + x]),
                                                                          __builtin_bit_cast(v8h, fr[fc][y]), acc[x][y],
                                                                          0, 0, 0);
-                    const int f = j >> 1;
+                    // half h of the next k-step's fragment f after MFMA
+                    // 2 f + h: four VALU instructions in every MFMA slot
+                    const int f = j >> 1, h = j & 1;
+                    auto half_decode = [&](uint32_t w, h2 sv) {
+                        if (h == 0) {
+                            const uint2 r = decode4_cvt<0>(w, sv);
+                            fr[fn][f].x = r.x;
+                            fr[fn][f].y = r.y;
+                        } else {
+                            const uint2 r = decode4_cvt<1>(w, sv);
+                            fr[fn][f].z = r.x;
+                            fr[fn][f].w = r.y;
+                        }
+                    };
                     if (d == 0) {
-                        if ((j & 1) == 0 && live(f)) fr[fn][f] = decode8_cvt(code[cb][f].y, bs[cb][f]);
+                        if (live(f)) half_decode(code[cb][f].y, bs[cb][f]);
                         if (j == 1 && c + 1 < 8) {
 #pragma unroll
                             for (int ff = 0; ff < 8; ++ff)
                                 if (live(ff)) code[nb][ff] = read_code(c + 1, ff);
                         }
-                        if ((j & 1) == 1 && c + 1 < 8 && live(f)) bs[nb][f] = scale_of(c + 1, f);
+                        if (h == 1 && c + 1 < 8 && live(f)) bs[nb][f] = scale_of(c + 1, f);
                     } else if (c + 1 < 8) {
                         if (j == 0) wait_lds();
-                        if ((j & 1) == 0 && live(f)) fr[fn][f] = decode8_cvt(code[nb][f].x, bs[nb][f]);
+                        if (live(f)) half_decode(code[nb][f].x, bs[nb][f]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -416,7 +445,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
         clock_mark(g.clocks, 1);
         return;
     }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 4096]);   // slots free after the barrier
+    // slots free after the barrier: 32 KiB per wave, one region per pass
+    epilogue<EPI, 4, false, true>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 32768]);
     clock_mark(g.clocks, 1);
 }
 
