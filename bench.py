@@ -449,6 +449,8 @@ def main():
         sa = torch.empty((wl.M,), dtype=torch.float32, device="cuda")
     out = torch.empty((wl.batch, wl.M, wl.n_out) if wl.batch > 1 else (wl.M, wl.n_out),
                       dtype=torch.bfloat16, device="cuda")
+    # a split-N output (fused input projections): one tensor per column segment
+    segs = [torch.empty((wl.M, w), dtype=torch.bfloat16, device="cuda") for w in wl.split] if wl.split else None
     ws = None
 
     def step(i, cp=None):
@@ -458,7 +460,8 @@ def main():
         if wl.fmt == "e4m3_row":
             spg.quantize_rowwise(A, out=qa, scale=sa)
             ev[i][1].record()
-            spg.gemm_scaled(qa, sa, w[0], w[1], wl.epilogue, residual=R, out=out, workspace=ws, clock_probe=cp)
+            spg.gemm_scaled(qa, sa, w[0], w[1], wl.epilogue, residual=R, out=None if segs else out,
+                            workspace=ws, clock_probe=cp, out_split=segs)
         elif wl.fmt == "e4m3_tensor":
             q, s = spg.quantize_tensor(A)
             ev[i][1].record()
@@ -588,6 +591,7 @@ def main():
         "config": {
             "workload": wl.name, "format": wl.fmt, "epilogue": "add (bf16 bias row)" if wl.bias else wl.epilogue,
             "M": wl.M, "N": wl.N, "K": wl.K, "batch": wl.batch,
+            **({"out_split": list(wl.split)} if wl.split else {}),
             "step": "activation quantize + gemm_scaled (weights pre-quantized)",
             "buffer_sets": sets, "plan": plan,
         },

@@ -177,6 +177,33 @@ int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q,
 /* ------------------------------------------------------------------------ */
 
 /*
+ * Output split along N (split-N epilogue): the output columns of one product
+ * go to up to SPG_MAX_OUT_SPLITS separate matrices, one per column range -
+ * the fused input projections (q | k | v ...) that ninfer PR #167 lists
+ * among the GEMM's call sites (attn_input_proj, gdn_input_proj) computed as
+ * one GEMM over the row-concatenated weights.  Segment s holds output
+ * columns [col_end[s-1], col_end[s]) (col_end[-1] = 0) as a bf16 matrix with
+ * row stride ldo[s] and batch stride stride_o[s] (elements).
+ *   count        : 1 .. SPG_MAX_OUT_SPLITS
+ *   col_end      : strictly increasing; every end but the last a multiple of
+ *                  64; the last equals the output width (N, N/2 for SWIGLU)
+ *   out[s]       : device, 16-byte aligned, ldo[s] a multiple of 8 with
+ *                  ldo[s] >= the segment's width and < 2^26; with batch > 1,
+ *                  stride_o[s] >= (M - 1) * ldo[s] + width
+ *   No two segments, and no segment and a residual or bias, may overlap.
+ * Anything else: SPG_EINVAL.  The values are those of the unsplit output.
+ */
+#define SPG_MAX_OUT_SPLITS 8
+typedef struct spg_out_split {
+    int32_t count;
+    int32_t reserved;
+    int64_t col_end[SPG_MAX_OUT_SPLITS];
+    void *out[SPG_MAX_OUT_SPLITS];
+    int64_t ldo[SPG_MAX_OUT_SPLITS];
+    int64_t stride_o[SPG_MAX_OUT_SPLITS];
+} spg_out_split;
+
+/*
  * Shape and layout of one gemm_scaled call.  Initialise with
  * spg_gemm_desc_init() so unused fields are zero and optional pointers NULL
  * (AstrAI: default-initialised parameter structs never carry garbage).
@@ -215,6 +242,10 @@ int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q,
  *              the GEMM epilogue: a null bias scale means a bf16 bias, a
  *              non-null one FP8 storage dequantized in the epilogue).  Set
  *              with any other epilogue or with ldr != 0: SPG_EINVAL.
+ *   out_split : optional (NULL by default), host memory read during the
+ *              call: the output as column segments (spg_out_split above).
+ *              When set, gemm_scaled's `out` must be NULL and ldo, stride_o
+ *              are not used.
  */
 typedef struct spg_gemm_desc {
     int64_t M, N, K, batch;
@@ -226,6 +257,7 @@ typedef struct spg_gemm_desc {
     const float *tscale_w;
     uint64_t *clock_probe;
     const float *bias_scale;
+    const spg_out_split *out_split;
 } spg_gemm_desc;
 
 /* Zero every field, set batch = 1 and the dense strides for M, N, K. */
@@ -233,7 +265,8 @@ void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32
 
 /*
  * gemm_scaled - out = epilogue(scale * (A W^T)), fp32 accumulation.
- *   out      : bf16 [M, N] (STORE, ADD) or [M, N/2] (SWIGLU)
+ *   out      : bf16 [M, N] (STORE, ADD) or [M, N/2] (SWIGLU); NULL when
+ *              d->out_split gives the output as column segments
  *   A, W     : codes as described by d->format
  *   sa, sw   : E4M3_ROW: fp32 [M] and fp32 [N] (per batch entry: + b*M, b*N
  *              unless that operand's batch stride is 0);

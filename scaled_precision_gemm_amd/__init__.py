@@ -39,6 +39,17 @@ class SpgError(RuntimeError):
         self.status = status
 
 
+MAX_OUT_SPLITS = 8
+
+
+class OutSplit(ctypes.Structure):
+    _fields_ = [
+        ("count", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("col_end", ctypes.c_int64 * MAX_OUT_SPLITS), ("out", ctypes.c_void_p * MAX_OUT_SPLITS),
+        ("ldo", ctypes.c_int64 * MAX_OUT_SPLITS), ("stride_o", ctypes.c_int64 * MAX_OUT_SPLITS),
+    ]
+
+
 class GemmDesc(ctypes.Structure):
     _fields_ = [
         ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("batch", ctypes.c_int64),
@@ -48,6 +59,7 @@ class GemmDesc(ctypes.Structure):
         ("format", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
         ("tscale_a", ctypes.c_void_p), ("tscale_w", ctypes.c_void_p),
         ("clock_probe", ctypes.c_void_p), ("bias_scale", ctypes.c_void_p),
+        ("out_split", ctypes.POINTER(OutSplit)),
     ]
 
 
@@ -230,8 +242,29 @@ def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residua
     return d, epi, batched
 
 
+def check_out_split(segs, M, n_out, batch, batched, dev):
+    """The segments of a split output: bf16 tensors [M, w] ([B, M, w] when
+    batched), rows contiguous, 16-byte aligned with a row stride that is a
+    multiple of 8, widths adding up to the output width with every boundary
+    but the last a multiple of 64."""
+    _need(isinstance(segs, (list, tuple)) and 1 <= len(segs) <= MAX_OUT_SPLITS,
+          f"out_split takes 1 to {MAX_OUT_SPLITS} output tensors")
+    end = 0
+    for i, t in enumerate(segs):
+        _need(isinstance(t, torch.Tensor) and t.device == dev and t.dtype == torch.bfloat16,
+              f"output segment {i} must be a bf16 tensor on {dev}")
+        _need(t.dim() == (3 if batched else 2), f"output segment {i} must be {'3' if batched else '2'}-D")
+        _need(t.shape[-2] == M and (not batched or t.shape[0] == batch), f"output segment {i} has the wrong rows")
+        _need(t.stride(-1) == 1 and t.stride(-2) % 8 == 0 and t.data_ptr() % 16 == 0,
+              f"output segment {i}: contiguous rows, 16-byte aligned, row stride a multiple of 8")
+        end += t.shape[-1]
+        _need(t.shape[-1] > 0 and (i + 1 == len(segs) or end % 64 == 0),
+              "every output segment boundary but the last must be a multiple of 64 columns")
+    _need(end == n_out, f"the output segments must add up to {n_out} columns")
+
+
 def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_a=None, tscale_w=None,
-                   scale_layout="row", bias_scale=None):
+                   scale_layout="row", bias_scale=None, out_split=None):
     """Shapes, dtypes, strides and devices of a gemm_scaled call, checked
     before anything reaches the library (raises ValueError).  The library
     trusts the sizes it is given, so an output, residual or scale tensor
@@ -282,6 +315,16 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
         _need(out.dtype == torch.bfloat16, "out must be bf16")
         _need(tuple(out.shape) == want, f"out must have shape {want}")
         _need(out.stride(-1) == 1, "rows of out must be contiguous")
+    if out_split is not None:
+        _need(out is None, "out and out_split are exclusive")
+        segs = list(out_split)
+        if segs and all(isinstance(w, int) for w in segs):
+            _need(len(segs) <= MAX_OUT_SPLITS and all(w > 0 for w in segs) and sum(segs) == n_out,
+                  f"out_split widths: 1 to {MAX_OUT_SPLITS} positive widths adding up to {n_out}")
+            _need(all(sum(segs[:i + 1]) % 64 == 0 for i in range(len(segs) - 1)),
+                  "every output segment boundary but the last must be a multiple of 64 columns")
+        else:
+            check_out_split(segs, M, n_out, batch, batched, dev)
     if bias_scale is not None:
         # an E4M3 bias row: uint8 codes [N], one fp32 scale
         _need(epi == EPI_ADD, "a bias scale is taken only by the add epilogue")
@@ -302,7 +345,7 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
 
 def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
                 out=None, tscale_a=None, tscale_w=None, workspace=None, clock_probe=None, scale_layout="row",
-                bias_scale=None):
+                bias_scale=None, out_split=None):
     """out = epilogue(scale * A W^T) in bf16.
 
     e4m3_row: A uint8 [M,K], sa fp32 [M]; W uint8 [N,K], sw fp32 [N]
@@ -318,10 +361,32 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
            residual of uint8 E4M3 codes [N], the bias added to every row is
            dec(code) * bias_scale (see spg_gemm_desc.bias_scale); without it
            a 1-D residual is a bf16 bias row
+    out_split: optional list of output column widths (ints) or of bf16
+           output tensors, one per column segment (see spg_out_split): the
+           output goes to them instead of one tensor, and they are returned
+           as a list (out must then be None)
     """
-    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale)
+    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale,
+                   out_split)
     _need(A.is_cuda, "operands must be CUDA tensors")
     d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w)
+    split = None
+    if out_split is not None:
+        segs = list(out_split)
+        if all(isinstance(w, int) for w in segs):
+            # row strides rounded up to 8 elements (the library's alignment rule)
+            segs = [torch.empty((d.batch, d.M, (w + 7) // 8 * 8) if batched else (d.M, (w + 7) // 8 * 8),
+                                dtype=torch.bfloat16, device=A.device)[..., :w] for w in segs]
+        split = OutSplit()
+        split.count = len(segs)
+        end = 0
+        for i, t in enumerate(segs):
+            end += t.shape[-1]
+            split.col_end[i] = end
+            split.out[i] = t.data_ptr()
+            split.ldo[i] = t.stride(-2)
+            split.stride_o[i] = t.stride(0) if batched else 0
+        d.out_split = ctypes.pointer(split)
     d.scale_layout = _LAYOUT.get(scale_layout, scale_layout)
     if clock_probe is not None:
         _need(clock_probe.dtype == torch.int64 and clock_probe.numel() == 4 and clock_probe.is_contiguous()
@@ -330,7 +395,7 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
     if bias_scale is not None:
         d.bias_scale = bias_scale.data_ptr()
     n_out = d.N // 2 if epi == EPI_SWIGLU else d.N
-    if out is None:
+    if out is None and split is None:
         shape = (d.batch, d.M, n_out) if batched else (d.M, n_out)
         out = torch.empty(shape, dtype=torch.bfloat16, device=A.device)
     nws = lib.gemm_scaled_workspace_bytes(ctypes.byref(d), epi)
@@ -340,7 +405,7 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
                            ctypes.byref(d), _ptr(workspace) if nws > 0 else None,
                            workspace.numel() if (workspace is not None and nws > 0) else 0, _stream(A)),
            "gemm_scaled")
-    return out
+    return segs if split is not None else out
 
 
 def gemm_workspace(A, W, fmt="e4m3_row", epilogue="store", out=None, residual=None):

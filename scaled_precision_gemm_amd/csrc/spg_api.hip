@@ -319,6 +319,35 @@ SPG_EXPORT size_t gemm_scaled_workspace_bytes(const spg_gemm_desc *d, int epilog
     return plan_workspace(&p);
 }
 
+// A bf16 output region [o0, o1): one matrix (or segment) of a call.
+struct Extent {
+    uintptr_t o0, o1;
+};
+
+// Checks of an output split (spg_out_split) against the call's shape; its
+// segments' extents go to ext[0 .. count).
+int validate_split(const spg_out_split *sp, const spg_gemm_desc *d, int64_t nout, Extent *ext)
+{
+    if (sp->count < 1 || sp->count > SPG_MAX_OUT_SPLITS) return SPG_EINVAL;
+    int64_t begin = 0;
+    for (int s = 0; s < sp->count; ++s) {
+        const int64_t end = sp->col_end[s], width = end - begin, ldo = sp->ldo[s], st = sp->stride_o[s];
+        if (width <= 0) return SPG_EINVAL;
+        if (s + 1 < sp->count ? (end % 64) != 0 : end != nout) return SPG_EINVAL;
+        if (s + 1 < sp->count && end / 64 > 0xFFFF) return SPG_EUNSUPPORTED;   // boundaries held in 16 bits
+        if (!sp->out[s] || !aligned16(sp->out[s]) || ldo < width || (ldo & 7) || st < 0) return SPG_EINVAL;
+        if (ldo >= (INT64_C(1) << 26)) return SPG_EUNSUPPORTED;
+        if (d->batch > 1 && st < (d->M - 1) * ldo + width) return SPG_EINVAL;
+        const uintptr_t o0 = (uintptr_t)sp->out[s];
+        ext[s] = Extent{o0, o0 + 2 * (uintptr_t)((d->batch - 1) * st + (d->M - 1) * ldo + width)};
+        begin = end;
+    }
+    for (int s = 0; s < sp->count; ++s)
+        for (int t = s + 1; t < sp->count; ++t)
+            if (ext[s].o0 < ext[t].o1 && ext[t].o0 < ext[s].o1) return SPG_EINVAL;
+    return SPG_OK;
+}
+
 SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void *W, const void *sw,
                            const void *residual, int epilogue, const spg_gemm_desc *d, void *ws,
                            size_t ws_bytes, void *stream)
@@ -327,13 +356,29 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     if (v != SPG_OK) return v;
     const int64_t nout = n_out_of(d, epilogue);
     if (d->M == 0 || nout == 0) return SPG_OK;
-    if (!out || !A || !W || !sa || !sw) return SPG_EINVAL;
-    if (!aligned2(out) || !aligned16(A) || !aligned16(W)) return SPG_EINVAL;
-    // batch entries of the output must not overlap (several entries would
-    // write the same elements concurrently)
-    if (d->batch > 1 && d->stride_o < (d->M - 1) * d->ldo + nout) return SPG_EINVAL;
-    const uintptr_t o0 = (uintptr_t)out;
-    const uintptr_t o1 = o0 + 2 * (uintptr_t)((d->batch - 1) * d->stride_o + (d->M - 1) * d->ldo + nout);
+    const spg_out_split *split = d->out_split;
+    if (!A || !W || !sa || !sw || (split ? out != nullptr : out == nullptr)) return SPG_EINVAL;
+    if (!aligned16(A) || !aligned16(W)) return SPG_EINVAL;
+    // the output's extents: one matrix, or one per segment
+    Extent ext[SPG_MAX_OUT_SPLITS];
+    int next = 1;
+    if (split) {
+        const int v2 = validate_split(split, d, nout, ext);
+        if (v2 != SPG_OK) return v2;
+        next = split->count;
+    } else {
+        if (!aligned2(out)) return SPG_EINVAL;
+        // batch entries of the output must not overlap (several entries
+        // would write the same elements concurrently)
+        if (d->batch > 1 && d->stride_o < (d->M - 1) * d->ldo + nout) return SPG_EINVAL;
+        ext[0].o0 = (uintptr_t)out;
+        ext[0].o1 = ext[0].o0 + 2 * (uintptr_t)((d->batch - 1) * d->stride_o + (d->M - 1) * d->ldo + nout);
+    }
+    auto overlaps_out = [&](uintptr_t a0, uintptr_t a1) {
+        for (int s = 0; s < next; ++s)
+            if (a0 < ext[s].o1 && ext[s].o0 < a1) return true;
+        return false;
+    };
     if (epilogue == SPG_EPI_ADD) {
         const bool codes = d->bias_scale != nullptr;   // E4M3 bias row: 1-byte elements
         if (!residual || (!codes && !aligned2(residual))) return SPG_EINVAL;
@@ -343,12 +388,12 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
         // (ldr == 0) inside the output - is rejected.
         const uintptr_t r0 = (uintptr_t)residual;
         const uintptr_t r1 = r0 + (codes ? 1 : 2) * (uintptr_t)((d->batch - 1) * d->stride_r + (d->M - 1) * d->ldr + nout);
-        const bool same = !codes && r0 == o0 && d->ldr == d->ldo && d->stride_r == d->stride_o;
-        if (r0 < o1 && o0 < r1 && !same) return SPG_EINVAL;
+        const bool same = !split && !codes && r0 == ext[0].o0 && d->ldr == d->ldo && d->stride_r == d->stride_o;
+        if (overlaps_out(r0, r1) && !same) return SPG_EINVAL;
         if (codes) {
             // read by every workgroup while others write the output
             const uintptr_t b0 = (uintptr_t)d->bias_scale;
-            if (!aligned4(d->bias_scale) || (b0 < o1 && o0 < b0 + 4)) return SPG_EINVAL;
+            if (!aligned4(d->bias_scale) || overlaps_out(b0, b0 + 4)) return SPG_EINVAL;
         }
     } else if (residual) {
         return SPG_EINVAL;
@@ -396,6 +441,23 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.scale_layout = d->format == SPG_FMT_NVFP4 ? d->scale_layout : SPG_SCALES_ROW_MAJOR;
     g.bias_mode = epilogue == SPG_EPI_ADD && d->ldr == 0 ? (d->bias_scale ? 2 : 1) : 0;
     g.bias_scale = d->bias_scale;
+    if (split) {
+        // segment 0 stands for the output in the alignment tests
+        g.out = split->out[0];
+        g.ldo = split->ldo[0];
+        g.stride_o = split->stride_o[0];
+        g.nseg = split->count;
+        int64_t begin = 0;
+        for (int s = 0; s < split->count; ++s) {
+            if (s + 1 < split->count)
+                g.seg_b[s >> 1] |= (uint32_t)(split->col_end[s] / 64) << (16 * (s & 1));
+            g.seg[s].out = (uint16_t *)split->out[s];
+            g.seg[s].ldo = split->ldo[s];
+            g.seg[s].stride = split->stride_o[s];
+            g.seg[s].begin = begin;
+            begin = split->col_end[s];
+        }
+    }
     g.split_k = p.split_k;
     const int64_t unit_k = p.bk;
     g.k_chunk = p.split_k > 1 ? cdiv(cdiv(d->K, p.split_k), unit_k) * unit_k : (d->K > 0 ? d->K : 1);

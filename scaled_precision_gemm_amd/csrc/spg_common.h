@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/spg.h"
@@ -124,7 +125,44 @@ struct GemmArgs {
     int32_t scale_layout;             // NVFP4 block-scale planes: SPG_SCALES_ROW_MAJOR or _BLOCKED
     int32_t bias_mode;                // ADD: 0 a residual matrix, 1 a bf16 bias row, 2 an E4M3 bias row
     const float *bias_scale;          // bias_mode 2: the bias row's fp32 scale
+    // Output column segments (spg_out_split); nseg == 0: the one output
+    // (out, ldo, stride_o).  Otherwise out / ldo hold segment 0 (every
+    // segment is 16-byte aligned with ldo a multiple of 8, which is all the
+    // alignment tests look at).  seg_b holds the segment boundaries in units
+    // of 64 columns, 16 bits each (boundary i in bits 16 (i % 2) of word
+    // i / 2).
+    int32_t nseg;
+    uint32_t seg_b[SPG_MAX_OUT_SPLITS / 2];
+    struct Seg {
+        uint16_t *out;
+        int64_t ldo, stride, begin;
+    } seg[SPG_MAX_OUT_SPLITS];
 };
+
+// Output element (b, row, col) of a split output (nseg > 0) and the row
+// stride of the segment holding it.  The segment's fields are loaded from the kernel-argument segment at an
+// offset computed from col: the compiler cannot hoist such loads out of a
+// persistent tile loop (read with constant indices, the whole table stayed
+// in ~60 scalar registers across the main loop: the row-scaled ADD kernel's
+// scalar spills grew from 194 to 282 and its tile by 7%), and unlike a
+// run-time index into the argument itself this does not copy the arguments
+// to scratch memory.  Every GEMM kernel takes one GemmArgs as its only
+// argument, so it starts the kernel-argument segment.
+__device__ __forceinline__ uint16_t *out_at(const GemmArgs &g, int64_t b, int64_t row, int64_t col, int64_t &ld)
+{
+    const uint32_t c64 = (uint32_t)(col >> 6);
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < SPG_MAX_OUT_SPLITS; ++i)
+        s += (i + 1 < g.nseg && c64 >= ((g.seg_b[i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) ? 1 : 0;
+    typedef const __attribute__((address_space(4))) GemmArgs::Seg *SegTable;
+    const SegTable tab = (SegTable)((const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr() +
+                                    offsetof(GemmArgs, seg));
+    uint16_t *const out = tab[s].out;
+    const int64_t l = tab[s].ldo, st = tab[s].stride, begin = tab[s].begin;
+    ld = l;
+    return out + (st ? b * st : 0) + row * l + (col - begin);
+}
 
 // Optional clock record of the main GEMM launch: thread 0 of workgroup 0
 // stores the shader-clock counter and the 100 MHz reference counter when the

@@ -335,7 +335,6 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
     const int64_t row = T.m0 + rl;
     if (row >= g.M) return;
     const float sa = lds_sa[rl];
-    uint16_t *orow = o.out + row * g.ldo;
     const uint16_t *rrow = EPI == SPG_EPI_ADD ? o.res + row * g.ldr : nullptr;
     const bool brow = EPI == SPG_EPI_ADD && g.bias_mode != 0;
 
@@ -392,11 +391,16 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
             v[3] += bf16_hi(rv[q].y);
         }
         const uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        if (col >= o.nvalid) continue;
+        int64_t ld;
+        uint16_t *const dst = g.nseg ? out_at(g, T.b, row, col, ld)   // a 4-column group never straddles segments
+                                     : o.out + row * g.ldo + col;
+        (void)ld;
         if (o.vec && col + 4 <= o.nvalid) {
-            *reinterpret_cast<uint2 *>(orow + col) = pk;
+            *reinterpret_cast<uint2 *>(dst) = pk;
         } else {
             const uint32_t w[2] = {pk.x, pk.y};
-            for (int j = 0; j < 4 && col + j < o.nvalid; ++j) orow[col + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+            for (int j = 0; j < 4 && col + j < o.nvalid; ++j) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
         }
     }
 }
@@ -440,7 +444,9 @@ constexpr int kEpiRegionBytes = 4 * 4096;   // per workgroup
 // MI: 32-row A blocks per wave (4; 2 in a half-height tile, whose waves
 // hold acc[x][0..1] and cover token rows wm * 64 .. wm * 64 + 63).
 // GIVEN: wave_in is the caller's wave index; otherwise it is derived here.
-template <int EPI, bool FULL, int MI = 4, bool GIVEN = false, bool BIAS = false, bool STAGED = false>
+// SPLITOUT: the output is column segments (g.nseg > 0), addressed per pass.
+template <int EPI, bool FULL, int MI = 4, bool GIVEN = false, bool BIAS = false, bool STAGED = false,
+          bool SPLITOUT = false>
 __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
                                               const float *lds_sw, float *lds_bias, uint8_t *region_base,
                                               int wave_in)
@@ -463,7 +469,7 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
     auto phys = [](int r, int c) -> int { return c ^ ((r >> 1) & 7); };
     const int rr = lane >> 3, rc = lane & 7;  // row-order lane position: 8 rows x 8 chunks
     // 32-bit element offsets inside a 32-row block (ldo, ldr < 2^26)
-    const uint32_t ldo = (uint32_t)g.ldo, ldr = (uint32_t)g.ldr;
+    const uint32_t ldo1 = (uint32_t)g.ldo, ldr = (uint32_t)g.ldr;
 
     // every scale factor this lane needs, read from LDS before any region
     // write (the compiler cannot move LDS reads across LDS writes it cannot
@@ -533,7 +539,10 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
             // keep each pass's work inside the pass (hoisting it all would
             // need more registers than the accumulators leave)
             __builtin_amdgcn_sched_barrier(0);
-            uint16_t *const obase = o.out + row0 * g.ldo + col0;   // uniform
+            int64_t ldo_p = 0;
+            uint16_t *const obase = SPLITOUT ? out_at(g, T.b, row0, col0, ldo_p)   // one segment per 64 columns
+                                             : o.out + row0 * g.ldo + col0;         // uniform
+            const uint32_t ldo = SPLITOUT ? (uint32_t)ldo_p : ldo1;
 
             // 1. residual block -> region
             if (EPI == SPG_EPI_ADD && !BIAS && !STAGED) {
@@ -631,7 +640,11 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
 // used by nothing else (ADD with a bias row; untouched otherwise).
 // STAGE: `region` is this wave's MI * 2 * 4 KiB (one region per pass), and
 // whole quadrants of a residual matrix are staged (see STAGED above).
-template <int EPI, int MI = 4, bool GIVEN = false, bool STAGE = false>
+// SO: the output is column segments (g.nseg > 0).  Kernels are instantiated
+// apart for it, so the split-output code is not part of the kernels that
+// write one output (inside a persistent kernel it cost those 4.5%: more
+// scalar spills and twice the code).
+template <int EPI, int MI = 4, bool GIVEN = false, bool STAGE = false, bool SO = false>
 __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const Acc &acc, const float *lds_sa,
                                          const float *lds_sw, float *lds_bias, uint8_t *region, int wave_in = 0)
 {
@@ -640,6 +653,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs &g, const Tile &T, const
     const int wm = wave >> 1, wn = wave & 1;
     const EpiOut o = epi_out<EPI>(g, T);
     const bool brow = EPI == SPG_EPI_ADD && g.bias_mode != 0;
+    if constexpr (SO) {
+        // split outputs: one instantiation per bias form, with bounds checks
+        if (EPI == SPG_EPI_ADD && brow)
+            epilogue_impl<EPI, false, MI, GIVEN, EPI == SPG_EPI_ADD, false, true>(g, T, acc, lds_sa, lds_sw, lds_bias,
+                                                                               region, wave_in);
+        else
+            epilogue_impl<EPI, false, MI, GIVEN, false, false, true>(g, T, acc, lds_sa, lds_sw, lds_bias, region, wave_in);
+        return;
+    }
     const bool full = T.m0 + wm * (MI * 32) + MI * 32 <= g.M && T.c0 + (SW ? wn * 64 + 64 : wn * 128 + 128) <= o.nvalid &&
                       (((uintptr_t)o.out) & 15) == 0 && (g.ldo & 7) == 0 &&
                       (EPI != SPG_EPI_ADD || brow || ((((uintptr_t)o.res) & 15) == 0 && (g.ldr & 7) == 0));

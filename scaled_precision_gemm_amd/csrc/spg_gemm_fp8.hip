@@ -72,7 +72,8 @@ struct CopySrc {
 // left out, so the stage is paced by the weight copies instead of 32 MFMAs on
 // zeros (the waves of the lower half compute the zero blocks of their rows,
 // which keeps all four waves equally busy).
-template <int EPI, int SMODE, bool SPLIT, int AM = 4>
+// SO: the output is column segments (a separate instantiation, see epilogue).
+template <int EPI, int SMODE, bool SPLIT, int AM = 4, bool SO = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 {
     __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlot + kEpiRegionBytes];
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
             // flight (measured: 1-2% of the 4096 x 34816 x 5120 product).  The
             // other epilogues measured slightly faster re-deriving it.
             const int sb = kScaleDma ? i % 3 : i & 1;
-            epilogue<EPI, 4, EPI == SPG_EPI_SWIGLU>(g, Tc, acc, lds_scale[sb][0], lds_scale[sb][1], lds_bias,
+            epilogue<EPI, 4, EPI == SPG_EPI_SWIGLU, false, SO>(g, Tc, acc, lds_scale[sb][0], lds_scale[sb][1], lds_bias,
                                                    &lds[2 * kSlot + wave * (kEpiRegionBytes / 4)], wave);
         }
         if (i + 1 < ntile) {
@@ -443,7 +444,7 @@ struct FragsH {
     uint4 a[2][2], b[4][2];
 };
 
-template <int EPI, int SMODE>
+template <int EPI, int SMODE, bool SO = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmArgs g)
 {
     __shared__ __attribute__((aligned(2048))) uint8_t lds[kSlotsH * kSlotH];
@@ -616,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
     lds_sw[tid] = vw;
     block_barrier();
     // 16 KiB per wave of the freed slots: one region per pass
-    epilogue<EPI, 2, false, true>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[wave * 16384]);
+    epilogue<EPI, 2, false, true, SO>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[wave * 16384]);
     clock_mark(g.clocks, 1);
 }
 
@@ -624,10 +625,14 @@ template <int EPI>
 hipError_t launch_half(const GemmArgs &g, hipStream_t s)
 {
     const dim3 grid((unsigned)(2 * g.tile_count));
-    if (g.format == SPG_FMT_E4M3_ROW)
-        gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_ROW><<<grid, kThreads, 0, s>>>(g);
-    else
-        gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_TENSOR><<<grid, kThreads, 0, s>>>(g);
+    const bool so = g.nseg != 0;
+    if (g.format == SPG_FMT_E4M3_ROW) {
+        if (so) gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_ROW, true><<<grid, kThreads, 0, s>>>(g);
+        else gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_ROW><<<grid, kThreads, 0, s>>>(g);
+    } else {
+        if (so) gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_TENSOR, true><<<grid, kThreads, 0, s>>>(g);
+        else gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_TENSOR><<<grid, kThreads, 0, s>>>(g);
+    }
     return hipGetLastError();
 }
 
@@ -638,30 +643,36 @@ hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
     // at most one per compute unit for unsplit products with two or more K
     // stages.
     const dim3 grid((unsigned)p.workgroups);
-    const bool split = g.split_k > 1;
+    const bool split = g.split_k > 1, so = g.nseg != 0;
     if (g.M <= 32) {
         // at most 32 tokens: one active A block per wave
         if (g.format == SPG_FMT_E4M3_ROW) {
             if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true, 1><<<grid, kThreads, 0, s>>>(g);
+            else if (so) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false, 1, true><<<grid, kThreads, 0, s>>>(g);
             else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false, 1><<<grid, kThreads, 0, s>>>(g);
         } else {
             if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, true, 1><<<grid, kThreads, 0, s>>>(g);
+            else if (so) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 1, true><<<grid, kThreads, 0, s>>>(g);
             else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 1><<<grid, kThreads, 0, s>>>(g);
         }
     } else if (g.M <= 64) {
         // at most 64 tokens: two active A blocks per wave
         if (g.format == SPG_FMT_E4M3_ROW) {
             if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true, 2><<<grid, kThreads, 0, s>>>(g);
+            else if (so) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false, 2, true><<<grid, kThreads, 0, s>>>(g);
             else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false, 2><<<grid, kThreads, 0, s>>>(g);
         } else {
             if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, true, 2><<<grid, kThreads, 0, s>>>(g);
+            else if (so) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 2, true><<<grid, kThreads, 0, s>>>(g);
             else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 2><<<grid, kThreads, 0, s>>>(g);
         }
     } else if (g.format == SPG_FMT_E4M3_ROW) {
         if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, true><<<grid, kThreads, 0, s>>>(g);
+        else if (so) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false, 4, true><<<grid, kThreads, 0, s>>>(g);
         else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_ROW, false><<<grid, kThreads, 0, s>>>(g);
     } else {
         if (split) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, true><<<grid, kThreads, 0, s>>>(g);
+        else if (so) gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false, 4, true><<<grid, kThreads, 0, s>>>(g);
         else gemm_fp8_kernel<EPI, SPG_FMT_E4M3_TENSOR, false><<<grid, kThreads, 0, s>>>(g);
     }
     hipError_t e = hipGetLastError();

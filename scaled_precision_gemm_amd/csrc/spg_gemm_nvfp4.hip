@@ -60,7 +60,7 @@ __device__ __forceinline__ h2 scale_h2(uint32_t code)
 
 // General path (any K multiple of 32): per-thread register-staged loads, the
 // tile decoded to f16 in LDS once per stage.
-template <int EPI>
+template <int EPI, bool SO = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const GemmArgs g)
 {
     constexpr int kLdsBytes = 4 * kStageBytes;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_general_kernel(const G
         splitk_store(g, T, split, acc);   // the slices are summed by splitk_reduce_kernel
         return;
     }
-    epilogue<EPI>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
+    epilogue<EPI, 4, false, false, SO>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 4096]);   // after the barrier above
 }
 
 // Decode for the fast path, with the hardware conversions.  Every E4M3
@@ -234,7 +234,7 @@ static_assert(4 * 32768 <= 2 * kSlotF, "the epilogue's staged regions fit in the
 // 32 (64) tokens have only their first 32 (64) tile rows, so AM = 1 (2)
 // leaves out the code reads, decodes and MFMAs of the empty A blocks: a stage
 // is then paced by the weights (their copies and decode), as for FP8.
-template <int EPI, bool SPLIT, int AM = 4>
+template <int EPI, bool SPLIT, int AM = 4, bool SO = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs g)
 {
     __shared__ __attribute__((aligned(2048))) uint8_t lds[2 * kSlotF];
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(const GemmArgs 
         return;
     }
     // slots free after the barrier: 32 KiB per wave, one region per pass
-    epilogue<EPI, 4, false, true>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 32768]);
+    epilogue<EPI, 4, false, true, SO>(g, T, acc, lds_sa, lds_sw, lds_bias, &lds[(threadIdx.x >> 6) * 32768]);
     clock_mark(g.clocks, 1);
 }
 
@@ -457,17 +457,23 @@ hipError_t launch_epi(const GemmArgs &g, const spg_plan &p, hipStream_t s)
     // the fast path copies 16-byte pieces of the scale planes: both must be
     // 16-byte aligned (rows are, since K / 16 is then a multiple of 16)
     const bool fast = p.bk == kBKF && (((uintptr_t)g.sa | (uintptr_t)g.sw) & 15) == 0;
+    const bool so = g.nseg != 0;
     if (fast) {
         if (g.M <= 32) {
             if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true, 1><<<grid, kThreads, 0, s>>>(g);
+            else if (so) gemm_nvfp4_kernel<EPI, false, 1, true><<<grid, kThreads, 0, s>>>(g);
             else gemm_nvfp4_kernel<EPI, false, 1><<<grid, kThreads, 0, s>>>(g);
         } else if (g.M <= 64) {
             if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true, 2><<<grid, kThreads, 0, s>>>(g);
+            else if (so) gemm_nvfp4_kernel<EPI, false, 2, true><<<grid, kThreads, 0, s>>>(g);
             else gemm_nvfp4_kernel<EPI, false, 2><<<grid, kThreads, 0, s>>>(g);
         } else {
             if (g.split_k > 1) gemm_nvfp4_kernel<EPI, true><<<grid, kThreads, 0, s>>>(g);
+            else if (so) gemm_nvfp4_kernel<EPI, false, 4, true><<<grid, kThreads, 0, s>>>(g);
             else gemm_nvfp4_kernel<EPI, false><<<grid, kThreads, 0, s>>>(g);
         }
+    } else if (so) {
+        gemm_nvfp4_general_kernel<EPI, true><<<grid, kThreads, 0, s>>>(g);
     } else {
         gemm_nvfp4_general_kernel<EPI><<<grid, kThreads, 0, s>>>(g);
     }

@@ -50,6 +50,7 @@ class Workload:
     w_std: float = 0.02
     seed: int = 0
     bias: bool = False  # "add" with one bf16 row [n_out] (a bias) instead of an [M, n_out] residual
+    split: tuple = ()   # output column widths of a split-N output (one tensor per segment), else one output
 
     @property
     def n_out(self) -> int:
@@ -97,4 +98,13 @@ WORKLOADS = {
     "nvfp4_swiglu_t16": Workload("nvfp4_swiglu_t16", "nvfp4", "swiglu", 16, 34816, 5120, seed=630),
     # the T=4096 [N=5120, K=6144] linear in row-scaled FP8 with a fused bf16 bias row
     "fp8_row_bias_t4096": Workload("fp8_row_bias_t4096", "e4m3_row", "add", 4096, 5120, 6144, seed=700, bias=True),
+    # fused input projections with split outputs (the pages name the call
+    # sites, attn_input_proj and gdn_input_proj, but give no shapes): an
+    # attention q | k | v projection with 40 query and 8 key/value heads of
+    # 128 from a 5120-wide hidden state, and a gated-delta-net q | k | v | z
+    # projection (16 + 16 key heads and 32 + 32 value heads of 128) from 2048
+    "fp8_row_attn_in_t4096": Workload("fp8_row_attn_in_t4096", "e4m3_row", "store", 4096, 7168, 5120, seed=800,
+                                      split=(5120, 1024, 1024)),
+    "fp8_row_gdn_in_t4096": Workload("fp8_row_gdn_in_t4096", "e4m3_row", "store", 4096, 12288, 2048, seed=810,
+                                     split=(2048, 2048, 4096, 4096)),
 }

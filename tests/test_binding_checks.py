@@ -39,6 +39,10 @@ def test_valid_call_reaches_the_device_check():
         call(row_args(epilogue="swiglu", out=t((M, N // 2), torch.bfloat16)))
     with pytest.raises(ValueError, match="CUDA"):
         call(row_args(epilogue="add", residual=t((N,), torch.uint8), bias_scale=t((1,), torch.float32)))
+    with pytest.raises(ValueError, match="CUDA"):
+        call(row_args(out_split=[64, N - 64]))
+    with pytest.raises(ValueError, match="CUDA"):
+        call(row_args(out_split=[t((M, 64), torch.bfloat16), t((M, N - 64), torch.bfloat16)]))
 
 
 @pytest.mark.parametrize("case,match", [
@@ -63,6 +67,12 @@ def test_valid_call_reaches_the_device_check():
     ("bias_scale_with_matrix", "E4M3 codes"),
     ("bias_scale_two_values", "bias_scale must be one fp32 value"),
     ("codes_without_bias_scale", "residual must be bf16"),
+    ("split_and_out", "exclusive"),
+    ("split_widths_sum", "adding up to"),
+    ("split_boundary", "multiple of 64"),
+    ("split_tensor_dtype", "must be a bf16 tensor"),
+    ("split_tensor_rows", "wrong rows"),
+    ("split_tensor_stride", "row stride a multiple of 8"),
 ])
 def test_bad_calls_raise_before_the_library(case, match):
     a = row_args()
@@ -112,5 +122,17 @@ def test_bad_calls_raise_before_the_library(case, match):
         a.update(epilogue="add", residual=t((N,), torch.uint8), bias_scale=t((2,), torch.float32))
     elif case == "codes_without_bias_scale":
         a.update(epilogue="add", residual=t((N,), torch.uint8))
+    elif case == "split_and_out":
+        a.update(out=t((M, N), torch.bfloat16), out_split=[64, N - 64])
+    elif case == "split_widths_sum":
+        a.update(out_split=[64, N - 63])
+    elif case == "split_boundary":
+        a.update(out_split=[32, N - 32])
+    elif case == "split_tensor_dtype":
+        a.update(out_split=[t((M, 64), torch.bfloat16), t((M, N - 64), torch.float16)])
+    elif case == "split_tensor_rows":
+        a.update(out_split=[t((M, 64), torch.bfloat16), t((M + 1, N - 64), torch.bfloat16)])
+    elif case == "split_tensor_stride":
+        a.update(out_split=[t((M, 68), torch.bfloat16)[:, :64], t((M, N - 64), torch.bfloat16)])
     with pytest.raises(ValueError, match=match):
         call(a)

@@ -882,6 +882,101 @@ def test_gemm_e4m3_bias_with_zero_weights_is_the_bias(spg):
 
 
 # ---------------------------------------------------------------------------
+# Split-N outputs (the fused input projections of ninfer PR #167's call-site
+# list): one GEMM, each column range into its own tensor.  Every segment must
+# equal the same columns of the unsplit output bit for bit (the same kernels
+# run; only the store addresses differ) and match the oracle - through 128-row
+# tiles, a K split with its reduction, few tokens, SwiGLU, a residual with a
+# ragged last segment, per-tensor batches and NVFP4.
+# ---------------------------------------------------------------------------
+
+SPLITS = [((300, 640, 512), "e4m3_row", "store", (256, 256, 128), 1),
+          ((1024, 768, 2048), "e4m3_row", "store", (384, 384), 1),
+          ((16, 5120, 4096), "e4m3_row", "store", (4096, 512, 512), 1),
+          ((300, 1280, 512), "e4m3_row", "swiglu", (384, 256), 1),
+          ((520, 1030, 1024), "e4m3_row", "add", (512, 448, 70), 1),
+          ((96, 300, 512), "e4m3_tensor", "store", (256, 44), 2),
+          ((257, 640, 512), "nvfp4", "store", (64, 512, 64), 1)]
+
+
+@pytest.mark.parametrize("shape,fmt,epi,widths,B", SPLITS,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_gemm_out_split(spg, shape, fmt, epi, widths, B):
+    M, N, K = shape
+    A16 = bf16_normal((B, M, K) if B > 1 else (M, K), 1.0, 300 + M)
+    W16 = bf16_normal((N, K), 0.02, 301 + N)
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, 302) if epi == "add" else None
+    A, W = dev(A16), dev(W16)
+    res = dev(R16) if R16 is not None else None
+    if fmt == "nvfp4":
+        qa, bsa, ta = spg.quantize_block16(A)
+        qw, bsw, tw = spg.quantize_block16(W)
+        run = lambda **kw: spg.gemm_scaled(qa, bsa, qw, bsw, epi, residual=res, fmt="nvfp4", tscale_a=ta,
+                                           tscale_w=tw, **kw)
+    else:
+        q = spg.quantize_rowwise if fmt == "e4m3_row" else spg.quantize_tensor
+        qa, sa = q(A)
+        qw, sw = q(W)
+        run = lambda **kw: spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res, fmt=fmt, **kw)
+    whole = run()
+    segs = run(out_split=list(widths))
+    torch.cuda.synchronize()
+    assert [t.shape[-1] for t in segs] == list(widths)
+    assert torch.equal(torch.cat(segs, dim=-1).view(torch.int16), whole.view(torch.int16))
+    gpu = host_u16(torch.cat(segs, dim=-1))
+    for b in range(B):
+        Ab = A16[b] if B > 1 else A16
+        ref = oracle_nvfp4(Ab, W16, epi, R16) if fmt == "nvfp4" else oracle_fp8(Ab, W16, epi, fmt, R16)
+        check_close(gpu[b] if B > 1 else gpu, ref["y"], ref["S"], f"split {shape} {fmt} {epi} batch {b}")
+
+
+def test_gemm_out_split_into_strided_views(spg):
+    # segments as column windows of wider buffers (row stride > width): the
+    # windows get the output, the rest of each buffer is left as it was
+    M, N, K = 520, 768, 1024
+    A16 = bf16_normal((M, K), 1.0, 310)
+    W16 = bf16_normal((N, K), 0.02, 311)
+    qa, sa = spg.quantize_rowwise(dev(A16))
+    qw, sw = spg.quantize_rowwise(dev(W16))
+    whole = spg.gemm_scaled(qa, sa, qw, sw, "store")
+    bufs = [torch.full((M, 512), 7.0, dtype=torch.bfloat16, device="cuda"),
+            torch.full((M, 704), -3.0, dtype=torch.bfloat16, device="cuda")]
+    views = [bufs[0][:, 64:448], bufs[1][:, 320:704]]
+    out = spg.gemm_scaled(qa, sa, qw, sw, "store", out_split=views)
+    torch.cuda.synchronize()
+    assert out[0].data_ptr() == views[0].data_ptr()
+    assert torch.equal(bufs[0][:, 64:448].view(torch.int16), whole[:, :384].view(torch.int16))
+    assert torch.equal(bufs[1][:, 320:704].view(torch.int16), whole[:, 384:].view(torch.int16))
+    assert torch.all(bufs[0][:, :64] == 7.0) and torch.all(bufs[0][:, 448:] == 7.0)
+    assert torch.all(bufs[1][:, :320] == -3.0)
+
+
+@pytest.mark.parametrize("name", ["fp8_row_attn_in_t4096", "fp8_row_gdn_in_t4096"])
+def test_workload_out_split_full_size(spg, name):
+    # the two projection workloads at full size: bitwise against the unsplit
+    # output, and the oracle on rows and columns that reach every tile
+    wl = WORKLOADS[name]
+    rng = np.random.default_rng(wl.seed)
+    A16, W16, _ = wl.inputs()
+    qa, sa = spg.quantize_rowwise(dev(A16))
+    qw, sw = spg.quantize_rowwise(dev(W16))
+    whole = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue)
+    segs = spg.gemm_scaled(qa, sa, qw, sw, wl.epilogue, out_split=list(wl.split))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(segs, dim=-1).view(torch.int16), whole.view(torch.int16))
+    del whole
+    rows = sample_every_tile(wl.M, rng, 256)
+    cols = sample_every_tile(wl.n_out, rng, 256)
+    bounds = np.cumsum((0,) + wl.split)
+    # both sides of every segment boundary
+    cols = np.unique(np.concatenate([cols, bounds[1:-1], bounds[1:-1] - 1]))
+    gpu = np.concatenate([host_u16(t[torch.from_numpy(rows).cuda()]) for t in segs], axis=1)[:, cols]
+    ref = oracle.linear_e4m3_rowwise(np.ascontiguousarray(A16[rows]), np.ascontiguousarray(W16[cols]), "store")
+    check_close(gpu, ref["y"], ref["S"], f"{name} sampled")
+
+
+# ---------------------------------------------------------------------------
 # few tokens (M <= 64, decode widths): one partly filled tile row, K split
 # over many slices; the instantiations for at most 32 and at most 64 tokens.  Ragged N (SwiGLU halves that are not a multiple of 4
 # columns), K not a multiple of 64, one to 32 tokens, per-tensor batches with

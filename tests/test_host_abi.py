@@ -205,6 +205,84 @@ def test_gemm_e4m3_bias_row_passes_validation(spg):
     assert spg.lib.spg_gemm_plan(ctypes.byref(d), 1, 256, ctypes.byref(p)) == 0
 
 
+def out_split(spg, widths, ptrs, ldos, strides=None):
+    sp = spg.OutSplit()
+    sp.count = len(widths)
+    end = 0
+    for i, w in enumerate(widths):
+        end += w
+        sp.col_end[i] = end
+        sp.out[i] = ptrs[i]
+        sp.ldo[i] = ldos[i]
+        sp.stride_o[i] = strides[i] if strides else 0
+    return sp
+
+
+SEG = [0x10000000, 0x20000000, 0x30000000]       # far apart, 16-byte aligned
+
+
+@pytest.mark.parametrize("case", [
+    "count_zero", "count_nine", "out_also_given", "boundary_not_64", "last_short", "ends_not_increasing",
+    "segment_misaligned", "ldo_short", "ldo_not_8", "segments_overlap", "residual_in_segment",
+    "batch_stride_short", "null_segment",
+])
+def test_gemm_out_split_validation(spg, case):
+    # N = 320 outputs as 128 | 128 | 64 by default
+    d = desc(spg, 64, 320, 64, 0)
+    widths, ptrs, ldos, strides = [128, 128, 64], list(SEG), [128, 128, 64], None
+    epi, kw = 0, {"out": None}
+    if case == "count_zero":
+        widths = []
+    elif case == "count_nine":
+        widths, ptrs, ldos = [64] * 5, SEG + [0x40000000, 0x50000000], [64] * 5
+    elif case == "out_also_given":
+        kw["out"] = FAKE
+    elif case == "boundary_not_64":
+        widths = [96, 160, 64]
+    elif case == "last_short":
+        widths = [128, 128, 32]
+    elif case == "ends_not_increasing":
+        widths = [128, 0, 192]
+    elif case == "segment_misaligned":
+        ptrs[1] += 8
+    elif case == "ldo_short":
+        ldos[0] = 120
+    elif case == "ldo_not_8":
+        ldos[2] = 68
+    elif case == "segments_overlap":
+        ptrs[1] = SEG[0] + 2 * 64 * 128 - 16      # inside segment 0's last row
+    elif case == "residual_in_segment":
+        epi, kw["res"] = 1, P(SEG[2] + 64)
+    elif case == "batch_stride_short":
+        d.batch, d.stride_a = 2, 64 * 64
+        strides = [64 * 128, 63 * 128, 64 * 64]
+    elif case == "null_segment":
+        ptrs[2] = 0
+    sp = out_split(spg, widths, ptrs, ldos, strides)
+    if case == "count_nine":
+        sp.count = 9
+    d.out_split = ctypes.pointer(sp)
+    assert call_gemm(spg, d, epi, **kw) == EINVAL
+
+
+def test_gemm_out_split_passes_validation(spg):
+    # a valid split (also with a residual elsewhere, and batched) gets past
+    # validation: SPG_EHIP without a device, never SPG_EINVAL
+    d = desc(spg, 64, 320, 64, 0)
+    sp = out_split(spg, [128, 128, 64], SEG, [128, 136, 64])
+    d.out_split = ctypes.pointer(sp)
+    assert call_gemm(spg, d, 0, out=None) != EINVAL
+    assert call_gemm(spg, d, 1, out=None, res=FAKE2) != EINVAL
+    d2 = desc(spg, 64, 640, 64, 0)
+    sp2 = out_split(spg, [320], [SEG[0]], [320])
+    d2.out_split = ctypes.pointer(sp2)
+    assert call_gemm(spg, d2, 2, out=None) != EINVAL       # SwiGLU: 320 outputs
+    d.batch, d.stride_a = 2, 64 * 64
+    sp3 = out_split(spg, [128, 128, 64], SEG, [128, 128, 64], [64 * 128, 64 * 128, 64 * 64])
+    d.out_split = ctypes.pointer(sp3)
+    assert call_gemm(spg, d, 0, out=None) != EINVAL
+
+
 def test_gemm_nvfp4_batch_unsupported(spg):
     d = desc(spg, 64, 64, 64, 2)
     d.batch = 2
