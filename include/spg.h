@@ -177,6 +177,20 @@ int quantize_block16_noalloc(const void *x, int64_t rows, int64_t K, uint8_t *q,
 /* ------------------------------------------------------------------------ */
 
 /*
+ * Operand storage (spg_gemm_desc.layout, flags).  The product is always
+ * out = epilogue(scale * A W^T) with A the logical M x K and W the logical
+ * N x K matrix; a flag stores that operand with K as its rows instead - the
+ * layouts of the backward products (AstrAI commit log, the crosswise
+ * backward GEMM entries: dX = dY W reads W K-major, dW = dY^T X reads both
+ * operands K-major).  FP8 formats only (NVFP4: SPG_EUNSUPPORTED).
+ */
+typedef enum {
+    SPG_LAYOUT_NT = 0,         /* A [M, K], W [N, K]: K contiguous in both    */
+    SPG_LAYOUT_A_KMAJOR = 1,   /* A stored [K, M]: lda >= M (row stride)       */
+    SPG_LAYOUT_W_KMAJOR = 2    /* W stored [K, N]: ldw >= N                    */
+} spg_layout;
+
+/*
  * Output split along N (split-N epilogue): the output columns of one product
  * go to up to SPG_MAX_OUT_SPLITS separate matrices, one per column range -
  * the fused input projections (q | k | v ...) that ninfer PR #167 lists
@@ -246,6 +260,13 @@ typedef struct spg_out_split {
  *              call: the output as column segments (spg_out_split above).
  *              When set, gemm_scaled's `out` must be NULL and ldo, stride_o
  *              are not used.
+ *   layout   : SPG_LAYOUT_* flags (0 by default).  A K-major operand is
+ *              copied transposed into the workspace by the call (a byte
+ *              transpose, HBM-bound) and the product then runs as for
+ *              SPG_LAYOUT_NT; lda / ldw are the stored row strides (>= M,
+ *              >= N; multiples of 16), stride_a / stride_w the stored batch
+ *              strides; sa / sw keep their meaning (per output row / column,
+ *              or per tensor).
  */
 typedef struct spg_gemm_desc {
     int64_t M, N, K, batch;
@@ -258,6 +279,8 @@ typedef struct spg_gemm_desc {
     uint64_t *clock_probe;
     const float *bias_scale;
     const spg_out_split *out_split;
+    int32_t layout;
+    int32_t reserved2;
 } spg_gemm_desc;
 
 /* Zero every field, set batch = 1 and the dense strides for M, N, K. */
@@ -282,7 +305,8 @@ void spg_gemm_desc_init(spg_gemm_desc *d, int64_t M, int64_t N, int64_t K, int32
  *   epilogue : SPG_EPI_*; SWIGLU pairs W rows j (gate) and j + N/2 (up) and
  *              needs N even
  *   ws       : device workspace of at least gemm_scaled_workspace_bytes(d, epilogue)
- *              (may be NULL when that is 0)
+ *              (may be NULL when that is 0): K-split partial tiles, and the
+ *              transposed copies of K-major operands
  *   With batch > 1 the output entries must not overlap:
  *   stride_o >= (M - 1) * ldo + n_out, else SPG_EINVAL.
  * Results: each element within 2^-8 |y| + 2^-12 S of the exact value y,

@@ -40,6 +40,7 @@ class SpgError(RuntimeError):
 
 
 MAX_OUT_SPLITS = 8
+LAYOUT_NT, LAYOUT_A_KMAJOR, LAYOUT_W_KMAJOR = 0, 1, 2
 
 
 class OutSplit(ctypes.Structure):
@@ -59,7 +60,7 @@ class GemmDesc(ctypes.Structure):
         ("format", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
         ("tscale_a", ctypes.c_void_p), ("tscale_w", ctypes.c_void_p),
         ("clock_probe", ctypes.c_void_p), ("bias_scale", ctypes.c_void_p),
-        ("out_split", ctypes.POINTER(OutSplit)),
+        ("out_split", ctypes.POINTER(OutSplit)), ("layout", ctypes.c_int32), ("reserved2", ctypes.c_int32),
     ]
 
 
@@ -200,8 +201,16 @@ def _desc(fmt: int, M: int, N: int, K: int) -> GemmDesc:
     return d
 
 
+def _logical_dims(A, W, a_kmajor, w_kmajor):
+    """(M, N, K in code bytes) of the product from the stored operands: A is
+    [M, K] or, K-major, [K, M]; W is [N, K] or, K-major, [K, N]."""
+    M, Ka = (A.shape[-1], A.shape[-2]) if a_kmajor else (A.shape[-2], A.shape[-1])
+    N, Kw = (W.shape[-1], W.shape[-2]) if w_kmajor else (W.shape[-2], W.shape[-1])
+    return M, N, Ka, Kw
+
+
 def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residual=None,
-              tscale_a=None, tscale_w=None) -> tuple[GemmDesc, int, int]:
+              tscale_a=None, tscale_w=None, a_kmajor=False, w_kmajor=False) -> tuple[GemmDesc, int, int]:
     fmt = _FMT.get(fmt, fmt)
     epi = _EPI.get(epilogue, epilogue)
     _need(A.dtype == torch.uint8 and W.dtype == torch.uint8, "A and W must be uint8 code tensors")
@@ -211,11 +220,11 @@ def make_desc(A: torch.Tensor, W: torch.Tensor, fmt, epilogue, out=None, residua
     _need(A3.stride(2) == 1 and W3.stride(2) == 1, "rows must be contiguous")
     batch = max(A3.shape[0], W3.shape[0])
     _need(A3.shape[0] in (1, batch) and W3.shape[0] in (1, batch), "batch sizes must match or be 1")
-    M, Kc = A3.shape[1:]
-    N = W3.shape[1]
+    M, N, Kc, Kw = _logical_dims(A3, W3, a_kmajor, w_kmajor)
     K = 2 * Kc if fmt == FMT_NVFP4 else Kc
-    _need(W3.shape[2] == Kc, "A and W disagree on K")
+    _need(Kw == Kc, "A and W disagree on K")
     d = _desc(fmt, M, N, K)
+    d.layout = (LAYOUT_A_KMAJOR if a_kmajor else 0) | (LAYOUT_W_KMAJOR if w_kmajor else 0)
     d.batch = batch
     d.lda, d.ldw = A3.stride(1), W3.stride(1)
     d.stride_a = A3.stride(0) if A3.shape[0] > 1 else 0
@@ -264,7 +273,7 @@ def check_out_split(segs, M, n_out, batch, batched, dev):
 
 
 def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_a=None, tscale_w=None,
-                   scale_layout="row", bias_scale=None, out_split=None):
+                   scale_layout="row", bias_scale=None, out_split=None, a_kmajor=False, w_kmajor=False):
     """Shapes, dtypes, strides and devices of a gemm_scaled call, checked
     before anything reaches the library (raises ValueError).  The library
     trusts the sizes it is given, so an output, residual or scale tensor
@@ -287,8 +296,12 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
     batch = max(Ab, Wb)
     _need(Ab in (1, batch) and Wb in (1, batch), "batch sizes of A and W must match or be 1")
     batched = A.dim() == 3 or W.dim() == 3
-    M, N, Kc = A.shape[-2], W.shape[-2], A.shape[-1]
-    _need(W.shape[-1] == Kc, "A and W disagree on K")
+    _need(fmt != FMT_NVFP4 or not (a_kmajor or w_kmajor), "K-major operands are taken only by the FP8 formats")
+    M, N, Kc, Kw = _logical_dims(A, W, a_kmajor, w_kmajor)
+    _need(Kw == Kc, "A and W disagree on K")
+    for name, t, km in (("A", A, a_kmajor), ("W", W, w_kmajor)):
+        _need(not km or (t.stride(-2) % 16 == 0 and t.data_ptr() % 16 == 0),
+              f"a K-major {name} needs 16-byte aligned rows")
     n_out = N // 2 if epi == EPI_SWIGLU else N
     _need(sa is not None and sw is not None, "sa and sw are required")
     if fmt == FMT_E4M3_ROW:
@@ -345,7 +358,7 @@ def check_operands(A, sa, W, sw, fmt, epilogue, out=None, residual=None, tscale_
 
 def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
                 out=None, tscale_a=None, tscale_w=None, workspace=None, clock_probe=None, scale_layout="row",
-                bias_scale=None, out_split=None):
+                bias_scale=None, out_split=None, a_kmajor=False, w_kmajor=False):
     """out = epilogue(scale * A W^T) in bf16.
 
     e4m3_row: A uint8 [M,K], sa fp32 [M]; W uint8 [N,K], sw fp32 [N]
@@ -365,11 +378,14 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
            output tensors, one per column segment (see spg_out_split): the
            output goes to them instead of one tensor, and they are returned
            as a list (out must then be None)
+    a_kmajor, w_kmajor: the operand is stored K-major - A as [K, M], W as
+           [K, N] ([B, K, .] batched), as the backward products read them
+           (dX = dY W: w_kmajor; dW = dY^T X: both); FP8 formats only
     """
     check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale,
-                   out_split)
+                   out_split, a_kmajor, w_kmajor)
     _need(A.is_cuda, "operands must be CUDA tensors")
-    d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w)
+    d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w, a_kmajor, w_kmajor)
     split = None
     if out_split is not None:
         segs = list(out_split)
@@ -408,10 +424,11 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
     return segs if split is not None else out
 
 
-def gemm_workspace(A, W, fmt="e4m3_row", epilogue="store", out=None, residual=None):
+def gemm_workspace(A, W, fmt="e4m3_row", epilogue="store", out=None, residual=None, a_kmajor=False,
+                   w_kmajor=False):
     """A device workspace large enough for gemm_scaled on these operands, or
     None when the plan needs none."""
-    d, epi, _ = make_desc(A, W, fmt, epilogue, out, residual)
+    d, epi, _ = make_desc(A, W, fmt, epilogue, out, residual, a_kmajor=a_kmajor, w_kmajor=w_kmajor)
     nws = lib.gemm_scaled_workspace_bytes(ctypes.byref(d), epi)
     return torch.empty((nws,), dtype=torch.uint8, device=A.device) if nws > 0 else None
 

@@ -48,11 +48,23 @@ int validate_desc(const spg_gemm_desc *d, int epi)
         if (d->batch != 1) return SPG_EUNSUPPORTED;
         if (d->scale_layout != SPG_SCALES_ROW_MAJOR && d->scale_layout != SPG_SCALES_BLOCKED) return SPG_EINVAL;
         if (d->scale_layout == SPG_SCALES_BLOCKED && (d->K % 256)) return SPG_EINVAL;
+        if (d->layout != SPG_LAYOUT_NT) return SPG_EUNSUPPORTED;
     } else {
         if (d->K % 16) return SPG_EINVAL;
-        if (d->lda < d->K || d->ldw < d->K) return SPG_EINVAL;
+        // stored row strides: K for K-contiguous operands, M / N for K-major ones
+        const int64_t need_a = (d->layout & SPG_LAYOUT_A_KMAJOR) ? d->M : d->K;
+        const int64_t need_w = (d->layout & SPG_LAYOUT_W_KMAJOR) ? d->N : d->K;
+        if (d->lda < need_a || d->ldw < need_w) return SPG_EINVAL;
         if (d->scale_layout != SPG_SCALES_ROW_MAJOR) return SPG_EINVAL;   // NVFP4 only
+        if (d->layout != SPG_LAYOUT_NT) {
+            // the transposed copies are read with row stride K; the
+            // transpose runs one 64 x 64 block per workgroup
+            if (d->K > (INT64_C(1) << 23)) return SPG_EUNSUPPORTED;
+            const int64_t blocks = cdiv(d->K, 64) * (cdiv(d->M, 64) + cdiv(d->N, 64)) * d->batch;
+            if (blocks >= (INT64_C(1) << 31)) return SPG_EUNSUPPORTED;
+        }
     }
+    if (d->layout < 0 || d->layout > (SPG_LAYOUT_A_KMAJOR | SPG_LAYOUT_W_KMAJOR)) return SPG_EINVAL;
     if ((d->lda & 15) || (d->ldw & 15)) return SPG_EINVAL;
     // a 256-row tile of codes must fit the 31-bit range of a buffer resource
     if (d->lda > (INT64_C(1) << 23) || d->ldw > (INT64_C(1) << 23)) return SPG_EUNSUPPORTED;
@@ -244,6 +256,22 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
         p->workgroups = main_tiles * p->split_k;
 }
 
+constexpr size_t kWsAlign = 256;
+size_t align_ws(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Workspace bytes of the transposed copies of K-major operands (A first,
+// then W, each 256-byte aligned); `a_bytes` gets the A part.
+size_t transpose_bytes(const spg_gemm_desc *d, size_t *a_bytes)
+{
+    size_t a = 0, w = 0;
+    if (d->layout & SPG_LAYOUT_A_KMAJOR)
+        a = align_ws((size_t)(d->stride_a ? d->batch : 1) * (size_t)d->M * (size_t)d->K);
+    if (d->layout & SPG_LAYOUT_W_KMAJOR)
+        w = align_ws((size_t)(d->stride_w ? d->batch : 1) * (size_t)d->N * (size_t)d->K);
+    if (a_bytes) *a_bytes = a;
+    return a + w;
+}
+
 size_t plan_workspace(const spg_plan *p)
 {
     if (p->split_k > 1) return (size_t)p->tiles * p->split_k * kTile * kTile * sizeof(float);
@@ -316,7 +344,7 @@ SPG_EXPORT size_t gemm_scaled_workspace_bytes(const spg_gemm_desc *d, int epilog
     if (validate_desc(d, epilogue) != SPG_OK) return 0;
     spg_plan p;
     make_plan(d, epilogue, device_units(), &p);
-    return plan_workspace(&p);
+    return transpose_bytes(d, nullptr) + plan_workspace(&p);
 }
 
 // A bf16 output region [o0, o1): one matrix (or segment) of a call.
@@ -409,14 +437,39 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
 
     spg_plan p;
     make_plan(d, epilogue, device_units(), &p);
-    const size_t need = plan_workspace(&p);
+    size_t t_a = 0;
+    const size_t t_bytes = transpose_bytes(d, &t_a);
+    const size_t need = t_bytes + plan_workspace(&p);
     if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return SPG_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    // K-major operands: transposed copies (K contiguous) in the workspace,
+    // on the call's stream ahead of the GEMM
+    const uint8_t *A_nt = (const uint8_t *)A, *W_nt = (const uint8_t *)W;
+    int64_t lda = d->lda, ldw = d->ldw, stride_a = d->stride_a, stride_w = d->stride_w;
+    if (d->layout & SPG_LAYOUT_A_KMAJOR) {
+        uint8_t *at = (uint8_t *)ws;
+        if (launch_transpose_u8(A_nt, d->K, d->M, d->lda, d->stride_a, d->stride_a ? d->batch : 1, at, s) !=
+            hipSuccess)
+            return SPG_EHIP;
+        A_nt = at;
+        lda = d->K;
+        stride_a = d->stride_a ? d->M * d->K : 0;
+    }
+    if (d->layout & SPG_LAYOUT_W_KMAJOR) {
+        uint8_t *wt = (uint8_t *)ws + t_a;
+        if (launch_transpose_u8(W_nt, d->K, d->N, d->ldw, d->stride_w, d->stride_w ? d->batch : 1, wt, s) !=
+            hipSuccess)
+            return SPG_EHIP;
+        W_nt = wt;
+        ldw = d->K;
+        stride_w = d->stride_w ? d->N * d->K : 0;
+    }
 
     GemmArgs g;
     memset(&g, 0, sizeof(g));
     g.out = out;
-    g.A = (const uint8_t *)A;
-    g.W = (const uint8_t *)W;
+    g.A = A_nt;
+    g.W = W_nt;
     g.sa = sa;
     g.sw = sw;
     g.residual = (const uint16_t *)residual;
@@ -424,12 +477,12 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.N = d->N;
     g.K = d->K;
     g.batch = d->batch;
-    g.lda = d->lda;
-    g.ldw = d->ldw;
+    g.lda = lda;
+    g.ldw = ldw;
     g.ldo = d->ldo;
     g.ldr = d->ldr;
-    g.stride_a = d->stride_a;
-    g.stride_w = d->stride_w;
+    g.stride_a = stride_a;
+    g.stride_w = stride_w;
     g.stride_o = d->stride_o;
     g.stride_r = d->stride_r;
     g.sa_bstride = d->M;
@@ -466,10 +519,9 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.div_per = make_fastdiv((uint32_t)(g.tiles_m * g.tiles_n));
     g.div_span = make_fastdiv((uint32_t)(8 * g.tiles_n));
     g.div_gm_last = make_fastdiv(g.tiles_m % 8 ? (uint32_t)(g.tiles_m % 8) : 8u);
-    if (p.split_k > 1) g.partials = (float *)ws;
+    if (p.split_k > 1) g.partials = (float *)((uint8_t *)ws + t_bytes);
     g.tile_begin = 0;
     g.tile_count = p.tiles - p.tail_tiles;
-    hipStream_t s = (hipStream_t)stream;
     auto launch = [&](const GemmArgs &a, const spg_plan &q) {
         return d->format == SPG_FMT_NVFP4 ? launch_gemm_nvfp4(a, q, s) : launch_gemm_fp8(a, q, s);
     };
@@ -492,7 +544,7 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
         gt.tile_count = p.tail_tiles;
         gt.split_k = p.tail_split;
         gt.k_chunk = cdiv(cdiv(d->K, p.tail_split), unit_k) * unit_k;
-        gt.partials = (float *)ws;
+        gt.partials = (float *)((uint8_t *)ws + t_bytes);
         spg_plan pt = p;
         pt.tiles = p.tail_tiles;
         pt.split_k = p.tail_split;

@@ -189,6 +189,10 @@ hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s);
 hipError_t launch_gemm_fp8_half(const GemmArgs &g, hipStream_t s);   // tiles tile_begin.. as 128-row halves
 hipError_t launch_gemm_nvfp4(const GemmArgs &g, const spg_plan &p, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs &g, int64_t tiles, hipStream_t s);
+// [R, C] codes (row stride ld, batch stride bstride, 16-byte aligned rows)
+// -> [C, R] with row stride R (R % 16 == 0), batch entries R * C apart.
+hipError_t launch_transpose_u8(const uint8_t *src, int64_t R, int64_t C, int64_t ld, int64_t bstride,
+                               int64_t batch, uint8_t *dst, hipStream_t s);
 hipError_t launch_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t K, int64_t ldx,
                                    uint8_t *q, int64_t ldq, float *scale, hipStream_t s);
 hipError_t launch_quantize_tensor(const uint16_t *x, int64_t batch, int64_t rows, int64_t K,

@@ -42,6 +42,8 @@ def test_valid_call_reaches_the_device_check():
     with pytest.raises(ValueError, match="CUDA"):
         call(row_args(out_split=[64, N - 64]))
     with pytest.raises(ValueError, match="CUDA"):
+        call(row_args(A=t((K, M), torch.uint8), W=t((K, N), torch.uint8), a_kmajor=True, w_kmajor=True))
+    with pytest.raises(ValueError, match="CUDA"):
         call(row_args(out_split=[t((M, 64), torch.bfloat16), t((M, N - 64), torch.bfloat16)]))
 
 
@@ -73,6 +75,8 @@ def test_valid_call_reaches_the_device_check():
     ("split_tensor_dtype", "must be a bf16 tensor"),
     ("split_tensor_rows", "wrong rows"),
     ("split_tensor_stride", "row stride a multiple of 8"),
+    ("kmajor_nvfp4", "only by the FP8 formats"),
+    ("kmajor_k_mismatch", "disagree on K"),
 ])
 def test_bad_calls_raise_before_the_library(case, match):
     a = row_args()
@@ -132,6 +136,12 @@ def test_bad_calls_raise_before_the_library(case, match):
         a.update(out_split=[t((M, 64), torch.bfloat16), t((M, N - 64), torch.float16)])
     elif case == "split_tensor_rows":
         a.update(out_split=[t((M, 64), torch.bfloat16), t((M + 1, N - 64), torch.bfloat16)])
+    elif case == "kmajor_nvfp4":
+        a.update(fmt="nvfp4", A=t((M, K // 2), torch.uint8), W=t((N, K // 2), torch.uint8),
+                 sa=t((M, K // 16), torch.uint8), sw=t((N, K // 16), torch.uint8),
+                 tscale_a=t((1,), torch.float32), tscale_w=t((1,), torch.float32), w_kmajor=True)
+    elif case == "kmajor_k_mismatch":
+        a.update(W=t((K + 16, N), torch.uint8), w_kmajor=True)
     elif case == "split_tensor_stride":
         a.update(out_split=[t((M, 68), torch.bfloat16)[:, :64], t((M, N - 64), torch.bfloat16)])
     with pytest.raises(ValueError, match=match):

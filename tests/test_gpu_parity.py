@@ -977,6 +977,79 @@ def test_workload_out_split_full_size(spg, name):
 
 
 # ---------------------------------------------------------------------------
+# K-major operands (the backward products' layouts: dX = dY W reads W as
+# [K, N], dW = dY^T X reads both operands K-major).  The call must equal the
+# NT product of the explicitly transposed codes bit for bit (it transposes
+# into the workspace and runs the same kernels) and match the oracle:
+# ragged shapes with padded row strides, few tokens through a K split (its
+# partials sit behind the transposed copies in the workspace), batches.
+# ---------------------------------------------------------------------------
+
+def kmajor(codes: torch.Tensor, ld: int) -> torch.Tensor:
+    """[.., R, K] codes stored K-major as [.., K, R] with row stride ld >= R."""
+    t = codes.transpose(-1, -2)
+    buf = torch.zeros(t.shape[:-1] + (ld,), dtype=torch.uint8, device=codes.device)
+    buf[..., : t.shape[-1]] = t
+    return buf[..., : t.shape[-1]]
+
+
+KMAJOR = [((300, 520, 1040), "e4m3_tensor", "store", (False, True), 1),
+          ((300, 520, 1040), "e4m3_tensor", "add", (True, True), 1),
+          ((257, 300, 512), "e4m3_row", "swiglu", (True, False), 1),
+          ((16, 4096, 2048), "e4m3_row", "store", (False, True), 1),
+          ((96, 200, 256), "e4m3_tensor", "store", (True, True), 2),
+          ((1024, 2048, 4096), "e4m3_tensor", "store", (True, True), 1)]
+
+
+@pytest.mark.parametrize("shape,fmt,epi,km,B", KMAJOR,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_gemm_kmajor_operands(spg, shape, fmt, epi, km, B):
+    M, N, K = shape
+    a_km, w_km = km
+    A16 = bf16_normal((B, M, K) if B > 1 else (M, K), 1.0, 400 + M)
+    W16 = bf16_normal((N, K), 0.02 if fmt == "e4m3_row" else 1.0, 401 + N)
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, 402) if epi == "add" else None
+    res = dev(R16) if R16 is not None else None
+    q = spg.quantize_rowwise if fmt == "e4m3_row" else spg.quantize_tensor
+    qa, sa = q(dev(A16))
+    qw, sw = q(dev(W16))
+    nt = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res, fmt=fmt)
+    ka = kmajor(qa, (M + 31) // 32 * 32) if a_km else qa
+    kw = kmajor(qw, (N + 15) // 16 * 16 + 16) if w_km else qw
+    got = spg.gemm_scaled(ka, sa, kw, sw, epi, residual=res, fmt=fmt, a_kmajor=a_km, w_kmajor=w_km)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), nt.view(torch.int16))
+    gpu = host_u16(got)
+    rng = np.random.default_rng(M + N)
+    big = M * N > 1 << 21
+    rows = sample_every_tile(M, rng, 256) if big else np.arange(M)
+    cols = sample_every_tile(n_out, rng, 128) if big else np.arange(n_out)
+    for b in range(B):
+        Ab = A16[b] if B > 1 else A16
+        g = gpu[b] if B > 1 else gpu
+        if big:
+            # per-tensor scales over the whole matrices, codes of the sampled rows
+            sa_o = oracle.amax(Ab) / np.float32(448.0)
+            sw_o = oracle.amax(W16) / np.float32(448.0)
+            qa_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(Ab[rows]), sa_o)
+            qw_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(W16[cols]), sw_o)
+            D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+            y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o)
+            check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"kmajor {shape} sampled")
+        else:
+            if fmt == "e4m3_tensor" and B > 1:
+                qa_o, sa_o = oracle.quantize_tensor(Ab)
+                qw_o, sw_o = oracle.quantize_tensor(W16)
+                D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+                y, S, _ = oracle.epilogue(epi, D, Da, sa_o[0], sw_o[0], R16)
+                ref = dict(y=y, S=S)
+            else:
+                ref = oracle_fp8(Ab, W16, epi, fmt, R16)
+            check_close(g, ref["y"], ref["S"], f"kmajor {shape} {fmt} {epi} {km} batch {b}")
+
+
+# ---------------------------------------------------------------------------
 # few tokens (M <= 64, decode widths): one partly filled tile row, K split
 # over many slices; the instantiations for at most 32 and at most 64 tokens.  Ragged N (SwiGLU halves that are not a multiple of 4
 # columns), K not a multiple of 64, one to 32 tokens, per-tensor batches with

@@ -283,6 +283,44 @@ def test_gemm_out_split_passes_validation(spg):
     assert call_gemm(spg, d, 0, out=None) != EINVAL
 
 
+def test_gemm_kmajor_layout_validation(spg):
+    # K-major operands: stored row strides are checked against M / N, the
+    # flags against their range, NVFP4 takes none
+    d = desc(spg, 32, 48, 64, 0)
+    d.layout = 4
+    assert call_gemm(spg, d) == EINVAL
+    d = desc(spg, 32, 48, 64, 0)
+    d.layout, d.lda = 1, 16                     # A stored [64, 32]: lda >= 32
+    assert call_gemm(spg, d) == EINVAL
+    d.lda = 32                                  # (NT would need lda >= K = 64)
+    assert call_gemm(spg, d) != EINVAL
+    d.layout, d.lda, d.ldw = 2, 64, 32          # W stored [64, 48]: ldw >= 48
+    assert call_gemm(spg, d) == EINVAL
+    d.ldw = 48
+    assert call_gemm(spg, d) != EINVAL
+    d4 = desc(spg, 64, 64, 64, 2)
+    d4.layout = 2
+    assert call_gemm(spg, d4) == EUNSUP
+
+
+def test_gemm_kmajor_workspace_holds_the_transposed_copies(spg):
+    # one 256-byte aligned [M, K] (and [N, K]) copy per batch entry of each
+    # K-major operand, ahead of any K-split partials
+    d = desc(spg, 300, 520, 1040, 1)
+    base = spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), 0)
+    for layout, extra in ((1, 300 * 1040), (2, 520 * 1040), (3, 300 * 1040 + 520 * 1040)):
+        d.layout = layout
+        al = lambda b: (b + 255) // 256 * 256
+        want = al(300 * 1040) * (layout & 1) + al(520 * 1040) * ((layout >> 1) & 1)
+        assert spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), 0) == base + want
+    # batched with a broadcast W: A copies per entry, one W copy
+    d = desc(spg, 64, 64, 128, 1)
+    d.batch, d.stride_a, d.layout, d.lda = 3, 128 * 64, 3, 64
+    d.ldw = 64
+    d.stride_o = 64 * 64
+    assert spg.lib.gemm_scaled_workspace_bytes(ctypes.byref(d), 0) == 3 * 64 * 128 + 64 * 128
+
+
 def test_gemm_nvfp4_batch_unsupported(spg):
     d = desc(spg, 64, 64, 64, 2)
     d.batch = 2
