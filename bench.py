@@ -136,7 +136,8 @@ def _find(d, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
-def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counters_dir=None):
+def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counters_dir=None, ea_dir=None,
+                       l2_dir=None):
     """Write profiles/<kernel>_<workload>.md (rocprofv3 kernel statistics, HBM
     traffic per launch and, given a counters run, MFMA and LDS utilisation)
     and the traffic record bench.py reports.
@@ -145,7 +146,14 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
     the same counters read for the plain copy dispatch of known size that
     --copy-probe-mib runs in the same process.  MfmaUtil and LdsUtil are
     rocprofv3's derived metrics (MFMA busy cycles over SIMD cycles, LDS busy
-    cycles over CU cycles, at the clock the kernel actually ran)."""
+    cycles over CU cycles, at the clock the kernel actually ran).
+
+    ea_dir (a run of TCC_EA0_RDREQ_sum and its 32-, 64- and 128-byte parts
+    with the same copy probe) checks FETCH_SIZE against raw request counts:
+    bytes = 32 n32 + 64 n64 + 128 n128.  l2_dir (TCC_HIT_sum, TCC_MISS_sum,
+    TCC_EA0_RDREQ_DRAM_sum, TCC_BUBBLE_sum) gives the L2 hit rate and the
+    share of the read requests addressed to memory (DRAM) rather than to
+    another die or IO."""
     wl = WORKLOADS[name]
     kname = "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel"
     stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
@@ -218,9 +226,33 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
                     if r["Counter_Name"] == metric and ("gemm_" in r["Kernel_Name"] or "splitk_reduce" in r["Kernel_Name"])]
             k = max(1, len(disp) // n_all)
             calls = [disp[i:i + k] for i in range(0, len(disp) - k + 1, k)][-st:]
-            per_call = [sum(v * d for v, d in c) / max(1, sum(d for _, d in c)) for c in calls]
-            util[metric] = float(np.median(per_call)) if per_call else None
+            call_vals = [sum(v * d for v, d in c) / max(1, sum(d for _, d in c)) for c in calls]
+            util[metric] = float(np.median(call_vals)) if call_vals else None
         util["dispatches_per_call"] = k
+
+    ea = None
+    if ea_dir:
+        ea = {}
+        for ctr in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"):
+            g, c = per_call(ea_dir, ctr, 4)
+            ea[ctr] = (float(np.median(g)), max(v for v, _ in c) if c else None)
+
+        def req_bytes(i):
+            n = [ea[f"TCC_EA0_RDREQ_{b}B_sum"][i] for b in (32, 64, 128)]
+            return None if any(v is None for v in n) else 32.0 * n[0] + 64.0 * n[1] + 128.0 * n[2]
+        ea["gemm_read_bytes"] = req_bytes(0)
+        ea["copy_read_bytes"] = req_bytes(1)
+        ea["copy_bytes"] = copy_bytes
+        ea["req_128_share"] = ea["TCC_EA0_RDREQ_128B_sum"][0] / max(1.0, ea["TCC_EA0_RDREQ_sum"][0])
+    l2 = None
+    if l2_dir:
+        l2 = {}
+        for ctr in ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_DRAM_sum", "TCC_BUBBLE_sum"):
+            g, _ = per_call(l2_dir, ctr, 5)
+            l2[ctr] = float(np.median(g))
+        l2["hit_rate"] = l2["TCC_HIT_sum"] / max(1.0, l2["TCC_HIT_sum"] + l2["TCC_MISS_sum"])
+        if ea:
+            l2["dram_share"] = l2["TCC_EA0_RDREQ_DRAM_sum"] / max(1.0, ea["TCC_EA0_RDREQ_sum"][0])
 
     rec = {
         "kernel": kname, "workload": name, "kernel_source_hash": kernel_source_hash(wl.fmt),
@@ -231,6 +263,13 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
     if util:
         rec["mfma_util_pct"] = util["MfmaUtil"]
         rec["lds_util_pct"] = util["LdsUtil"]
+    if ea:
+        rec["ea_read_bytes_per_launch"] = ea["gemm_read_bytes"]
+        rec["copy_probe_ea_read_bytes"] = ea["copy_read_bytes"]
+    if l2:
+        rec["l2_hit_rate"] = l2["hit_rate"]
+        if "dram_share" in l2:
+            rec["ea_read_request_dram_share"] = l2["dram_share"]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     allrec = json.load(open(tpath)) if os.path.exists(tpath) else {}
@@ -257,6 +296,22 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
             fh.write(f"Achieved over the call: {wl.flops / (timed_avg_us * 1e-6) / 1e12:.0f} TFLOP/s; HBM "
                      f"{(rd + wr) / (timed_avg_us * 1e-6) / 1e9:.0f} GB/s measured, "
                      f"{gemm_bytes(wl) / (timed_avg_us * 1e-6) / 1e9:.0f} GB/s algorithmic (of 8000).\n\n")
+        if ea:
+            cb = ea["copy_bytes"] or 0
+            fh.write(f"Read side from raw L2-to-memory (EA) request counts by size (`--pmc TCC_EA0_RDREQ_sum "
+                     f"TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum`, same copy probe): "
+                     f"the {cb / 1e6:.1f} MB copy issues requests for {(ea['copy_read_bytes'] or 0) / 1e6:.1f} MB, "
+                     f"which FETCH_SIZE counts {1 / f_read if f_read else 0:.2f}x (hence its read scale); the GEMM "
+                     f"call's requests come to {ea['gemm_read_bytes'] / 1e6:.1f} MB "
+                     f"({ea['gemm_read_bytes'] / gemm_bytes(wl):.2f}x the algorithmic bytes; the scaled FETCH_SIZE "
+                     f"gives {rd / 1e6:.1f} MB), {100 * ea['req_128_share']:.0f}% of them 128-byte requests.  "
+                     f"These counters sit at the L2: whether the memory side serves a request from its "
+                     f"last-level cache or from HBM is not visible to them.\n\n")
+        if l2:
+            fh.write(f"L2 (`--pmc TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_sum TCC_BUBBLE_sum`): hit rate "
+                     f"{100 * l2['hit_rate']:.1f}%"
+                     + (f"; {100 * l2['dram_share']:.1f}% of the read requests addressed to memory (DRAM) rather "
+                        f"than another die or IO" if "dram_share" in l2 else "") + ".\n\n")
         if util:
             fh.write(f"Utilisation (`rocprofv3 --pmc MfmaUtil LdsUtil`, duration-weighted over the call's "
                      f"{util['dispatches_per_call']} dispatch(es), median over the timed calls): MFMA busy "
@@ -398,16 +453,17 @@ def main():
                          "dispatch for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="no GPU work: turn rocprofv3 output of this workload (STATS_DIR FETCH_DIR WRITE_DIR "
-                         "[COUNTERS_DIR]) into profiles/ summaries")
+                         "[COUNTERS_DIR [EA_DIR L2_DIR]]) into profiles/ summaries")
     ap.add_argument("--command", default="", help="with --summarize: the command line that produced the runs")
     args = ap.parse_args()
 
     if args.summarize:
-        if len(args.summarize) not in (3, 4):
-            ap.error("--summarize takes STATS_DIR FETCH_DIR WRITE_DIR [COUNTERS_DIR]")
+        if len(args.summarize) not in (3, 4, 6):
+            ap.error("--summarize takes STATS_DIR FETCH_DIR WRITE_DIR [COUNTERS_DIR [EA_DIR L2_DIR]]")
         d = args.summarize
         summarize_profiles(args.workload, d[0], d[1], d[2], command=args.command,
-                           counters_dir=d[3] if len(d) == 4 else None)
+                           counters_dir=d[3] if len(d) >= 4 else None, ea_dir=d[4] if len(d) == 6 else None,
+                           l2_dir=d[5] if len(d) == 6 else None)
         return
 
     if args.gpus != 1:
