@@ -114,12 +114,18 @@ def _load():
 lib = _load()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    """torch's current stream on t's device, as a raw hipStream_t value."""
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _check(status: int, what: str):
@@ -382,12 +388,32 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
            [K, N] ([B, K, .] batched), as the backward products read them
            (dX = dY W: w_kmajor; dW = dY^T X: both); FP8 formats only
     """
-    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale,
-                   out_split, a_kmajor, w_kmajor)
-    _need(A.is_cuda, "operands must be CUDA tensors")
-    d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w, a_kmajor, w_kmajor)
-    split = None
-    if out_split is not None:
+    segs = None
+    if out_split is None:
+        # the checks and the descriptor depend only on what _sig reads, so a
+        # call that repeats an earlier call's signature reuses its checked
+        # descriptor (the per-call pointers are filled in below)
+        try:
+            key = (fmt, epilogue, scale_layout, a_kmajor, w_kmajor, _sig(A), _sig(sa), _sig(W), _sig(sw),
+                   _sig(out), _sig(residual), _sig(tscale_a), _sig(tscale_w), _sig(bias_scale))
+            hit = _GEMM_CACHE.get(key)
+        except TypeError:      # a non-tensor argument or an unhashable option: the full checks report it
+            key = hit = None
+        if hit is None:
+            hit = _prepare(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout,
+                           bias_scale, a_kmajor, w_kmajor)
+            if key is not None:
+                if len(_GEMM_CACHE) >= _GEMM_CACHE_MAX:
+                    _GEMM_CACHE.clear()
+                _GEMM_CACHE[key] = hit
+        tmpl, epi, out_shape, nws = hit
+        d = GemmDesc.from_buffer_copy(tmpl)
+    else:
+        check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale,
+                       out_split, a_kmajor, w_kmajor)
+        _need(A.is_cuda, "operands must be CUDA tensors")
+        d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w, a_kmajor, w_kmajor)
+        d.scale_layout = _LAYOUT.get(scale_layout, scale_layout)
         segs = list(out_split)
         if all(isinstance(w, int) for w in segs):
             # row strides rounded up to 8 elements (the library's alignment rule)
@@ -403,25 +429,65 @@ def gemm_scaled(A, sa, W, sw, epilogue="store", residual=None, fmt="e4m3_row",
             split.ldo[i] = t.stride(-2)
             split.stride_o[i] = t.stride(0) if batched else 0
         d.out_split = ctypes.pointer(split)
-    d.scale_layout = _LAYOUT.get(scale_layout, scale_layout)
+        out_shape = None
+        nws = lib.gemm_scaled_workspace_bytes(ctypes.byref(d), epi)
     if clock_probe is not None:
-        _need(clock_probe.dtype == torch.int64 and clock_probe.numel() == 4 and clock_probe.is_contiguous()
-              and clock_probe.device == A.device, "clock_probe must be 4 contiguous int64 values on A's device")
+        _need(isinstance(clock_probe, torch.Tensor) and clock_probe.dtype == torch.int64 and clock_probe.numel() == 4
+              and clock_probe.is_contiguous() and clock_probe.device == A.device,
+              "clock_probe must be 4 contiguous int64 values on A's device")
+    if tscale_a is not None:
+        d.tscale_a = tscale_a.data_ptr()
+    if tscale_w is not None:
+        d.tscale_w = tscale_w.data_ptr()
+    if clock_probe is not None:
         d.clock_probe = clock_probe.data_ptr()
     if bias_scale is not None:
         d.bias_scale = bias_scale.data_ptr()
-    n_out = d.N // 2 if epi == EPI_SWIGLU else d.N
-    if out is None and split is None:
-        shape = (d.batch, d.M, n_out) if batched else (d.M, n_out)
-        out = torch.empty(shape, dtype=torch.bfloat16, device=A.device)
+    if out is None and out_shape is not None:
+        out = torch.empty(out_shape, dtype=torch.bfloat16, device=A.device)
+    if nws > 0:
+        if workspace is None or workspace.numel() < nws:
+            workspace = torch.empty((nws,), dtype=torch.uint8, device=A.device)
+        wsp, wsn = workspace.data_ptr(), workspace.numel()
+    else:
+        wsp, wsn = None, 0
+    _check(lib.gemm_scaled(_ptr(out), A.data_ptr(), _ptr(sa), W.data_ptr(), _ptr(sw), _ptr(residual), epi,
+                           ctypes.byref(d), wsp, wsn, _stream(A)), "gemm_scaled")
+    return segs if segs is not None else out
+
+
+_GEMM_CACHE: dict = {}
+_GEMM_CACHE_MAX = 256
+
+
+def _sig(t):
+    """What the argument checks read of a tensor: shape, strides, dtype,
+    device and the pointer's alignment (TypeError for a non-tensor)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError
+    return (t.shape, t.stride(), t.dtype, t.device, t.data_ptr() & 15)
+
+
+def _prepare(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale,
+             a_kmajor, w_kmajor):
+    """Checks a gemm_scaled call without an output split and returns its
+    descriptor with the pointer fields cleared (as bytes), the epilogue code,
+    the shape of the output to allocate when none is given, and the
+    workspace bytes the library asks for."""
+    check_operands(A, sa, W, sw, fmt, epilogue, out, residual, tscale_a, tscale_w, scale_layout, bias_scale,
+                   None, a_kmajor, w_kmajor)
+    _need(A.is_cuda, "operands must be CUDA tensors")
+    d, epi, batched = make_desc(A, W, fmt, epilogue, out, residual, tscale_a, tscale_w, a_kmajor, w_kmajor)
+    d.scale_layout = _LAYOUT.get(scale_layout, scale_layout)
+    if bias_scale is not None:
+        d.bias_scale = bias_scale.data_ptr()
     nws = lib.gemm_scaled_workspace_bytes(ctypes.byref(d), epi)
-    if nws > 0 and (workspace is None or workspace.numel() < nws):
-        workspace = torch.empty((nws,), dtype=torch.uint8, device=A.device)
-    _check(lib.gemm_scaled(_ptr(out), _ptr(A), _ptr(sa), _ptr(W), _ptr(sw), _ptr(residual), epi,
-                           ctypes.byref(d), _ptr(workspace) if nws > 0 else None,
-                           workspace.numel() if (workspace is not None and nws > 0) else 0, _stream(A)),
-           "gemm_scaled")
-    return segs if split is not None else out
+    d.tscale_a = d.tscale_w = d.bias_scale = None
+    n_out = d.N // 2 if epi == EPI_SWIGLU else d.N
+    out_shape = (d.batch, d.M, n_out) if batched else (d.M, n_out)
+    return bytes(d), epi, out_shape, nws
 
 
 def gemm_workspace(A, W, fmt="e4m3_row", epilogue="store", out=None, residual=None, a_kmajor=False,
