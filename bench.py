@@ -38,12 +38,23 @@ HBM_GBS = 8000.0
 
 # the kernels of one gemm_scaled call (the GEMM, its split-K reduction) and
 # the planner that picks their launches (split, tail, grid), which changes
-# the traffic as much as the kernels do
+# the traffic as much as the kernels do; by the plan's kernel (0, 2: FP8
+# tiles, 1: NVFP4 tiles, 3: decode width)
+KERNEL_NAMES = {0: "gemm_fp8_kernel", 1: "gemm_nvfp4_kernel", 2: "gemm_fp8_kernel", 3: "gemm_narrow_kernel"}
 GEMM_SOURCES = {
-    "e4m3_row": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip", "spg_api.hip"],
-    "e4m3_tensor": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_splitk.hip", "spg_api.hip"],
-    "nvfp4": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h", "spg_splitk.hip", "spg_api.hip"],
+    "gemm_fp8_kernel": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_common.h", "spg_splitk.hip", "spg_api.hip"],
+    "gemm_nvfp4_kernel": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h", "spg_common.h", "spg_splitk.hip",
+                          "spg_api.hip"],
+    "gemm_narrow_kernel": ["spg_gemm_narrow.hip", "spg_gemm_common.h", "spg_common.h", "spg_api.hip"],
 }
+
+
+def kernel_of(wl) -> str:
+    """Name of the main GEMM kernel the planner picks for a workload (the
+    library's planner, called on the host; MI355X's 256 compute units)."""
+    import scaled_precision_gemm_amd as spg
+    p = spg.gemm_plan(wl.M, wl.N, wl.K, wl.fmt, wl.epilogue, batch=wl.batch, units=256)
+    return KERNEL_NAMES[p["kernel"]]
 
 
 def code_only(text: str) -> str:
@@ -54,11 +65,11 @@ def code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash(fmt: str, read=None) -> str:
-    """Hash of the GEMM kernel sources of a format, comments ignored.  `read`
+def kernel_source_hash(kname: str, read=None) -> str:
+    """Hash of the sources of a GEMM kernel's calls, comments ignored.  `read`
     maps a csrc file name to its text (default: the working tree)."""
     h = hashlib.sha256()
-    for f in GEMM_SOURCES[fmt]:
+    for f in GEMM_SOURCES[kname]:
         if read is None:
             with open(os.path.join(ROOT, "scaled_precision_gemm_amd", "csrc", f)) as fh:
                 text = fh.read()
@@ -117,7 +128,7 @@ def traffic_from_profiles(wl, name):
         rec = json.load(open(path)).get(name)
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(wl.fmt):
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(kernel_of(wl)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -155,7 +166,7 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
     share of the read requests addressed to memory (DRAM) rather than to
     another die or IO."""
     wl = WORKLOADS[name]
-    kname = "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel"
+    kname = kernel_of(wl)
     stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
     lines = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in stats:
@@ -255,7 +266,7 @@ def summarize_profiles(name, stats_dir, fetch_dir, write_dir, command="", counte
             l2["dram_share"] = l2["TCC_EA0_RDREQ_DRAM_sum"] / max(1.0, ea["TCC_EA0_RDREQ_sum"][0])
 
     rec = {
-        "kernel": kname, "workload": name, "kernel_source_hash": kernel_source_hash(wl.fmt),
+        "kernel": kname, "workload": name, "kernel_source_hash": kernel_source_hash(kname),
         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
         "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": gemm_bytes(wl),
         "fetch_scale": f_read, "write_scale": f_write, "rocprof_avg_call_us": timed_avg_us,
@@ -602,7 +613,7 @@ def main():
         achieved_v, peak_v, unit = achieved, peak, "TFLOP/s"
     roofline = {
         "bound": "hbm" if hbm_bound else "mfma",
-        "kernel": "gemm_nvfp4_kernel" if wl.fmt == "nvfp4" else "gemm_fp8_kernel",
+        "kernel": KERNEL_NAMES[plan["kernel"]],
         "achieved": round(achieved_v, 1),
         "peak": peak_v,
         "unit": unit,

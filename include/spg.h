@@ -347,7 +347,11 @@ int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t
  * than 64 tokens the tile geometry (256 x 256, or 128 x 256 over the whole
  * product) is chosen with the route model above: factor 1 for 256 x 256,
  * 1.9 for 128 x 256 (measured), the 256 x 256 route's partial last round
- * replaced by its tail.
+ * replaced by its tail.  Products of at most 32 tokens with at least 32
+ * blocks of 16 output columns (over the batch) take the decode-width kernel
+ * (kernel 3): one workgroup per 32 output columns (SWIGLU: 16), K split
+ * between its four waves and summed in LDS, no workspace (ninfer PR #160
+ * gives decode widths a GEMV route of their own).
  * Returns SPG_OK or the validation error gemm_scaled would return.  The
  * workspace holds one fp32 256x256 partial tile per split tile and slice.
  */
@@ -360,7 +364,11 @@ typedef struct spg_plan {
                              /* compute unit when the FP8 kernel runs an      */
                              /* unsplit product persistently                  */
     int32_t kernel;          /* 0: FP8 256 x 256 tiles; 1: NVFP4; 2: FP8      */
-                             /* 128 x 256 tiles (bm = 128) over the product   */
+                             /* 128 x 256 tiles (bm = 128) over the product;  */
+                             /* 3: decode width (both formats; bm = 16 or 32  */
+                             /* tokens, bn = 32 output columns, 16 for        */
+                             /* SWIGLU; tiles = workgroups =                  */
+                             /* batch * ceil(columns / bn))                   */
     int32_t tail_split;      /* > 1: the last tail_tiles tiles run in a second */
                              /* launch split tail_split ways along K (whole   */
                              /* rounds of tiles stay unsplit), else 1         */

@@ -161,10 +161,42 @@ double route_cost(const spg_route_candidate &c, int64_t M, int64_t N, int64_t ba
 constexpr spg_route_candidate kFullTile = {256, 256, 1, 1.0};
 constexpr spg_route_candidate kHalfTile = {128, 256, 1, 1.9};
 
-void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p)
+// The decode-width kernel for products of at most 32 tokens (kernel 3): one
+// workgroup per 16 output columns and batch entry, so it needs enough
+// columns to spread the weight stream (at least 32 workgroups; below that
+// the tiled route's K split gives more).  Its buffer ranges are 32-bit: a
+// blocked NVFP4 scale plane is addressed whole.  NVFP4 scale words are
+// copied 4 bytes at a time: K % 64 == 0 (whole words per row) and, for
+// row-major planes, 4-byte aligned planes (checked by the caller, which
+// has the pointers: `aligned_scales`).
+bool narrow_route(const spg_gemm_desc *d, int64_t nout, bool aligned_scales = true)
+{
+    if (d->M < 1 || d->M > 32 || d->K <= 0) return false;
+    if (d->format == SPG_FMT_NVFP4 && (d->K % 64 != 0 || !aligned_scales)) return false;
+    const int64_t blocks = d->batch * cdiv(nout, 16);
+    if (blocks < 32 || blocks >= (INT64_C(1) << 31)) return false;
+    if (d->format == SPG_FMT_NVFP4 && d->scale_layout == SPG_SCALES_BLOCKED &&
+        cdiv(d->N, 256) * (d->K / 256) * 4096 >= (INT64_C(1) << 31))
+        return false;
+    return true;
+}
+
+void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p, bool aligned_scales = true)
 {
     memset(p, 0, sizeof(*p));
     const int64_t nout = n_out_of(d, epi);
+    if (narrow_route(d, nout, aligned_scales)) {
+        p->kernel = 3;
+        p->bm = d->M <= 16 ? 16 : 32;
+        p->bn = narrow_cols(epi);
+        p->bk = d->format == SPG_FMT_NVFP4 ? 256 : 128;
+        p->split_k = 1;
+        p->tiles = d->batch * cdiv(nout, p->bn);
+        p->workgroups = p->tiles;
+        p->tail_split = 1;
+        p->tail_bm = (int32_t)kTile;
+        return;
+    }
     p->bm = (int32_t)kTile;
     p->bn = (int32_t)kTile;   // weight rows per tile (SWIGLU: 128 gate + 128 up)
     // K elements per pipeline stage: FP8 128; NVFP4 256 (copied straight into
@@ -342,9 +374,13 @@ SPG_EXPORT int spg_gemm_plan(const spg_gemm_desc *d, int epilogue, int32_t units
 SPG_EXPORT size_t gemm_scaled_workspace_bytes(const spg_gemm_desc *d, int epilogue)
 {
     if (validate_desc(d, epilogue) != SPG_OK) return 0;
-    spg_plan p;
-    make_plan(d, epilogue, device_units(), &p);
-    return transpose_bytes(d, nullptr) + plan_workspace(&p);
+    // enough for either plan of a call: the scale planes' alignment (known
+    // only at the call) can take an NVFP4 product off the decode-width route
+    spg_plan p, q;
+    make_plan(d, epilogue, device_units(), &p, true);
+    make_plan(d, epilogue, device_units(), &q, false);
+    const size_t w = plan_workspace(&p) > plan_workspace(&q) ? plan_workspace(&p) : plan_workspace(&q);
+    return transpose_bytes(d, nullptr) + w;
 }
 
 // A bf16 output region [o0, o1): one matrix (or segment) of a call.
@@ -436,7 +472,7 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     if (((uintptr_t)d->clock_probe & 7u) != 0) return SPG_EINVAL;
 
     spg_plan p;
-    make_plan(d, epilogue, device_units(), &p);
+    make_plan(d, epilogue, device_units(), &p, aligned4(sa) && aligned4(sw));
     size_t t_a = 0;
     const size_t t_bytes = transpose_bytes(d, &t_a);
     const size_t need = t_bytes + plan_workspace(&p);
@@ -520,6 +556,12 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
     g.div_span = make_fastdiv((uint32_t)(8 * g.tiles_n));
     g.div_gm_last = make_fastdiv(g.tiles_m % 8 ? (uint32_t)(g.tiles_m % 8) : 8u);
     if (p.split_k > 1) g.partials = (float *)((uint8_t *)ws + t_bytes);
+    if (p.kernel == 3) {
+        g.tiles_m = 1;
+        g.tiles_n = cdiv(nout, narrow_cols(epilogue));
+        g.clocks = d->clock_probe;
+        return launch_gemm_narrow(g, s) == hipSuccess ? SPG_OK : SPG_EHIP;
+    }
     g.tile_begin = 0;
     g.tile_count = p.tiles - p.tail_tiles;
     auto launch = [&](const GemmArgs &a, const spg_plan &q) {

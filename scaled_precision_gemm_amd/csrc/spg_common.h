@@ -188,6 +188,14 @@ inline FastDiv make_fastdiv(uint32_t d)
 hipError_t launch_gemm_fp8(const GemmArgs &g, const spg_plan &p, hipStream_t s);
 hipError_t launch_gemm_fp8_half(const GemmArgs &g, hipStream_t s);   // tiles tile_begin.. as 128-row halves
 hipError_t launch_gemm_nvfp4(const GemmArgs &g, const spg_plan &p, hipStream_t s);
+// Products of at most 32 tokens: one workgroup per narrow_cols(epilogue)
+// output columns (g.tiles_n column blocks per product) and batch entry.
+// SWIGLU blocks carry 16 gate and 16 up rows; the others 32 weight rows, so
+// each token fragment a wave reads serves two weight fragments (measured on
+// 16 x 5120 x 17408: 20 us against 24 with 16 columns; the SwiGLU prefers
+// 16: 37 against 44).
+constexpr int narrow_cols(int epilogue) { return epilogue == SPG_EPI_SWIGLU ? 16 : 32; }
+hipError_t launch_gemm_narrow(const GemmArgs &g, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs &g, int64_t tiles, hipStream_t s);
 // [R, C] codes (row stride ld, batch stride bstride, 16-byte aligned rows)
 // -> [C, R] with row stride R (R % 16 == 0), batch entries R * C apart.

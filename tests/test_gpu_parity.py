@@ -743,7 +743,8 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
 
 BIAS = [((128, 256, 512), "e4m3_row", 1), ((300, 258, 1040), "e4m3_tensor", 1), ((17, 34, 48), "e4m3_row", 1),
         ((2304, 7936, 256), "e4m3_row", 1), ((520, 1030, 2064), "e4m3_row", 1), ((16, 5120, 17408), "e4m3_row", 1),
-        ((96, 300, 512), "e4m3_tensor", 3), ((257, 300, 512), "nvfp4", 1), ((64, 64, 256), "nvfp4", 1)]
+        ((96, 300, 512), "e4m3_tensor", 3), ((257, 300, 512), "nvfp4", 1), ((64, 64, 256), "nvfp4", 1),
+        ((20, 1000, 1040), "e4m3_row", 1), ((8, 520, 512), "nvfp4", 1), ((6, 520, 256), "e4m3_tensor", 2)]
 
 
 @pytest.mark.parametrize("shape,fmt,B", BIAS, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
@@ -896,7 +897,10 @@ SPLITS = [((300, 640, 512), "e4m3_row", "store", (256, 256, 128), 1),
           ((300, 1280, 512), "e4m3_row", "swiglu", (384, 256), 1),
           ((520, 1030, 1024), "e4m3_row", "add", (512, 448, 70), 1),
           ((96, 300, 512), "e4m3_tensor", "store", (256, 44), 2),
-          ((257, 640, 512), "nvfp4", "store", (64, 512, 64), 1)]
+          ((257, 640, 512), "nvfp4", "store", (64, 512, 64), 1),
+          ((20, 1280, 1024), "e4m3_row", "swiglu", (384, 256), 1),
+          ((8, 640, 512), "nvfp4", "store", (64, 512, 64), 1),
+          ((4, 1100, 256), "e4m3_row", "add", (512, 448, 140), 1)]
 
 
 @pytest.mark.parametrize("shape,fmt,epi,widths,B", SPLITS,
@@ -1050,10 +1054,15 @@ def test_gemm_kmajor_operands(spg, shape, fmt, epi, km, B):
 
 
 # ---------------------------------------------------------------------------
-# few tokens (M <= 64, decode widths): one partly filled tile row, K split
-# over many slices; the instantiations for at most 32 and at most 64 tokens.  Ragged N (SwiGLU halves that are not a multiple of 4
-# columns), K not a multiple of 64, one to 32 tokens, per-tensor batches with
-# a broadcast weight, and the two prefill linears at 16 tokens.
+# few tokens (M <= 64).  At most 32 tokens with at least 32 blocks of 16
+# output columns: the decode-width kernel (one workgroup per 16 columns, K
+# split over its waves) - one and two token blocks (M <= 16, 17..32), ragged
+# column blocks (SwiGLU halves that are not a multiple of 4 columns), K
+# tails inside a 128-byte chunk and K below one chunk (waves without work).
+# Otherwise the tiled few-token route: one partly filled tile row, K split
+# over many slices (instantiations for at most 32 and at most 64 tokens).
+# Per-tensor batches with a broadcast or a per-batch weight, and the two
+# prefill linears at 16 tokens.
 # ---------------------------------------------------------------------------
 
 NARROW = [((1, 64, 256), "store", "e4m3_row"), ((5, 200, 1040), "add", "e4m3_row"),
@@ -1061,7 +1070,10 @@ NARROW = [((1, 64, 256), "store", "e4m3_row"), ((5, 200, 1040), "add", "e4m3_row
           ((32, 520, 2048), "add", "e4m3_tensor"), ((7, 34, 48), "swiglu", "e4m3_tensor"),
           ((16, 5120, 17408), "add", "e4m3_row"), ((16, 34816, 5120), "swiglu", "e4m3_row"),
           ((33, 300, 1040), "store", "e4m3_row"), ((48, 2060, 528), "swiglu", "e4m3_tensor"),
-          ((64, 5120, 4096), "add", "e4m3_row")]
+          ((64, 5120, 4096), "add", "e4m3_row"),
+          ((1, 1000, 1040), "store", "e4m3_row"), ((17, 600, 4112), "add", "e4m3_row"),
+          ((5, 1034, 528), "swiglu", "e4m3_tensor"), ((32, 1024, 128), "swiglu", "e4m3_row"),
+          ((24, 700, 80), "add", "e4m3_tensor"), ((2, 4096, 16), "store", "e4m3_row")]
 
 
 @pytest.mark.parametrize("shape,epi,fmt", NARROW, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
@@ -1077,8 +1089,9 @@ def test_gemm_narrow(spg, shape, epi, fmt):
     check_close(gpu, ref["y"], ref["S"], f"narrow {shape} {epi} {fmt}")
 
 
-def test_gemm_narrow_batched_broadcast_and_deterministic(spg):
-    B, M, N, K = 3, 9, 300, 1536
+@pytest.mark.parametrize("N", [300, 600], ids=["tiled", "decode_width"])
+def test_gemm_narrow_batched_broadcast_and_deterministic(spg, N):
+    B, M, K = 3, 9, 1536
     A16 = bf16_normal((B, M, K), 1.0, 91)
     W16 = bf16_normal((N, K), 0.02, 92)
     qa, sa = spg.quantize_tensor(dev(A16))
@@ -1094,11 +1107,34 @@ def test_gemm_narrow_batched_broadcast_and_deterministic(spg):
         check_close(out1[b], y, S, f"narrow batch {b}")
 
 
+def test_gemm_narrow_batched_per_batch_weights(spg):
+    # per-tensor products with a weight of their own per batch entry
+    B, M, N, K = 2, 4, 512, 640
+    A16 = bf16_normal((B, M, K), 1.0, 93)
+    W16 = bf16_normal((B, N, K), 0.02, 94)
+    assert spg.gemm_plan(M, N, K, "e4m3_tensor", "store", batch=B)["kernel"] == 3
+    qa, sa = spg.quantize_tensor(dev(A16))
+    qw, sw = spg.quantize_tensor(dev(W16))
+    out = host_u16(spg.gemm_scaled(qa, sa, qw, sw, "store", fmt="e4m3_tensor"))
+    for b in range(B):
+        qao, sao = oracle.quantize_tensor(A16[b])
+        qwo, swo = oracle.quantize_tensor(W16[b])
+        D, Da = oracle.gemm_e4m3_sums(qao, qwo)
+        y, S, _ = oracle.epilogue("store", D, Da, sao[0], swo[0])
+        check_close(out[b], y, S, f"narrow per-batch weight {b}")
+
+
 NARROW_NVFP4 = [((1, 64, 256), "store", "row"), ((5, 200, 1024), "add", "blocked"),
                 ((16, 2060, 512), "swiglu", "row"), ((31, 520, 2048), "store", "blocked"),
                 ((16, 5120, 6144), "add", "blocked"), ((16, 34816, 5120), "swiglu", "blocked"),
                 ((33, 300, 1024), "store", "row"), ((64, 2048, 4096), "add", "blocked"),
-                ((7, 400, 512), "swiglu", "row"), ((48, 520, 1056), "store", "row")]
+                ((7, 400, 512), "swiglu", "row"), ((48, 520, 1056), "store", "row"),
+                # decode-width kernel (K % 64 == 0): K tails inside a chunk,
+                # two token blocks; K % 64 != 0 stays on the tiled route
+                ((1, 1000, 1056), "store", "row"), ((20, 1034, 96), "swiglu", "row"),
+                ((9, 520, 768), "add", "blocked"), ((32, 2048, 256), "add", "row"),
+                ((16, 5120, 6144), "add", "row"), ((5, 1000, 320), "swiglu", "row"),
+                ((3, 1024, 64), "store", "row")]
 
 
 @pytest.mark.parametrize("shape,epi,layout", NARROW_NVFP4, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
@@ -1126,7 +1162,7 @@ def test_gemm_nvfp4_narrow(spg, shape, epi, layout):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K,epi", [(300, 260, 320, "add"), (1000, 1030, 4096, "add"), (16, 520, 2080, "swiglu"),
-                                       (130, 264, 512, "store")])
+                                       (130, 264, 512, "store"), (16, 1040, 2080, "swiglu"), (7, 600, 528, "add")])
 def test_gemm_padded_leading_dimensions(spg, M, N, K, epi):
     A16 = bf16_normal((M, K), 1.0, M + 11)
     W16 = bf16_normal((N, K), 0.02, N + 13)
@@ -1163,7 +1199,8 @@ def test_gemm_padded_leading_dimensions(spg, M, N, K, epi):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K,epi", [(321, 1345, 512, "store"), (1153, 321, 1040, "add"), (1345, 2 * 1153, 256, "swiglu"),
-                                       (4001, 321, 128, "add"), (33, 4001, 2064, "store")])
+                                       (4001, 321, 128, "add"), (33, 4001, 2064, "store"),
+                                       (16, 1345, 1040, "add"), (32, 2 * 1153, 256, "swiglu")])
 def test_gemm_page_tail_widths_with_guard_bands(spg, M, N, K, epi):
     A16 = bf16_normal((M, K), 1.0, M * 3 + 1)
     W16 = bf16_normal((N, K), 0.02, N * 5 + 2)

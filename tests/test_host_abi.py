@@ -411,23 +411,37 @@ def test_plans_for_the_workloads(spg):
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (16 * 136, 1, 256)
     p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu", units=304)
     assert p["workgroups"] == 304
-    # 16 tokens: the weight-streaming cost model (waves * (slice + 1024))
+    # at most 32 tokens: the decode-width kernel, one workgroup per 32 output
+    # columns (SwiGLU: 16 columns, 16 gate + 16 up rows), no K split, no
+    # workspace
+    p = spg.gemm_plan(16, 34816, 5120, "e4m3_row", "swiglu")
+    assert (p["kernel"], p["bm"], p["bn"], p["tiles"], p["split_k"], p["workgroups"]) == (3, 16, 16, 1088, 1, 1088)
+    p = spg.gemm_plan(16, 5120, 17408, "e4m3_row", "add")
+    assert (p["kernel"], p["bn"], p["tiles"], p["split_k"], p["workgroups"]) == (3, 32, 160, 1, 160)
+    p = spg.gemm_plan(32, 5120, 6144, "nvfp4", "add")
+    assert (p["kernel"], p["bm"], p["bk"], p["workgroups"]) == (3, 32, 256, 160)
+    # NVFP4 with K % 64 != 0 (scale rows of whole 4-byte words only): tiled
+    assert spg.gemm_plan(16, 5120, 6176, "nvfp4", "add")["kernel"] == 1
+    # fewer than 32 column blocks: the tiled route
+    assert spg.gemm_plan(16, 496, 512, "e4m3_row", "store")["kernel"] == 0
+    assert spg.gemm_plan(1, 512, 512, "e4m3_tensor", "store")["kernel"] == 3
+    # 33 to 64 tokens: the weight-streaming cost model (waves * (slice + 1024))
     # picks 3 slices for the SwiGLU (408 workgroups, 1.6 waves beat 2.7 at
     # 5 slices) and keeps 8 for the down-projection (one wave of 160)
-    p = spg.gemm_plan(16, 34816, 5120, "e4m3_row", "swiglu")
+    p = spg.gemm_plan(48, 34816, 5120, "e4m3_row", "swiglu")
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (136, 3, 408)
-    p = spg.gemm_plan(16, 5120, 17408, "e4m3_row", "add")
+    p = spg.gemm_plan(48, 5120, 17408, "e4m3_row", "add")
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (20, 8, 160)
-    # NVFP4 at 16 tokens (fast path, K % 256 == 0) takes the weight-streaming
+    # NVFP4 at 48 tokens (fast path, K % 256 == 0) takes the weight-streaming
     # model too; with K % 256 != 0 (general path) the wave-quantised one
-    p = spg.gemm_plan(16, 34816, 5120, "nvfp4", "swiglu")
+    p = spg.gemm_plan(48, 34816, 5120, "nvfp4", "swiglu")
     assert (p["split_k"], p["workgroups"]) == (3, 408)
-    p = spg.gemm_plan(16, 34816, 5152, "nvfp4", "swiglu")
+    p = spg.gemm_plan(48, 34816, 5152, "nvfp4", "swiglu")
     assert p["split_k"] == 5
     # no K slice is ever empty
     for K in (8448, 9472, 12544, 14080):
         for fmt in ("nvfp4", "e4m3_row"):
-            p = spg.gemm_plan(16, 5120, K, fmt, "add")
+            p = spg.gemm_plan(48, 5120, K, fmt, "add")
             s, bk = p["split_k"], p["bk"]
             chunk = -(-(-(-K // s)) // bk) * bk
             assert (s - 1) * chunk < K, (K, fmt, s)
@@ -556,8 +570,12 @@ MI355X_PLANS = [
     ((4096, 5120, 6144, "nvfp4", "add", 1), (1, 256, 1, 64, 4, 256)),        # NVFP4: K-split tail
     ((8192, 8192, 8192, "e4m3_tensor", "store", 1), (0, 256, 1, 0, 1, 256)),
     ((512, 512, 512, "e4m3_tensor", "store", 64), (0, 256, 1, 0, 1, 256)),
-    ((16, 5120, 17408, "e4m3_row", "add", 1), (0, 256, 8, 0, 1, 256)),       # few tokens: split model
-    ((16, 34816, 5120, "e4m3_row", "swiglu", 1), (0, 256, 3, 0, 1, 256)),
+    ((48, 5120, 17408, "e4m3_row", "add", 1), (0, 256, 8, 0, 1, 256)),       # 33-64 tokens: split model
+    ((48, 34816, 5120, "e4m3_row", "swiglu", 1), (0, 256, 3, 0, 1, 256)),
+    ((16, 5120, 17408, "e4m3_row", "add", 1), (3, 16, 1, 0, 1, 256)),        # decode widths
+    ((16, 34816, 5120, "e4m3_row", "swiglu", 1), (3, 16, 1, 0, 1, 256)),
+    ((16, 5120, 6144, "nvfp4", "add", 1), (3, 16, 1, 0, 1, 256)),
+    ((32, 34816, 5120, "nvfp4", "swiglu", 1), (3, 32, 1, 0, 1, 256)),
 ]
 
 
