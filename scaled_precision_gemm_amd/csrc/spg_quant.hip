@@ -262,29 +262,86 @@ __global__ __launch_bounds__(kThreads) void quant_tensor_encode_kernel(
 // NVFP4 encode of one 16-element group given the tensor scale t: the block
 // scale code b = E4M3(fl32(amax_g / fl32(6 t))), e = fl32(dec(b) t), and the
 // eight packed code bytes of E2M1(fl32(x / e)) (a zero e gives signed zeros).
-// Both NVFP4 quantize kernels use it, so their codes are identical.
+// Both NVFP4 quantize kernels use these, so their codes are identical.
 // ---------------------------------------------------------------------------
+
+// The E2M1 code of fl32(x / e) from y = fl32(1 / e) (one IEEE division per
+// group instead of one per element): q0 = fl32(x y) is within one ulp of
+// x / e, the residual x - q0 e is exact (an FMA), and fl32(q0 + r y) is the
+// correctly rounded quotient (Markstein's theorem on division by a correctly
+// rounded reciprocal, binary arithmetic without underflow or overflow); the
+// sign is restored for zeros.  Taken for e in [2^-100, 2^100]; the
+// quotients of a group are at most about 12 in magnitude (e is the group
+// maximum over 6, rounded to E4M3), so they never overflow, and where x is
+// tiny or subnormal an inexact residual can only move a quotient that is
+// far below the first E2M1 rounding boundary (0.25).  Checked against the
+// division on the CPU: the E2M1 codes agree for every bf16 x (zeros and
+// subnormals included) with 38k divisors e = fl32(dec(b) t) over the whole
+// range (1.9e9 cases).  Other e take the division.
+__device__ __forceinline__ float div_rn(float x, float e, float y, bool fast_e)
+{
+#pragma clang fp contract(off)
+    if (fast_e) {
+        const float q0 = x * y;
+        const float r = __builtin_fmaf(-q0, e, x);
+        return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
+    }
+    return x / e;
+}
+
+// Block scale code and element divisor of a group with maximum magnitude
+// bits gm (bf16 bits << 16).
+struct GroupScale {
+    uint32_t b;
+    float e, y;
+    bool fast;
+};
+
+__device__ __forceinline__ GroupScale group_scale(uint32_t gm, float t, float six_t)
+{
+    GroupScale s;
+    s.b = 0;
+    if (t > 0.0f) s.b = encode_e4m3(__uint_as_float(gm << 16) / six_t);
+    s.e = decode_e4m3(s.b) * t;
+    s.fast = s.e >= 0x1p-100f && s.e <= 0x1p100f;
+    s.y = s.fast ? 1.0f / s.e : 0.0f;
+    return s;
+}
+
+// E2M1 codes of eight elements (one 16-byte vector of bf16), packed low
+// nibble first: four bytes.  The rounding to E2M1 is v_cvt_scalef32_pk_fp4_f32
+// with scale 1 (two quotients per instruction): round to nearest even,
+// saturating at +-6, signed zeros kept - the same code as encode_e2m1 for
+// every binary32 input that is not a NaN (checked exhaustively on the GPU,
+// all 2^32 inputs; the quotients here are finite).
+__device__ __forceinline__ uint32_t encode_half8(const uint4 &v, const GroupScale &s)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (!(s.e > 0.0f)) {   // zero scale: signed zeros
+        uint32_t packed = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            packed |= (((w[i] >> 12) & 0x8u) | (((w[i] >> 28) & 0x8u) << 4)) << (8 * i);
+        return packed;
+    }
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = div_rn(bf16_lo(w[i]), s.e, s.y, s.fast);
+        f[2 * i + 1] = div_rn(bf16_hi(w[i]), s.e, s.y, s.fast);
+    }
+    uint32_t packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], 1.0f, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, f[2], f[3], 1.0f, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, f[4], f[5], 1.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, f[6], f[7], 1.0f, 3);
+}
+
 __device__ __forceinline__ void encode_group16(const uint4 &v0, const uint4 &v1, uint32_t gm, float t, float six_t,
                                                uint2 &codes, uint32_t &b)
 {
-    b = 0;
-    if (t > 0.0f) b = encode_e4m3(__uint_as_float(gm << 16) / six_t);
-    const float e = decode_e4m3(b) * t;
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t c0, c1;
-        if (e > 0.0f) {
-            c0 = encode_e2m1(bf16_lo(w[i]) / e);
-            c1 = encode_e2m1(bf16_hi(w[i]) / e);
-        } else {
-            c0 = (w[i] >> 12) & 0x8u;
-            c1 = (w[i] >> 28) & 0x8u;
-        }
-        packed[i >> 2] |= (c0 | (c1 << 4)) << (8 * (i & 3));
-    }
-    codes = make_uint2(packed[0], packed[1]);
+    const GroupScale s = group_scale(gm, t, six_t);
+    b = s.b;
+    codes = make_uint2(encode_half8(v0, s), encode_half8(v1, s));
 }
 
 // Byte offset of block scale (row, group g) in the scale plane.  Row-major:
@@ -299,10 +356,16 @@ __device__ __forceinline__ uint64_t scale_offset(uint32_t row, uint32_t g, uint3
     return ((uint64_t)(row >> 8) * (G >> 4) + (g >> 4)) * 4096u + (row & 255u) * 16u + (g & 15u);
 }
 
-// Two-pass NVFP4, pass 2: fold the partial maxima into t, then one thread per
-// 16-element group (two 16-byte loads, one 8-byte code store, one scale
-// byte).  Work items past the tensor's groups (groups .. groups_pad) write
-// the zero scale bytes of the padding rows of a blocked plane.
+// Two-pass NVFP4, pass 2: fold the partial maxima into t, then encode.  A
+// wave takes 64 groups per trip in two windows of 32: lane l loads half
+// l % 2 of group l / 2 of each window (16 bytes at 16 l: every load covers
+// 1 KiB of whole lines), the lane pair exchanges half-group maxima, the even
+// lane forms the scale of its window-0 group and the odd lane that of its
+// window-1 group, and they exchange those, so each group's scale is formed
+// once.  Each lane stores the four code bytes of its two halves; the even
+// lane stores window 0's scale byte, the odd lane window 1's.  Groups past
+// the tensor (groups .. groups_pad) get the zero scale bytes of the padding
+// rows of a blocked plane.
 __global__ __launch_bounds__(kThreads) void quant_block16_encode_kernel(
     const uint16_t *__restrict__ x, int64_t groups, int64_t groups_pad, FastDiv div_g, uint32_t G, int layout,
     const uint32_t *__restrict__ partial, int64_t parts, uint8_t *__restrict__ q, uint8_t *__restrict__ bscale,
@@ -313,17 +376,32 @@ __global__ __launch_bounds__(kThreads) void quant_block16_encode_kernel(
     const float t = __uint_as_float(m << 16) / 2688.0f;
     const float six_t = 6.0f * t;
     if (blockIdx.x == 0 && threadIdx.x == 0) *tscale = t;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups_pad;
-         g += (int64_t)gridDim.x * kThreads) {
-        const uint32_t row = fdiv_q((uint32_t)g, div_g), col = (uint32_t)g - row * G;
-        uint32_t b = 0;
-        if (g < groups) {
-            const uint4 v0 = ld16(x + g * 16), v1 = ld16(x + g * 16 + 8);
-            uint2 codes;
-            encode_group16(v0, v1, max(amax8(v0), amax8(v1)), t, six_t, codes, b);
-            *reinterpret_cast<uint2 *>(q + g * 8) = codes;
+    const int lane = threadIdx.x & 63, h = lane & 1;
+    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t base = wave * 64; base < groups_pad; base += waves * 64) {
+        const int64_t g0 = base + (lane >> 1), g1 = g0 + 32;
+        const bool in0 = g0 < groups, in1 = g1 < groups;
+        const uint4 v0 = in0 ? ld16(x + g0 * 16 + h * 8) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 v1 = in1 ? ld16(x + g1 * 16 + h * 8) : make_uint4(0u, 0u, 0u, 0u);
+        uint32_t m0 = amax8(v0), m1 = amax8(v1);
+        m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 1, 64));
+        m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 1, 64));
+        // this lane's group: window h; the partner's: the other window
+        const GroupScale mine = group_scale(h ? m1 : m0, t, six_t);
+        GroupScale other;
+        other.b = (uint32_t)__shfl_xor((int)mine.b, 1, 64);
+        other.e = __shfl_xor(mine.e, 1, 64);
+        other.y = __shfl_xor(mine.y, 1, 64);
+        other.fast = __shfl_xor((int)mine.fast, 1, 64) != 0;
+        const GroupScale &s0 = h ? other : mine, &s1 = h ? mine : other;
+        if (in0) *reinterpret_cast<uint32_t *>(q + g0 * 8 + h * 4) = encode_half8(v0, s0);
+        if (in1) *reinterpret_cast<uint32_t *>(q + g1 * 8 + h * 4) = encode_half8(v1, s1);
+        const int64_t gs = h ? g1 : g0;
+        if (gs < groups_pad) {
+            const uint32_t row = fdiv_q((uint32_t)gs, div_g), col = (uint32_t)gs - row * G;
+            bscale[scale_offset(row, col, G, layout)] = (gs < groups) ? (uint8_t)mine.b : (uint8_t)0;
         }
-        bscale[scale_offset(row, col, G, layout)] = (uint8_t)b;
     }
 }
 
