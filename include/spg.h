@@ -408,6 +408,19 @@ int spg_probe_mfma(int kind, int64_t iters, int32_t workgroups, float *sink, uin
 
 int spg_probe_read(const void *src, int64_t bytes, int32_t workgroups, uint32_t *sink, void *stream);
 
+/*
+ * spg_probe_fp4_rounding: the NVFP4 quantizers round quotients to E2M1 with
+ * the conversion instruction v_cvt_scalef32_pk_fp4_f32 (scale 1); ninfer PR
+ * #160's format needs round-to-nearest-even with saturation at +-6 and the
+ * sign of zero kept.  This probe converts every binary32 value that is not a
+ * NaN with the instruction and with the library's bit-level E2M1 encoder and
+ * counts the differences.  result: device, 34 x uint32 (4-byte aligned),
+ * written on `stream`: [0] the number of differences, [1] how many were
+ * recorded, then up to 16 pairs (input bits, instruction code | encoder code
+ * << 8).  SPG_EINVAL for a null or misaligned result.
+ */
+int spg_probe_fp4_rounding(uint32_t *result, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

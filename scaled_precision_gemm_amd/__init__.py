@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "quantize_rowwise", "quantize_tensor", "quantize_block16", "gemm_scaled",
-    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read",
+    "gemm_plan", "gemm_workspace", "route_select", "route_cost", "probe_mfma", "probe_read", "probe_fp4_rounding",
     "lib", "LIB_PATH",
     "FMT_E4M3_ROW", "FMT_E4M3_TENSOR", "FMT_NVFP4", "EPI_STORE", "EPI_ADD", "EPI_SWIGLU",
     "SpgError", "check_operands", "block16_scale_shape", "SCALES_ROW_MAJOR", "SCALES_BLOCKED", "QUANT_SINGLE_LAUNCH",
@@ -97,6 +97,7 @@ SIGNATURES = {
     "spg_gemm_plan": (ctypes.c_int, [ctypes.POINTER(GemmDesc), ctypes.c_int, _I32, ctypes.POINTER(Plan)]),
     "spg_probe_mfma": (ctypes.c_int, [ctypes.c_int, _I64, _I32, _P, _P, _P]),
     "spg_probe_read": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "spg_probe_fp4_rounding": (ctypes.c_int, [_P, _P]),
 }
 
 
@@ -532,6 +533,16 @@ def probe_mfma(kind: int, iters: int, workgroups: int, device="cuda"):
     clocks = torch.zeros((4,), dtype=torch.int64, device=device)
     _check(lib.spg_probe_mfma(kind, iters, workgroups, _ptr(sink), _ptr(clocks), _stream(sink)), "spg_probe_mfma")
     return sink, clocks, workgroups * 4 * iters * 4 * PROBE_MFMA_FLOPS[kind]
+
+
+def probe_fp4_rounding(device="cuda") -> dict:
+    """Compare the E2M1 conversion instruction with the library's encoder on
+    every non-NaN binary32 input (see spg_probe_fp4_rounding)."""
+    res = torch.empty((34,), dtype=torch.int32, device=device)
+    _check(lib.spg_probe_fp4_rounding(_ptr(res), _stream(res)), "spg_probe_fp4_rounding")
+    h = res.cpu().numpy().view("uint32")
+    n = int(min(h[1], 16))
+    return {"differences": int(h[0]), "examples": [(int(h[2 + 2 * k]), int(h[3 + 2 * k])) for k in range(n)]}
 
 
 def probe_read(buf: torch.Tensor, workgroups: int):

@@ -14,6 +14,10 @@
 //  * HBM read: a grid-stride stream of 16-byte loads over a buffer larger
 //    than the last-level cache, folded with XOR into one word per thread (the
 //    folded words are checkable against the buffer).
+//  * FP4 rounding: the NVFP4 quantizers round quotients to E2M1 with
+//    v_cvt_scalef32_pk_fp4_f32 (scale 1); this probe compares that
+//    instruction with the library's E2M1 encoder for every binary32 input
+//    that is not a NaN (2^32 - 2^24 values) and counts the differences.
 #include "spg_common.h"
 
 namespace spg {
@@ -116,11 +120,56 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const v4i *__
     sink[tid] = x;
 }
 
+__global__ __launch_bounds__(64) void probe_clear_kernel(uint32_t *out, int n)
+{
+    if ((int)threadIdx.x < n) out[threadIdx.x] = 0u;
+}
+
+// Thread t checks the 256 inputs 256 t .. 256 t + 255 (two per conversion);
+// out[0] counts differences, out[1] the recorded ones, and the first 16 are
+// kept as (input bits, instruction code | encoder code << 8).
+__global__ __launch_bounds__(kProbeThreads) void probe_fp4_kernel(uint32_t *out)
+{
+    const uint32_t u0 = (uint32_t)(((uint64_t)blockIdx.x * kProbeThreads + threadIdx.x) * 256u);
+    uint32_t bad = 0;
+    for (uint32_t i = 0; i < 256; i += 2) {
+        const uint32_t ua = u0 + i, ub = ua + 1;
+        const uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, __uint_as_float(ua), __uint_as_float(ub),
+                                                                    1.0f, 0);
+        const uint32_t us[2] = {ua, ub};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if ((us[j] & 0x7FFFFFFFu) > 0x7F800000u) continue;   // NaN
+            const uint32_t got = (r >> (4 * j)) & 0xFu, want = encode_e2m1(__uint_as_float(us[j]));
+            if (got != want) {
+                ++bad;
+                const uint32_t k = atomicAdd(&out[1], 1u);
+                if (k < 16) {
+                    out[2 + 2 * k] = us[j];
+                    out[3 + 2 * k] = got | (want << 8);
+                }
+            }
+        }
+    }
+    if (bad) atomicAdd(&out[0], bad);
+}
+
 }  // namespace
 
 }  // namespace spg
 
 using namespace spg;
+
+SPG_EXPORT int spg_probe_fp4_rounding(uint32_t *result, void *stream)
+{
+    if (!result || ((uintptr_t)result & 3)) return SPG_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    probe_clear_kernel<<<1, 64, 0, s>>>(result, 34);
+    if (hipGetLastError() != hipSuccess) return SPG_EHIP;
+    // 65536 workgroups x 256 threads x 256 inputs = every 32-bit pattern
+    probe_fp4_kernel<<<dim3(65536), kProbeThreads, 0, s>>>(result);
+    return hipGetLastError() == hipSuccess ? SPG_OK : SPG_EHIP;
+}
 
 SPG_EXPORT int spg_probe_mfma(int kind, int64_t iters, int32_t workgroups, float *sink, uint64_t *clocks,
                               void *stream)

@@ -274,10 +274,11 @@ __global__ __launch_bounds__(kThreads) void quant_tensor_encode_kernel(
 // quotients of a group are at most about 12 in magnitude (e is the group
 // maximum over 6, rounded to E4M3), so they never overflow, and where x is
 // tiny or subnormal an inexact residual can only move a quotient that is
-// far below the first E2M1 rounding boundary (0.25).  Checked against the
-// division on the CPU: the E2M1 codes agree for every bf16 x (zeros and
-// subnormals included) with 38k divisors e = fl32(dec(b) t) over the whole
-// range (1.9e9 cases).  Other e take the division.
+// far below the first E2M1 rounding boundary (0.25).  The E2M1 codes agree
+// with those of the division for every bf16 x (zeros and subnormals
+// included) over divisors e = fl32(dec(b) t) across the whole range
+// (tests/arith/reciprocal_division.c; 1.9e9 cases run once, 4e7 in the CPU
+// test suite).  Other e take the division.
 __device__ __forceinline__ float div_rn(float x, float e, float y, bool fast_e)
 {
 #pragma clang fp contract(off)
@@ -312,8 +313,8 @@ __device__ __forceinline__ GroupScale group_scale(uint32_t gm, float t, float si
 // nibble first: four bytes.  The rounding to E2M1 is v_cvt_scalef32_pk_fp4_f32
 // with scale 1 (two quotients per instruction): round to nearest even,
 // saturating at +-6, signed zeros kept - the same code as encode_e2m1 for
-// every binary32 input that is not a NaN (checked exhaustively on the GPU,
-// all 2^32 inputs; the quotients here are finite).
+// every binary32 input that is not a NaN (spg_probe_fp4_rounding checks all
+// 2^32 inputs on the device; the quotients here are finite).
 __device__ __forceinline__ uint32_t encode_half8(const uint4 &v, const GroupScale &s)
 {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

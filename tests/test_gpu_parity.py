@@ -255,6 +255,14 @@ def test_quantize_block16_every_bf16_value_in_unit_groups(spg):
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
+def test_fp4_conversion_instruction_matches_the_e2m1_encoder(spg):
+    # the NVFP4 quantizers round with v_cvt_scalef32_pk_fp4_f32: it must give
+    # the library's E2M1 code (nearest even, saturating, signed zero) for
+    # every binary32 input that is not a NaN
+    r = spg.probe_fp4_rounding()
+    assert r["differences"] == 0, r["examples"]
+
+
 def test_quantize_block16_wide_scale_range_and_zero(spg):
     # group magnitudes from 2^-20 to 1 relative to the tensor maximum:
     # subnormal and zero block-scale codes

@@ -550,6 +550,8 @@ def test_probe_validation_errors(spg):
     assert spg.lib.spg_probe_read(buf, 1000, 1, buf, None) == 1          # not a multiple of 16
     assert spg.lib.spg_probe_read(P(0x10008), 1024, 1, buf, None) == 1   # source not 16-byte aligned
     assert spg.lib.spg_probe_read(buf, 1024, 0, buf, None) == 1
+    assert spg.lib.spg_probe_fp4_rounding(None, None) == 1               # null result
+    assert spg.lib.spg_probe_fp4_rounding(P(0x10002), None) == 1         # not 4-byte aligned
 
 
 # ---------------------------------------------------------------------------
