@@ -446,6 +446,33 @@ def test_gemm_add_in_place(spg):
     check_close(host_u16(r), ref["y"], ref["S"], "in-place add")
 
 
+def test_binding_cache_rechecks_changed_signatures(spg):
+    # gemm_scaled reuses the checked descriptor of a repeated call signature
+    # (shapes, strides, dtypes, devices, pointer alignment); any change of
+    # those is checked again
+    M, N, K = 16, 512, 256
+    A16 = bf16_normal((M, K), 1.0, 41)
+    W16 = bf16_normal((N, K), 0.02, 42)
+    qa, sa = spg.quantize_rowwise(dev(A16))
+    qw, sw = spg.quantize_rowwise(dev(W16))
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    r1 = spg.gemm_scaled(qa, sa, qw, sw, out=out).clone()
+    r2 = spg.gemm_scaled(qa, sa, qw, sw, out=out)             # the cached descriptor
+    assert torch.equal(r1.view(torch.int16), r2.view(torch.int16))
+    with pytest.raises(ValueError):
+        spg.gemm_scaled(qa, sa, qw, sw, out=torch.empty((M, N + 8), dtype=torch.bfloat16, device="cuda"))
+    # K-major W: 16-byte aligned rows pass; the same shape one byte off does not
+    wt = torch.zeros((K, N + 16), dtype=torch.uint8, device="cuda")
+    wt[:, :N] = qw.t()
+    for _ in range(2):
+        rk = spg.gemm_scaled(qa, sa, wt[:, :N], sw, w_kmajor=True)
+        assert torch.equal(rk.view(torch.int16), r1.view(torch.int16))
+    with pytest.raises(ValueError, match="16-byte"):
+        spg.gemm_scaled(qa, sa, wt[:, 1:N + 1], sw, w_kmajor=True)
+    ref = oracle_fp8(A16, W16, "store", "e4m3_row", None)
+    check_close(host_u16(r1), ref["y"], ref["S"], "cached call")
+
+
 def test_gemm_is_deterministic(spg):
     A16 = bf16_normal((1024, 2048), 1.0, 31)
     W16 = bf16_normal((512, 2048), 0.02, 32)
