@@ -1142,6 +1142,25 @@ def test_gemm_narrow_batched_broadcast_and_deterministic(spg, N):
         check_close(out1[b], y, S, f"narrow batch {b}")
 
 
+@pytest.mark.parametrize("M", [8, 32, 300], ids=["decode_width", "decode_width_two_blocks", "tiled"])
+def test_gemm_row_scaled_batches_with_residual(spg, M):
+    # row scales per batch entry (A and W rows of every entry have their own),
+    # per-entry weights, a batched residual
+    B, N, K = 2, 600, 512
+    A16 = bf16_normal((B, M, K), 1.0, 95 + M)
+    W16 = bf16_normal((B, N, K), 0.02, 96)
+    R16 = bf16_normal((B, M, N), 1.0, 97)
+    qa = torch.stack([spg.quantize_rowwise(dev(A16[b]))[0] for b in range(B)])
+    sa = torch.stack([spg.quantize_rowwise(dev(A16[b]))[1] for b in range(B)])
+    qw = torch.stack([spg.quantize_rowwise(dev(W16[b]))[0] for b in range(B)])
+    sw = torch.stack([spg.quantize_rowwise(dev(W16[b]))[1] for b in range(B)])
+    assert spg.gemm_plan(M, N, K, "e4m3_row", "add", batch=B)["kernel"] == (3 if M <= 32 else 2)
+    out = host_u16(spg.gemm_scaled(qa, sa, qw, sw, "add", residual=dev(R16)))
+    for b in range(B):
+        ref = oracle_fp8(A16[b], W16[b], "add", "e4m3_row", R16[b])
+        check_close(out[b], ref["y"], ref["S"], f"row-scaled batch {b} M={M}")
+
+
 def test_gemm_narrow_batched_per_batch_weights(spg):
     # per-tensor products with a weight of their own per batch entry
     B, M, N, K = 2, 4, 512, 640
