@@ -105,7 +105,8 @@ struct Chunk {
 // row R at j ^ ((R >> 1) & 7) (the tiled kernels' swizzle: a fragment read
 // of 16 rows touches every bank once), then for NVFP4 one 4-byte scale
 // word per lane and block, fetched by the lane that reads it.  DEPTH slots
-// per wave (about 16 KiB), so two workgroups fit a compute unit.
+// per wave (at most 16 KiB, at least two slots), so two or three
+// workgroups share a compute unit.
 template <int EPI, bool FP4, int TB, int RB>
 __global__ __launch_bounds__(kNarrowThreads) void gemm_narrow_kernel(const GemmArgs g)
 {
