@@ -148,23 +148,28 @@ double route_cost(const spg_route_candidate &c, int64_t M, int64_t N, int64_t ba
 // The two FP8 tile geometries, in that model, for MI355X (256 compute units,
 // one workgroup each: both kernels use most of the LDS):
 //   256 x 256 tiles (persistent kernel), factor 1;
-//   128 x 256 tiles (the half-height kernel, one tile per workgroup): a half
-//   tile still copies the whole 256-row W panel, 3/4 of a full tile's copy
-//   bytes for 1/2 of its MFMAs, and the copies (L2 to LDS) are what bounds
-//   these kernels.  Measured over whole products a half tile takes ~0.95 of a
-//   full tile's time (384 x 43008 x 4096: 0.101 ms in 128-row tiles against
-//   0.093 ms in 256-row tiles with a half-height tail; 640 x 26624 x 4096:
-//   0.098 against 0.088 ms), i.e. factor 1.9 on its half-size work.
-// So 128-row tiles are taken only where 256-row tiles would leave half of
-// each tile empty (65 to 128 tokens in one round); everywhere else the full
-// geometry wins.
+//   128 x 256 tiles (the half-height kernel, one tile per workgroup), factor
+//   2.2: measured over whole products a half tile costs as much as a full one
+//   or more - it copies 3/4 of a full tile's bytes per stage for 1/2 of its
+//   MFMAs, and its copies bound it.  Measured (half-tile route against
+//   full tiles): 384 x 43008 x 4096 0.101 against 0.093 ms, 640 x 26624 x
+//   4096 0.098 against 0.088 ms, 288 x 21760 x 4096 48.7 against 45.0 us,
+//   384 x 21760 x 8192 117 against 85 us, 96 and 128 x 34816 x 5120 SwiGLU 97
+//   and 101 against 65 us, 128 x 43008 x 4096 71 against 51 us; the one
+//   product it won, 352 x 21760 x 4096 with a residual add, by 11% (58.6
+//   against 65.2 us).  With 2.2 the half geometry is priced above the full one
+//   wherever both take the same number of rounds, so whole products keep
+//   256-row tiles and the half-height kernel serves the short last round
+//   (below), where it runs on twice the compute units.  The half route is
+//   priced only for more than 128 tokens: up to 128 each tile column has one
+//   non-empty half, no more workgroups than full tiles.
 constexpr spg_route_candidate kFullTile = {256, 256, 1, 1.0};
-constexpr spg_route_candidate kHalfTile = {128, 256, 1, 1.9};
+constexpr spg_route_candidate kHalfTile = {128, 256, 1, 2.2};
 
 // The decode-width kernel for products of at most 32 tokens (kernel 3): one
-// workgroup per 16 output columns and batch entry, so it needs enough
-// columns to spread the weight stream (at least 32 workgroups; below that
-// the tiled route's K split gives more).  Its buffer ranges are 32-bit: a
+// workgroup per narrow_cols() output columns and batch entry, so it needs
+// enough columns to spread the weight stream (at least 32 blocks of 16
+// columns; below that the tiled route's K split gives more workgroups).  Its buffer ranges are 32-bit: a
 // blocked NVFP4 scale plane is addressed whole.  NVFP4 scale words are
 // copied 4 bytes at a time: K % 64 == 0 (whole words per row) and, for
 // row-major planes, 4-byte aligned planes (checked by the caller, which
@@ -258,7 +263,7 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p, bool ali
     // Geometry (FP8, unsplit, more than 64 tokens): the full route's cost in
     // the PR #167 model, its partial last round replaced by the tail chosen
     // above, against the half-height geometry over the whole product.
-    if (p->kernel == 0 && p->split_k == 1 && d->M > 64 && d->K > 0 && p->tiles > 0) {
+    if (p->kernel == 0 && p->split_k == 1 && d->M > 128 && d->K > 0 && p->tiles > 0) {
         const int64_t Nw = tiles_n * kTile;   // tile columns in W rows (SWIGLU: 128 gate + 128 up each)
         double full = route_cost(kFullTile, d->M, Nw, d->batch, units);
         if (p->tail_tiles > 0) {
