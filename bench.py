@@ -40,9 +40,10 @@ HBM_GBS = 8000.0
 # the planner that picks their launches (split, tail, grid), which changes
 # the traffic as much as the kernels do; by the plan's kernel (0, 2: FP8
 # tiles, 1: NVFP4 tiles, 3: decode width)
-KERNEL_NAMES = {0: "gemm_fp8_kernel", 1: "gemm_nvfp4_kernel", 2: "gemm_fp8_kernel", 3: "gemm_narrow_kernel"}
+KERNEL_NAMES = {0: "gemm_fp8_kernel", 1: "gemm_nvfp4_kernel", 2: "gemm_fp8_half_kernel", 3: "gemm_narrow_kernel"}
 GEMM_SOURCES = {
     "gemm_fp8_kernel": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_common.h", "spg_splitk.hip", "spg_api.hip"],
+    "gemm_fp8_half_kernel": ["spg_gemm_fp8.hip", "spg_gemm_common.h", "spg_common.h", "spg_api.hip"],
     "gemm_nvfp4_kernel": ["spg_gemm_nvfp4.hip", "spg_gemm_common.h", "spg_common.h", "spg_splitk.hip",
                           "spg_api.hip"],
     "gemm_narrow_kernel": ["spg_gemm_narrow.hip", "spg_gemm_common.h", "spg_common.h", "spg_api.hip"],

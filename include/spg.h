@@ -344,12 +344,11 @@ int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t
  * The plan gemm_scaled would launch for `d` on a device with `units` compute
  * units: tile shape, K-split, the number of workgroups and the tail (split
  * along K, or run as half-height tiles).  For unsplit FP8 products of more
- * than 128 tokens the tile geometry (256 x 256, or 128 x 256 over the whole
+ * than 64 tokens the tile geometry (256 x 256, or 128 x 256 over the whole
  * product) is chosen with the route model above: factor 1 for 256 x 256,
- * 2.2 for 128 x 256 (measured: a half tile costs at least a full tile's
- * time over whole products, so whole products keep 256-row tiles and the
- * 128-row kernel runs the short last round), the 256 x 256 route's partial
- * last round replaced by its tail.  Products of at most 32 tokens with at least 32
+ * 1.24 for 128 x 256 (measured: a round of half tiles takes ~0.62 of a
+ * round of full tiles), the 256 x 256 route's partial last round replaced
+ * by its tail.  Products of at most 32 tokens with at least 32
  * blocks of 16 output columns (over the batch) take the decode-width kernel
  * (kernel 3): one workgroup per 32 output columns (SWIGLU: 16), K split
  * between its four waves and summed in LDS, no workspace (ninfer PR #160
@@ -366,7 +365,9 @@ typedef struct spg_plan {
                              /* compute unit when the FP8 kernel runs an      */
                              /* unsplit product persistently                  */
     int32_t kernel;          /* 0: FP8 256 x 256 tiles; 1: NVFP4; 2: FP8      */
-                             /* 128 x 256 tiles (bm = 128) over the product;  */
+                             /* 128 x 256 tiles (bm = 128) over the product,  */
+                             /* one workgroup each (tiles counts 128-row      */
+                             /* tiles);                                       */
                              /* 3: decode width (both formats; bm = 16 or 32  */
                              /* tokens, bn = 32 output columns, 16 for        */
                              /* SWIGLU; tiles = workgroups =                  */

@@ -148,23 +148,23 @@ double route_cost(const spg_route_candidate &c, int64_t M, int64_t N, int64_t ba
 // The two FP8 tile geometries, in that model, for MI355X (256 compute units,
 // one workgroup each: both kernels use most of the LDS):
 //   256 x 256 tiles (persistent kernel), factor 1;
-//   128 x 256 tiles (the half-height kernel, one tile per workgroup), factor
-//   2.2: measured over whole products a half tile costs as much as a full one
-//   or more - it copies 3/4 of a full tile's bytes per stage for 1/2 of its
-//   MFMAs, and its copies bound it.  Measured (half-tile route against
-//   full tiles): 384 x 43008 x 4096 0.101 against 0.093 ms, 640 x 26624 x
-//   4096 0.098 against 0.088 ms, 288 x 21760 x 4096 48.7 against 45.0 us,
-//   384 x 21760 x 8192 117 against 85 us, 96 and 128 x 34816 x 5120 SwiGLU 97
-//   and 101 against 65 us, 128 x 43008 x 4096 71 against 51 us; the one
-//   product it won, 352 x 21760 x 4096 with a residual add, by 11% (58.6
-//   against 65.2 us).  With 2.2 the half geometry is priced above the full one
-//   wherever both take the same number of rounds, so whole products keep
-//   256-row tiles and the half-height kernel serves the short last round
-//   (below), where it runs on twice the compute units.  The half route is
-//   priced only for more than 128 tokens: up to 128 each tile column has one
-//   non-empty half, no more workgroups than full tiles.
+//   128 x 256 tiles (the half-height kernel over a grid of 128-row tiles, one
+//   per workgroup), factor 1.24: a round of half tiles takes ~0.62 of a round
+//   of full tiles (0.53 - 0.67 over several rounds, 0.56 - 0.80 in single
+//   rounds: it copies 3/4 of a full tile's bytes per stage for half the
+//   MFMAs).  Measured (half route against full tiles, GPU time per call):
+//   288 x 21760 x 4096 29 against 45 us, 352 x 21760 x 4096 with a residual
+//   add 37 against 66, 384 x 21760 x 8192 69 against 86, 384 x 43008 x 4096
+//   72 against 85, 300 x 43520 x 4096 SwiGLU 66 against 80, 96 - 128 tokens
+//   (1 - 168 tile columns, K 512 - 5120) 0.35 - 0.91 of the full tiles'
+//   time; and the other way 640 x 26624 x 4096 81 against 75, 200 x 40000 x
+//   4096 66 against 52, 2048 x 8192 x 4096 59 against 54, 160 x 65536 x 2048
+//   35 against 31, 1536 x 16384 x 4096 89 against 86, 4096 x 34816 x 5120
+//   SwiGLU 733 against 552.  The factor puts every one of these on its
+//   faster side.  Products of at most 64 tokens keep the full kernel's
+//   few-token instantiations, which skip the MFMAs of empty row blocks.
 constexpr spg_route_candidate kFullTile = {256, 256, 1, 1.0};
-constexpr spg_route_candidate kHalfTile = {128, 256, 1, 2.2};
+constexpr spg_route_candidate kHalfTile = {128, 256, 1, 1.24};
 
 // The decode-width kernel for products of at most 32 tokens (kernel 3): one
 // workgroup per narrow_cols() output columns and batch entry, so it needs
@@ -262,8 +262,8 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p, bool ali
     }
     // Geometry (FP8, unsplit, more than 64 tokens): the full route's cost in
     // the PR #167 model, its partial last round replaced by the tail chosen
-    // above, against the half-height geometry over the whole product.
-    if (p->kernel == 0 && p->split_k == 1 && d->M > 128 && d->K > 0 && p->tiles > 0) {
+    // above, against the half-height kernel over a grid of 128-row tiles.
+    if (p->kernel == 0 && p->split_k == 1 && d->M > 64 && d->K > 0 && p->tiles > 0) {
         const int64_t Nw = tiles_n * kTile;   // tile columns in W rows (SWIGLU: 128 gate + 128 up each)
         double full = route_cost(kFullTile, d->M, Nw, d->batch, units);
         if (p->tail_tiles > 0) {
@@ -275,12 +275,13 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p, bool ali
         }
         const double half = route_cost(kHalfTile, d->M, Nw, d->batch, units);
         if (half < full) {
-            p->kernel = 2;                    // the half-height kernel over every tile
+            p->kernel = 2;
             p->bm = (int32_t)(kTile / 2);
+            p->tiles = d->batch * cdiv(d->M, kTile / 2) * tiles_n;
             p->tail_tiles = 0;
             p->tail_split = 1;
             p->tail_bm = (int32_t)kTile;
-            p->workgroups = 2 * p->tiles;     // two 128-row halves per 256-row tile
+            p->workgroups = p->tiles;         // one workgroup per 128-row tile
             return;
         }
     }
@@ -566,6 +567,13 @@ SPG_EXPORT int gemm_scaled(void *out, const void *A, const void *sa, const void 
         g.tiles_n = cdiv(nout, narrow_cols(epilogue));
         g.clocks = d->clock_probe;
         return launch_gemm_narrow(g, s) == hipSuccess ? SPG_OK : SPG_EHIP;
+    }
+    if (p.kernel == 2) {
+        // the half-height kernel over a grid of 128-row tiles
+        g.tiles_m = cdiv(d->M, kTile / 2);
+        g.div_per = make_fastdiv((uint32_t)(g.tiles_m * g.tiles_n));
+        g.div_gm_last = make_fastdiv(g.tiles_m % 8 ? (uint32_t)(g.tiles_m % 8) : 8u);
+        g.rows128 = 1;
     }
     g.tile_begin = 0;
     g.tile_count = p.tiles - p.tail_tiles;

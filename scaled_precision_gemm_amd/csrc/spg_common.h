@@ -139,6 +139,10 @@ struct GemmArgs {
         uint16_t *out;
         int64_t ldo, stride, begin;
     } seg[SPG_MAX_OUT_SPLITS];
+    // Half-height kernel: 0 - its work items are the two 128-row halves of
+    // 256-row tiles tile_begin ..; 1 - the launch covers a grid of 128-row
+    // tiles (tiles_m, the divisions and tile_count describe that grid)
+    int32_t rows128;
 };
 
 // Output element (b, row, col) of a split output (nseg > 0) and the row

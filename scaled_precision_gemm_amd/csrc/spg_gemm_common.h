@@ -121,7 +121,7 @@ struct Tile {
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) { return fdiv_q(n, f); }
 
 // All in 32-bit scalar arithmetic (tile counts are below 2^31).
-template <int EPI>
+template <int EPI, int ROWS = kBM>
 __device__ __forceinline__ Tile tile_from_id(const GemmArgs &g, int64_t t)
 {
     Tile T;
@@ -135,7 +135,7 @@ __device__ __forceinline__ Tile tile_from_id(const GemmArgs &g, int64_t t)
     const uint32_t gm = min((uint32_t)kGroupM, tiles_m - first_m);
     const uint32_t tn = gm == (uint32_t)kGroupM ? tin / kGroupM : fdiv(tin, g.div_gm_last);
     T.b = b;
-    T.m0 = (int64_t)(first_m + (tin - tn * gm)) * kBM;
+    T.m0 = (int64_t)(first_m + (tin - tn * gm)) * ROWS;
     T.tn = tn;
     T.n0 = EPI == SPG_EPI_SWIGLU ? (int64_t)tn * (kBN / 2) : (int64_t)tn * kBN;
     T.c0 = T.n0;

@@ -417,9 +417,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(const GemmArgs g)
 // compute units - 4096 x 34816 x 5120 SwiGLU: 2176 tiles = 8.5 rounds of 256
 // - those tiles run in a second launch as 128 x 256 halves, so the round is
 // spread over every compute unit and takes about half as long; unlike a K
-// split this needs no partial tiles and no reduction), and the whole product
-// when the planner's route model prefers 128-row tiles (M just past a
-// multiple of 256).  A half whose rows all lie past M returns at once.
+// split this needs no partial tiles and no reduction), and whole products
+// over a grid of 128-row tiles: 65 - 128 tokens, where a full tile's lower
+// half would hold no rows, and where the planner's route model prefers
+// 128-row tiles.  A tail half whose rows all lie past M returns at once.
 //
 // Same data path as the full kernel (direct-to-LDS copies of 128-byte row
 // segments, the same swizzle, W fragments first), with the A side halved:
@@ -457,11 +458,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // work item v: half v & 1 of tile tile_begin + v / 2 (the two halves of a
-    // tile are neighbours in the XCD-aware order and share its W panel)
-    const uint32_t v = (uint32_t)xcd_remap(blockIdx.x, (int64_t)2 * g.tile_count);
-    Tile T = tile_from_id<EPI>(g, g.tile_begin + (v >> 1));
-    T.m0 += (int64_t)(v & 1u) * kHalfRows;
+    // work item v: over a grid of 128-row tiles, tile v; else half v & 1 of
+    // 256-row tile tile_begin + v / 2 (the two halves of a tile are
+    // neighbours in the XCD-aware order and share its W panel)
+    const bool grid128 = g.rows128 != 0;
+    const uint32_t v = (uint32_t)xcd_remap(blockIdx.x, (grid128 ? 1 : 2) * g.tile_count);
+    Tile T;
+    if (grid128) {
+        T = tile_from_id<EPI, kHalfRows>(g, g.tile_begin + v);
+    } else {
+        T = tile_from_id<EPI>(g, g.tile_begin + (v >> 1));
+        T.m0 += (int64_t)(v & 1u) * kHalfRows;
+    }
     if (T.m0 >= g.M) return;                       // lower half of a ragged last tile row
 
     // The scale factors are written to LDS after the main loop: a wait the
@@ -624,7 +632,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_half_kernel(const GemmAr
 template <int EPI>
 hipError_t launch_half(const GemmArgs &g, hipStream_t s)
 {
-    const dim3 grid((unsigned)(2 * g.tile_count));
+    const dim3 grid((unsigned)((g.rows128 ? 1 : 2) * g.tile_count));
     const bool so = g.nseg != 0;
     if (g.format == SPG_FMT_E4M3_ROW) {
         if (so) gemm_fp8_half_kernel<EPI, SPG_FMT_E4M3_ROW, true><<<grid, kThreads, 0, s>>>(g);

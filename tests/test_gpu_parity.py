@@ -703,12 +703,12 @@ def test_gemm_tail_split_sampled(spg, fmt, K):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K,epi,fmt,B", [
-    (4096, 4352, 1024, "store", "e4m3_row", 1),
-    (4000, 4312, 1040, "add", "e4m3_row", 1),
+    (4096, 4352, 2048, "store", "e4m3_row", 1),
+    (4000, 4312, 2064, "add", "e4m3_row", 1),
     (3900, 8704, 1024, "swiglu", "e4m3_row", 1),
-    (2048, 4352, 1024, "store", "e4m3_tensor", 2),
-    (4000, 4312, 1040, "bias", "e4m3_row", 1),
-    (4000, 4312, 1040, "bias8", "e4m3_row", 1),
+    (2048, 4352, 2048, "store", "e4m3_tensor", 2),
+    (4000, 4312, 2064, "bias", "e4m3_row", 1),
+    (4000, 4312, 2064, "bias8", "e4m3_row", 1),
 ], ids=["store", "add_ragged", "swiglu_ragged", "tensor_batch2", "bias_ragged", "e4m3_bias_ragged"])
 def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
     bias8 = epi == "bias8"      # ADD with an E4M3 bias row and its scale
@@ -767,6 +767,97 @@ def test_gemm_half_tail(spg, M, N, K, epi, fmt, B):
         D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
         y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, Rs, None if bvals is None else bvals[cols])
         check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"half tail {M}x{N}x{K} {epi} {fmt} batch {b}")
+
+
+# ---------------------------------------------------------------------------
+# the half-height kernel over a grid of 128-row tiles for a whole product,
+# several rounds of workgroups and raster groups of eight tile rows (the last
+# one partial), ragged M, N and K: two rows of every 128-row tile row (its
+# first and its last) and two columns of every tile column are checked, plus
+# random ones.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,epi,fmt,B", [
+    (4096, 4352, 1024, "store", "e4m3_row", 1),
+    (4000, 4312, 1040, "add", "e4m3_row", 1),
+    (2048, 4352, 1024, "store", "e4m3_tensor", 2),
+    (700, 8704, 1040, "swiglu", "e4m3_row", 1),
+    (1100, 7168, 512, "bias8", "e4m3_row", 1),
+], ids=["store_3_rounds", "add_ragged", "tensor_batch2", "swiglu_ragged", "e4m3_bias_ragged"])
+def test_gemm_half_grid_sampled(spg, M, N, K, epi, fmt, B):
+    bias8 = epi == "bias8"
+    epi = "add" if bias8 else epi
+    plan = spg.gemm_plan(M, N, K, fmt, epi, batch=B)
+    tile_n = 128 if epi == "swiglu" else 256
+    n_out = N // 2 if epi == "swiglu" else N
+    assert plan["kernel"] == 2 and plan["workgroups"] == B * -(-M // 128) * -(-n_out // tile_n)
+    rng = np.random.default_rng(M + N + K + B)
+    A16 = bf16_normal((B, M, K) if B > 1 else (M, K), 1.0, 60)
+    W16 = bf16_normal((N, K), 0.02, 61)
+    R16 = bf16_normal((M, n_out), 1.0, 62) if epi == "add" and not bias8 else None
+    res, bscale, bvals = (dev(R16) if R16 is not None else None), None, None
+    if bias8:
+        res, bscale, bvals = e4m3_bias(spg, bf16_normal((n_out,), 1.0, 63))
+    A, W = dev(A16), dev(W16)
+    if fmt == "e4m3_row":
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res, bias_scale=bscale)
+    else:
+        qa, sa = spg.quantize_tensor(A)
+        qw, sw = spg.quantize_tensor(W)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, fmt="e4m3_tensor")
+    torch.cuda.synchronize()
+    gpu = host_u16(out)
+    del A, W, qa, qw, out
+    torch.cuda.empty_cache()
+    firsts = np.arange(0, M, 128)
+    rows = np.unique(np.concatenate([firsts, np.minimum(firsts + 127, M - 1), sample(M, 16, rng)]))
+    cfirst = np.arange(0, n_out, tile_n)
+    cols = np.unique(np.concatenate([cfirst, np.minimum(cfirst + tile_n - 1, n_out - 1), sample(n_out, 16, rng)]))
+    wrows = np.concatenate([cols, cols + N // 2]) if epi == "swiglu" else cols
+    for b in range(B):
+        Ab = A16[b] if B > 1 else A16
+        Rs = np.ascontiguousarray(R16[np.ix_(rows, cols)]) if R16 is not None else None
+        if fmt == "e4m3_row":
+            qa_o, sa_o = oracle.quantize_rowwise(np.ascontiguousarray(Ab[rows]))
+            qw_o, sw_o = oracle.quantize_rowwise(np.ascontiguousarray(W16[wrows]))
+        else:
+            sa_o = oracle.amax(Ab) / np.float32(448.0)
+            sw_o = oracle.amax(W16) / np.float32(448.0)
+            qa_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(Ab[rows]), sa_o)
+            qw_o = oracle.quantize_rows_with_scale(np.ascontiguousarray(W16[wrows]), sw_o)
+        D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+        y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, Rs, None if bvals is None else bvals[cols])
+        g = gpu[b] if B > 1 else gpu
+        check_close(np.ascontiguousarray(g[np.ix_(rows, cols)]), y, S, f"half grid {M}x{N}x{K} {epi} {fmt} batch {b}")
+
+
+# ---------------------------------------------------------------------------
+# 65 - 128 tokens: unsplit FP8 products run as one row of 128-row half tiles
+# (the lower half of a 256-row tile would be empty).  Whole outputs: ragged
+# M, N and K, a single K stage, a K tail inside the first stage, SwiGLU
+# pairing, both scale forms, and more tile columns than compute units (257:
+# a second round of workgroups).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,epi,fmt", [
+    (65, 700, 1040, "store", "e4m3_row"),
+    (100, 600, 512, "swiglu", "e4m3_row"),
+    (128, 1000, 384, "add", "e4m3_tensor"),
+    (97, 520, 128, "add", "e4m3_row"),
+    (128, 300, 16, "swiglu", "e4m3_tensor"),
+    (128, 65792, 256, "store", "e4m3_row"),
+], ids=["ragged_store", "swiglu", "tensor_add", "one_stage", "k16", "257_tiles"])
+def test_gemm_half_route_up_to_128_tokens(spg, M, N, K, epi, fmt):
+    plan = spg.gemm_plan(M, N, K, fmt, epi)
+    assert plan["kernel"] == 2 and plan["bm"] == 128 and plan["workgroups"] == plan["tiles"]
+    A16 = bf16_normal((M, K), 1.0, 70 + M)
+    W16 = bf16_normal((N, K), 0.02, 71 + N)
+    R16 = bf16_normal((M, N), 1.0, 72) if epi == "add" else None
+    gpu = run_fp8(spg, A16, W16, epi, fmt, R16)
+    ref = oracle_fp8(A16, W16, epi, fmt, R16)
+    check_close(gpu, ref["y"], ref["S"], f"half route {M}x{N}x{K} {epi} {fmt}")
 
 
 # ---------------------------------------------------------------------------
@@ -1142,11 +1233,12 @@ def test_gemm_narrow_batched_broadcast_and_deterministic(spg, N):
         check_close(out1[b], y, S, f"narrow batch {b}")
 
 
-@pytest.mark.parametrize("M", [8, 32, 300], ids=["decode_width", "decode_width_two_blocks", "tiled"])
-def test_gemm_row_scaled_batches_with_residual(spg, M):
+@pytest.mark.parametrize("M,K", [(8, 512), (32, 512), (100, 512), (300, 512), (300, 2048)],
+                         ids=["decode_width", "decode_width_two_blocks", "half_tiles", "half_tiles_3_rows", "split_k"])
+def test_gemm_row_scaled_batches_with_residual(spg, M, K):
     # row scales per batch entry (A and W rows of every entry have their own),
     # per-entry weights, a batched residual
-    B, N, K = 2, 600, 512
+    B, N = 2, 600
     A16 = bf16_normal((B, M, K), 1.0, 95 + M)
     W16 = bf16_normal((B, N, K), 0.02, 96)
     R16 = bf16_normal((B, M, N), 1.0, 97)
@@ -1154,7 +1246,7 @@ def test_gemm_row_scaled_batches_with_residual(spg, M):
     sa = torch.stack([spg.quantize_rowwise(dev(A16[b]))[1] for b in range(B)])
     qw = torch.stack([spg.quantize_rowwise(dev(W16[b]))[0] for b in range(B)])
     sw = torch.stack([spg.quantize_rowwise(dev(W16[b]))[1] for b in range(B)])
-    assert spg.gemm_plan(M, N, K, "e4m3_row", "add", batch=B)["kernel"] == (3 if M <= 32 else 0)
+    assert spg.gemm_plan(M, N, K, "e4m3_row", "add", batch=B)["kernel"] == (3 if M <= 32 else 0 if K > 1024 else 2)
     out = host_u16(spg.gemm_scaled(qa, sa, qw, sw, "add", residual=dev(R16)))
     for b in range(B):
         ref = oracle_fp8(A16[b], W16[b], "add", "e4m3_row", R16[b])

@@ -445,10 +445,10 @@ def test_plans_for_the_workloads(spg):
             s, bk = p["split_k"], p["bk"]
             chunk = -(-(-(-K // s)) // bk) * bk
             assert (s - 1) * chunk < K, (K, fmt, s)
-    # 128 tokens, one tile: 256-row tiles (the 128-row geometry is priced
-    # above them)
+    # 128 tokens, one tile: one 128-row half tile (the lower half of a
+    # 256-row tile would hold no rows)
     p = spg.gemm_plan(128, 256, 512, "e4m3_row", "store")
-    assert (p["tiles"], p["split_k"], p["workgroups"], p["bm"], p["kernel"]) == (1, 1, 1, 256, 0)
+    assert (p["tiles"], p["split_k"], p["workgroups"], p["bm"], p["kernel"]) == (1, 1, 1, 128, 2)
     p = spg.gemm_plan(512, 512, 512, "e4m3_tensor", "store", batch=64)
     assert (p["tiles"], p["split_k"], p["workgroups"]) == (256, 1, 256)
     p = spg.gemm_plan(8192, 8192, 8192, "e4m3_tensor", "store")
@@ -468,9 +468,13 @@ def test_plans_for_the_workloads(spg):
     # tiles (no partials) do: 8 whole rounds, then 256 halves of 128 tiles
     p = spg.gemm_plan(4096, 34816, 5120, "e4m3_row", "swiglu")
     assert (p["workgroups"], p["tail_tiles"], p["tail_split"], p["tail_bm"]) == (256, 128, 1, 128)
-    # short K, 16 tiles left: half-height tiles (a K split of 1024 is too short)
-    p = spg.gemm_plan(4096, 4352, 1024, "e4m3_row", "store")
+    # 16 tiles left, K 2048: half-height tiles (a K split of 2048 is too short)
+    p = spg.gemm_plan(4096, 4352, 2048, "e4m3_row", "store")
     assert (p["tiles"], p["tail_tiles"], p["tail_split"], p["tail_bm"]) == (272, 16, 1, 128)
+    # K 1024: the tail's launch outweighs a short round; 128-row tiles over
+    # the whole product (3 rounds at 0.62) are priced below it
+    p = spg.gemm_plan(4096, 4352, 1024, "e4m3_row", "store")
+    assert (p["kernel"], p["tiles"], p["workgroups"], p["tail_tiles"]) == (2, 544, 544, 0)
     # more than half a round left: no half-height tail (it would take 2 rounds)
     p = spg.gemm_plan(4096, 4096 + 12 * 256, 5120, "e4m3_row", "store")
     assert p["tiles"] == 16 * 28 and p["tail_bm"] == 256
@@ -563,14 +567,25 @@ def test_probe_validation_errors(spg):
 # ---------------------------------------------------------------------------
 MI355X_PLANS = [
     # (M, N, K, fmt, epi, batch) -> (kernel, bm, split_k, tail_tiles, tail_split, tail_bm)
-    ((128, 256, 512, "e4m3_row", "store", 1), (0, 256, 1, 0, 1, 256)),       # 65-128 tokens: 256-row tiles
-    ((96, 34816, 5120, "e4m3_row", "swiglu", 1), (0, 256, 1, 0, 1, 256)),
-    ((257, 300, 160, "e4m3_row", "store", 1), (0, 256, 1, 0, 1, 256)),
-    ((352, 21760, 4096, "e4m3_row", "add", 1), (0, 256, 1, 0, 1, 256)),
+    ((128, 256, 512, "e4m3_row", "store", 1), (2, 128, 1, 0, 1, 256)),       # 128-row tiles where they measured faster
+    ((96, 34816, 5120, "e4m3_row", "swiglu", 1), (2, 128, 1, 0, 1, 256)),
+    ((257, 300, 160, "e4m3_row", "store", 1), (2, 128, 1, 0, 1, 256)),
+    ((288, 21760, 4096, "e4m3_row", "store", 1), (2, 128, 1, 0, 1, 256)),
+    ((352, 21760, 4096, "e4m3_row", "add", 1), (2, 128, 1, 0, 1, 256)),
+    ((384, 21760, 8192, "e4m3_row", "store", 1), (2, 128, 1, 0, 1, 256)),
+    ((384, 43008, 4096, "e4m3_row", "store", 1), (2, 128, 1, 0, 1, 256)),
+    ((300, 43520, 4096, "e4m3_row", "swiglu", 1), (2, 128, 1, 0, 1, 256)),
+    ((640, 26624, 4096, "e4m3_row", "store", 1), (0, 256, 1, 56, 1, 128)),   # 256-row tiles where they measured faster
+    ((200, 40000, 4096, "e4m3_row", "store", 1), (0, 256, 1, 0, 1, 256)),
+    ((2048, 8192, 4096, "e4m3_row", "store", 1), (0, 256, 1, 0, 1, 256)),
+    ((160, 65536, 2048, "e4m3_row", "store", 1), (0, 256, 1, 0, 1, 256)),
+    ((1536, 16384, 4096, "e4m3_row", "store", 1), (0, 256, 1, 128, 1, 128)),
+    ((128, 5120, 4096, "e4m3_row", "add", 1), (0, 256, 4, 0, 1, 256)),       # split along K: no geometry choice
     ((1024, 5120, 17408, "e4m3_row", "add", 1), (0, 256, 3, 0, 1, 256)),    # 80 tiles: K split 3
     ((4096, 34816, 5120, "e4m3_row", "swiglu", 1), (0, 256, 1, 128, 1, 128)),  # 8.5 rounds: half-height tail
     ((4096, 5120, 6144, "e4m3_row", "add", 1), (0, 256, 1, 64, 1, 128)),
-    ((384, 43008, 4096, "e4m3_row", "store", 1), (0, 256, 1, 80, 1, 128)),
+    ((4096, 7168, 5120, "e4m3_row", "store", 1), (0, 256, 1, 0, 1, 256)),
+    ((4096, 12288, 2048, "e4m3_row", "store", 1), (0, 256, 1, 0, 1, 256)),
     ((4096, 5120, 6144, "nvfp4", "add", 1), (1, 256, 1, 64, 4, 256)),        # NVFP4: K-split tail
     ((8192, 8192, 8192, "e4m3_tensor", "store", 1), (0, 256, 1, 0, 1, 256)),
     ((512, 512, 512, "e4m3_tensor", "store", 64), (0, 256, 1, 0, 1, 256)),
@@ -591,16 +606,25 @@ def test_mi355x_plan_decisions(spg, case, want):
 
 
 def test_geometry_costs_follow_the_route_model(spg):
-    # the planner's two candidates priced by the exported PR #167 model.  With
-    # the measured factor 2.2 a 128-row tile costs more than a 256-row one
-    # whenever both routes take the same number of rounds, and the half route
-    # never takes fewer, so whole products keep 256-row tiles; a factor below
-    # 2 (the first calibration, 1.9) would pick 128-row tiles at 128 tokens
-    full, half = (256, 256, 1, 1.0), (128, 256, 1, 2.2)
+    # the planner's two candidates priced by the exported PR #167 model: a
+    # round of 128-row tiles at 0.62 of a round of 256-row tiles (factor 1.24
+    # on half the area), so 128-row tiles win wherever they take the same
+    # number of rounds, and lose at twice the rounds
+    full, half = (256, 256, 1, 1.0), (128, 256, 1, 1.24)
     assert spg.route_cost(*full, 384, 43008, 1, 256) == 2 * 256 * 256
-    assert spg.route_cost(*half, 384, 43008, 1, 256) == 2.2 * 2 * 128 * 256
-    assert spg.route_select([full, half], 128, 34816, 1, 256) == 0
+    assert spg.route_cost(*half, 384, 43008, 1, 256) == 1.24 * 2 * 128 * 256
+    assert spg.route_select([full, half], 128, 34816, 1, 256) == 1
+    assert spg.route_select([full, half], 288, 21760, 1, 256) == 1
+    assert spg.route_select([full, half], 2048, 8192, 1, 256) == 0
     assert spg.route_select([full, half], 4096, 34816, 1, 256) == 0
-    assert spg.route_select([full, (128, 256, 1, 1.9)], 128, 34816, 1, 256) == 1
-    for M in (96, 128, 257, 384, 1024):
-        assert spg.gemm_plan(M, 43008, 4096, "e4m3_row", "store")["kernel"] == 0
+    # the planner counts the 128-row grid's tiles and launches one workgroup
+    # per tile; a partial last round of 256-row tiles is priced with its tail
+    for M, tiles in ((65, 168), (128, 168), (257, 504), (384, 504)):
+        p = spg.gemm_plan(M, 43008, 4096, "e4m3_row", "store")
+        assert (p["kernel"], p["bm"], p["workgroups"], p["tiles"]) == (2, 128, tiles, tiles)
+    p = spg.gemm_plan(1024, 43008, 4096, "e4m3_row", "store")
+    assert p["kernel"] == 0 and p["tiles"] == 672
+    p = spg.gemm_plan(100, 4096, 512, "e4m3_tensor", "store", batch=3)
+    assert (p["kernel"], p["workgroups"], p["tiles"]) == (2, 48, 48)
+    p = spg.gemm_plan(1100, 7168, 512, "e4m3_row", "store")
+    assert (p["kernel"], p["tiles"]) == (2, 9 * 28)
