@@ -508,6 +508,20 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
                 }
         wait_vmem<0>();   // only this wave reads its regions
     }
+    // ADD over whole quadrants: each pass's residual block is loaded during
+    // the pass before (issued right after that pass's block reached the
+    // region), so its round trip overlaps the conversion and the stores
+    // instead of opening every pass
+    constexpr bool PREF = EPI == SPG_EPI_ADD && !BIAS && !STAGED && FULL;
+    v4i rpre[4];
+    auto res_load = [&](int y, int p) {
+        const uint16_t *rb = o.res + (T.m0 + wm * (MI * 32) + y * 32) * g.ldr + T.c0 + wn * 128 + p * 64;
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            rpre[it] = __builtin_nontemporal_load(
+                reinterpret_cast<const v4i *>(rb + (uint32_t)((it * 8 + rr) * ldr + rc * 8)));   // read once
+    };
+    if (PREF) res_load(0, 0);
     constexpr int NX = SW ? 2 : 4;
     float sa_r[MI];
     v4f sw_r[BIAS ? 1 : NX][4], swu_r[SW ? 2 : 1][4];
@@ -545,7 +559,17 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
             const uint32_t ldo = SPLITOUT ? (uint32_t)ldo_p : ldo1;
 
             // 1. residual block -> region
-            if (EPI == SPG_EPI_ADD && !BIAS && !STAGED) {
+            if (PREF) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int r = it * 8 + rr;
+                    *reinterpret_cast<v4i *>(region + r * 128 + phys(r, rc) * 16) = rpre[it];
+                }
+                if (p + 1 < NP)
+                    res_load(y, p + 1);
+                else if (y + 1 < MI)
+                    res_load(y + 1, 0);
+            } else if (EPI == SPG_EPI_ADD && !BIAS && !STAGED) {
                 const uint16_t *const rbase = o.res + row0 * g.ldr + col0;
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {

@@ -363,12 +363,20 @@ def test_gemm_fp8_extreme_shapes(spg, shape, epi):
     check_close(gpu, ref["y"], ref["S"], f"{shape} {epi}")
 
 
-def test_gemm_zero_weight_add_returns_residual_bitwise(spg):
-    A16 = bf16_normal((300, 256), 1.0, 1)
-    W16 = np.zeros((260, 256), np.uint16)
-    R16 = bf16_normal((300, 260), 1.0, 2)
+@pytest.mark.parametrize("M,N,K,kernel", [(300, 260, 256, 2), (4096, 5120, 2048, 0)],
+                         ids=["half_tiles", "persistent_with_half_tail"])
+def test_gemm_zero_weight_add_returns_residual_bitwise(spg, M, N, K, kernel):
+    # every residual element lands where it belongs: whole-quadrant passes
+    # (each pass's residual loaded during the pass before), staged blocks of
+    # the half-height kernel, ragged edges
+    assert spg.gemm_plan(M, N, K, "e4m3_row", "add")["kernel"] == kernel
+    A16 = bf16_normal((M, K), 1.0, 1)
+    W16 = np.zeros((N, K), np.uint16)
+    R16 = bf16_normal((M, N), 1.0, 2)
     gpu = run_fp8(spg, A16, W16, "add", "e4m3_row", R16)
-    assert np.array_equal(gpu, R16)
+    # the product is +0, and +0 + r is r except for r = -0 (IEEE: +0)
+    assert np.any(R16 == 0x8000) == (kernel == 0)   # this residual holds one -0
+    assert np.array_equal(gpu, np.where(R16 == 0x8000, np.uint16(0), R16))
 
 
 @pytest.mark.parametrize("fmt", ["e4m3_row", "e4m3_tensor"])
