@@ -343,8 +343,8 @@ int spg_route_select(const spg_route_candidate *c, int32_t n, int64_t M, int64_t
 /*
  * The plan gemm_scaled would launch for `d` on a device with `units` compute
  * units: tile shape, K-split, the number of workgroups and the tail (split
- * along K, or run as half-height tiles).  For unsplit FP8 products of more
- * than 64 tokens the tile geometry (256 x 256, or 128 x 256 over the whole
+ * along K, or run as half-height tiles).  For unsplit FP8 products the tile
+ * geometry (256 x 256, or 128 x 256 over the whole
  * product) is chosen with the route model above: factor 1 for 256 x 256,
  * 1.24 for 128 x 256 (measured: a round of half tiles takes ~0.62 of a
  * round of full tiles), the 256 x 256 route's partial last round replaced

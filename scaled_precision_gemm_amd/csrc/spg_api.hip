@@ -161,8 +161,11 @@ double route_cost(const spg_route_candidate &c, int64_t M, int64_t N, int64_t ba
 //   4096 66 against 52, 2048 x 8192 x 4096 59 against 54, 160 x 65536 x 2048
 //   35 against 31, 1536 x 16384 x 4096 89 against 86, 4096 x 34816 x 5120
 //   SwiGLU 733 against 552.  The factor puts every one of these on its
-//   faster side.  Products of at most 64 tokens keep the full kernel's
-//   few-token instantiations, which skip the MFMAs of empty row blocks.
+//   faster side.  At 33 - 64 tokens the half tiles also beat the full
+//   kernel's few-token instantiations (which skip the MFMAs of empty row
+//   blocks): 0.79 - 0.88 of their time (48 x 34816 x 1024 SwiGLU 11.9
+//   against 14.0 us, 64 x 65536 x 2048 24.0 against 27.6 us); those
+//   instantiations keep the products split along K.
 constexpr spg_route_candidate kFullTile = {256, 256, 1, 1.0};
 constexpr spg_route_candidate kHalfTile = {128, 256, 1, 1.24};
 
@@ -260,10 +263,10 @@ void make_plan(const spg_gemm_desc *d, int epi, int units, spg_plan *p, bool ali
             }
         }
     }
-    // Geometry (FP8, unsplit, more than 64 tokens): the full route's cost in
-    // the PR #167 model, its partial last round replaced by the tail chosen
-    // above, against the half-height kernel over a grid of 128-row tiles.
-    if (p->kernel == 0 && p->split_k == 1 && d->M > 64 && d->K > 0 && p->tiles > 0) {
+    // Geometry (FP8, unsplit): the full route's cost in the PR #167 model, its
+    // partial last round replaced by the tail chosen above, against the
+    // half-height kernel over a grid of 128-row tiles.
+    if (p->kernel == 0 && p->split_k == 1 && d->K > 0 && p->tiles > 0) {
         const int64_t Nw = tiles_n * kTile;   // tile columns in W rows (SWIGLU: 128 gate + 128 up each)
         double full = route_cost(kFullTile, d->M, Nw, d->batch, units);
         if (p->tail_tiles > 0) {

@@ -422,8 +422,8 @@ def test_plans_for_the_workloads(spg):
     assert (p["kernel"], p["bm"], p["bk"], p["workgroups"]) == (3, 32, 256, 160)
     # NVFP4 with K % 64 != 0 (scale rows of whole 4-byte words only): tiled
     assert spg.gemm_plan(16, 5120, 6176, "nvfp4", "add")["kernel"] == 1
-    # fewer than 32 column blocks: the tiled route
-    assert spg.gemm_plan(16, 496, 512, "e4m3_row", "store")["kernel"] == 0
+    # fewer than 32 column blocks: the tiled route (unsplit: 128-row tiles)
+    assert spg.gemm_plan(16, 496, 512, "e4m3_row", "store")["kernel"] == 2
     assert spg.gemm_plan(1, 512, 512, "e4m3_tensor", "store")["kernel"] == 3
     # 33 to 64 tokens: the weight-streaming cost model (waves * (slice + 1024))
     # picks 3 slices for the SwiGLU (408 workgroups, 1.6 waves beat 2.7 at
@@ -561,7 +561,7 @@ def test_probe_validation_errors(spg):
 
 # ---------------------------------------------------------------------------
 # the MI355X plan: tile geometry (ninfer PR #167's route model, recalibrated
-# for 256 compute units: 256 x 256 factor 1, 128 x 256 factor 2.2), split-K,
+# for 256 compute units: 256 x 256 factor 1, 128 x 256 factor 1.24), split-K,
 # tails; the decisions for the benchmark workloads and the cases where the
 # 128-row geometry is taken
 # ---------------------------------------------------------------------------
