@@ -1034,7 +1034,8 @@ SPLITS = [((300, 640, 512), "e4m3_row", "store", (256, 256, 128), 1),
           ((257, 640, 512), "nvfp4", "store", (64, 512, 64), 1),
           ((20, 1280, 1024), "e4m3_row", "swiglu", (384, 256), 1),
           ((8, 640, 512), "nvfp4", "store", (64, 512, 64), 1),
-          ((4, 1100, 256), "e4m3_row", "add", (512, 448, 140), 1)]
+          ((4, 1100, 256), "e4m3_row", "add", (512, 448, 140), 1),
+          ((260, 700, 512), "e4m3_tensor", "store", (256, 384, 60), 2)]
 
 
 @pytest.mark.parametrize("shape,fmt,epi,widths,B", SPLITS,
@@ -1136,7 +1137,8 @@ KMAJOR = [((300, 520, 1040), "e4m3_tensor", "store", (False, True), 1),
           ((257, 300, 512), "e4m3_row", "swiglu", (True, False), 1),
           ((16, 4096, 2048), "e4m3_row", "store", (False, True), 1),
           ((96, 200, 256), "e4m3_tensor", "store", (True, True), 2),
-          ((1024, 2048, 4096), "e4m3_tensor", "store", (True, True), 1)]
+          ((1024, 2048, 4096), "e4m3_tensor", "store", (True, True), 1),
+          ((260, 520, 512), "e4m3_tensor", "add", (True, True), 2)]
 
 
 @pytest.mark.parametrize("shape,fmt,epi,km,B", KMAJOR,
