@@ -286,3 +286,21 @@ def test_a_bf16_rounded_output_always_passes_the_bound():
     out = np.array([[oracle.bf16_from_f64(v) for v in y[0]]], np.uint16)
     ok, ex = oracle.within_tolerance(out, y, np.zeros_like(y))
     assert ok.all() and ex.max() <= 1.0
+
+
+def test_the_bound_reaches_down_to_bf16_subnormals():
+    # below bf16's normal range (2^-126) its values are spaced 2^-133 apart:
+    # the correctly rounded result of a y there can be 2^-134 away (more than
+    # 2^-8 |y|), and it still passes; the floor adds nothing a normal-range
+    # check would notice, and an error of two steps fails
+    rng = np.random.default_rng(19)
+    y = np.concatenate([rng.uniform(-1, 1, 400) * 2.0 ** -126, rng.uniform(-1, 1, 400) * 2.0 ** -134,
+                        [2.0 ** -134, 3 * 2.0 ** -134, -2.0 ** -130, 2.0 ** -120]])[None, :]
+    out = np.array([[oracle.bf16_from_f64(v) for v in y[0]]], np.uint16)
+    S = np.zeros_like(y)
+    ok, ex = oracle.within_tolerance(out, y, S)
+    assert ok.all() and ex.max() <= 1.0
+    assert np.any(np.abs(oracle.bf16_to_f64(out) - y) > 2.0 ** -8 * np.abs(y))   # the floor is what passes these
+    off = np.array([[oracle.bf16_from_f64(v + np.copysign(2.0 * 2.0 ** -133, v)) for v in y[0]]], np.uint16)
+    ok, _ = oracle.within_tolerance(off, y, S)
+    assert not ok[0, :800].any()
