@@ -102,9 +102,23 @@ __device__ __forceinline__ int lane_id()
     return r;
 }
 
-// silu(z) = z / (1 + e^-z) with the hardware reciprocal (about 1 ulp; the
-// SwiGLU output tolerance is 2^-8 relative)
-__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+// silu(g) * u = g u / (1 + exp(-g)) with the hardware reciprocal (about 1
+// ulp; the SwiGLU output tolerance is 2^-8 relative), the denominator
+// carried as (1 + exp(-g)) 2^-64 and the 2^-64 given back last.  Unscaled,
+// from g = -87.3 the reciprocal of the denominator is subnormal (the
+// hardware reciprocal flushes it to zero) and from g = -88.7 exp(-g)
+// overflows, while silu(g) u can still be a normal bf16 value (g = -88,
+// u = -46: 1.8e-35).  Scaled, the reciprocal stays normal down to g = -131
+// and exp(-g) 2^-64 is finite down to g = -133; below that
+// |silu(g) u| < |g u| 2^-190, which rounds to zero in bf16 for any |g u|
+// under 2^57.  Against the unscaled form this costs one multiply; the offset
+// in the exponent argument costs 2^-18 of absolute precision in it (a
+// relative 2^-18 in exp, far below bf16's 2^-9).
+__device__ __forceinline__ float swiglu_f32(float g, float u)
+{
+    const float d = __builtin_amdgcn_exp2f(__builtin_fmaf(g, -1.44269504f, -64.0f)) + 0x1p-64f;
+    return (g * u) * __builtin_amdgcn_rcpf(d) * 0x1p-64f;
+}
 
 struct Tile {
     int64_t global;   // tile id over the whole batch (split-K bookkeeping)
@@ -376,7 +390,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs &g, const Tile &T,
             if (EPI == SPG_EPI_SWIGLU) {
                 const float vg = a[e] * sa * sw[j];
                 const float vu = up[e] * sa * swu[j];
-                v[j] = silu_f32(vg) * vu;
+                v[j] = swiglu_f32(vg, vu);
             } else {
                 v[j] = a[e] * sa * sw[j];
             }
@@ -610,7 +624,7 @@ __device__ __forceinline__ void epilogue_impl(const GemmArgs &g, const Tile &T, 
                         if (SW) {
                             const float vg = acc[x][y][e] * sa * sw[j];
                             const float vu = acc[x + 2][y][e] * sa * swu[j];
-                            v[j] = silu_f32(vg) * vu;
+                            v[j] = swiglu_f32(vg, vu);
                         } else {
                             v[j] = acc[x][y][e] * sa * sw[j];
                         }

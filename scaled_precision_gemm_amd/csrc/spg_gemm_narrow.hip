@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_narrow_kernel(const GemmA
             if (EPI == SPG_EPI_SWIGLU) {
                 const float vg = v[0][e] * sa * sw[0][e];
                 const float vu = v[NH - 1][e] * sa * sw[NH - 1][e];
-                o[e] = silu_f32(vg) * vu;
+                o[e] = swiglu_f32(vg, vu);
             } else {
                 o[e] = v[0][e] * sa * sw[0][e];
             }

@@ -869,6 +869,46 @@ def test_gemm_half_route_up_to_128_tokens(spg, M, N, K, epi, fmt):
 
 
 # ---------------------------------------------------------------------------
+# SwiGLU with gate values far below zero (unit-variance weights, long K):
+# where 1 + exp(-g) leaves the range whose reciprocal is a normal float, the
+# epilogue switches to the limit form g u exp(g); outputs down to bf16's
+# subnormals must still match.  Every route: 128-row tiles, 256-row tiles,
+# the split-K reduction, the decode-width kernel, NVFP4.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,M,N,K,kernel,split", [
+    ("e4m3_tensor", 300, 1024, 1536, 2, False),
+    ("e4m3_tensor", 512, 16896, 512, 0, False),
+    ("e4m3_tensor", 64, 1024, 8192, 0, True),
+    ("e4m3_tensor", 16, 1024, 4096, 3, False),
+    ("nvfp4", 512, 2048, 1536, 1, False),
+    ("nvfp4", 256, 1024, 4096, 1, True),
+], ids=["half_tiles", "full_tiles", "split_k", "decode_width", "nvfp4", "nvfp4_split_k"])
+def test_swiglu_far_negative_gates(spg, fmt, M, N, K, kernel, split):
+    plan = spg.gemm_plan(M, N, K, fmt, "swiglu")
+    assert plan["kernel"] == kernel and (plan["split_k"] > 1) == split
+    A16 = bf16_normal((M, K), 1.0, 30 + M)
+    W16 = bf16_normal((N, K), 1.0, 31 + K)
+    if fmt == "nvfp4":
+        gpu = run_nvfp4(spg, A16, W16, "swiglu")
+        qa, bsa, ta = oracle.quantize_block16(A16)
+        qw, bsw, tw = oracle.quantize_block16(W16)
+        D, Da = oracle.gemm_nvfp4_sums(qa, bsa, qw, bsw)
+        sc = float(ta) * float(tw)
+        y, S, _ = oracle.epilogue("swiglu", D, Da, ta, tw, None)
+    else:
+        gpu = run_fp8(spg, A16, W16, "swiglu", fmt)
+        qa, sa = oracle.quantize_tensor(A16)
+        qw, sw = oracle.quantize_tensor(W16)
+        D, Da = oracle.gemm_e4m3_sums(qa, qw)
+        sc = float(sa[0]) * float(sw[0])
+        y, S, _ = oracle.epilogue("swiglu", D, Da, sa[0], sw[0], None)
+    gate = D[:, : N // 2] * sc
+    assert np.count_nonzero(gate < -88.0) > 0 and np.count_nonzero((gate < -80.0) & (np.abs(y) > 2.0 ** -126)) > 0
+    check_close(gpu, y, S, f"far negative gates {fmt} {M}x{N}x{K}")
+
+
+# ---------------------------------------------------------------------------
 # bf16 bias: the ADD epilogue with one residual row (row stride 0) added to
 # every token row - unsplit tiles, several tiles per persistent workgroup,
 # split-K with its reduction (many and few tokens), both FP8 scale forms and

@@ -1,0 +1,102 @@
+"""Seeded random shapes through the planner's routes: the decode-width
+kernel, 128-row and 256-row tiles, the few-token instantiations with their
+K split, both FP8 scale forms and NVFP4, all three epilogues (the tails of
+products larger than one round are covered by the sampled full-size tests).
+Whole outputs are compared with the oracle (quantize -> exact GEMM sums ->
+scales -> epilogue) within the acceptance bound; the quantized codes and
+scales must match bit for bit.  The shapes are drawn once from a fixed
+seed, small enough for the oracle to finish in a few seconds each.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic import bf16_normal
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=36, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = ("e4m3_row", "e4m3_tensor", "nvfp4")[i % 3]
+        epi = ("store", "add", "swiglu")[(i // 3) % 3]
+        M = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 129)), int(rng.integers(129, 520))]))
+        N = int(rng.integers(1, 500)) * 2
+        kq = 32 if fmt == "nvfp4" else 16
+        K = int(rng.integers(1, 1600 // kq + 1)) * kq
+        out.append((fmt, epi, M, N, K))
+    # shapes that reach the few-token K split, 256-row tiles, and 128-row
+    # tiles over several raster groups
+    out += [("e4m3_row", "add", 40, 1024, 8192), ("nvfp4", "store", 48, 2048, 4096),
+            ("e4m3_row", "add", 512, 16640, 256), ("e4m3_tensor", "store", 512, 16640, 512),
+            ("e4m3_row", "store", 1300, 2560, 512), ("e4m3_tensor", "swiglu", 700, 4352, 512)]
+    return out
+
+
+CASES = _cases()
+
+
+def dev(x16):
+    return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def spg():
+    import scaled_precision_gemm_amd as m
+    return m
+
+
+@pytest.mark.parametrize("fmt,epi,M,N,K", CASES, ids=lambda v: str(v))
+def test_random_shape_matches_the_oracle(spg, fmt, epi, M, N, K):
+    plan = spg.gemm_plan(M, N, K, fmt, epi)
+    print(f"{fmt} {epi} {M}x{N}x{K} kernel {plan['kernel']} split {plan['split_k']} "
+          f"tail {plan['tail_tiles']}/{plan['tail_split']}/{plan['tail_bm']}", flush=True)
+    n_out = N // 2 if epi == "swiglu" else N
+    A16 = bf16_normal((M, K), 1.0, 7 * M + K)
+    W16 = bf16_normal((N, K), 0.02 if fmt != "e4m3_tensor" else 1.0, 11 * N + K)
+    R16 = bf16_normal((M, n_out), 1.0, M + N) if epi == "add" else None
+    res = dev(R16) if R16 is not None else None
+    A, W = dev(A16), dev(W16)
+    if fmt == "e4m3_row":
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        qa_o, sa_o = oracle.quantize_rowwise(A16)
+        qw_o, sw_o = oracle.quantize_rowwise(W16)
+        assert np.array_equal(qa.cpu().numpy(), qa_o) and np.array_equal(sa.cpu().numpy(), sa_o)
+        assert np.array_equal(qw.cpu().numpy(), qw_o) and np.array_equal(sw.cpu().numpy(), sw_o)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res)
+        D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+        y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, R16)
+    elif fmt == "e4m3_tensor":
+        qa, sa = spg.quantize_tensor(A)
+        qw, sw = spg.quantize_tensor(W)
+        qa_o, sa_o = oracle.quantize_tensor(A16)
+        qw_o, sw_o = oracle.quantize_tensor(W16)
+        assert np.array_equal(qa.cpu().numpy(), qa_o) and np.array_equal(sa.cpu().numpy(), sa_o)
+        assert np.array_equal(qw.cpu().numpy(), qw_o) and np.array_equal(sw.cpu().numpy(), sw_o)
+        out = spg.gemm_scaled(qa, sa, qw, sw, epi, residual=res, fmt="e4m3_tensor")
+        D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+        y, S, _ = oracle.epilogue(epi, D, Da, sa_o[0], sw_o[0], R16)
+    else:
+        qa, ba, ta = spg.quantize_block16(A)
+        qw, bw, tw = spg.quantize_block16(W)
+        qa_o, ba_o, ta_o = oracle.quantize_block16(A16)
+        qw_o, bw_o, tw_o = oracle.quantize_block16(W16)
+        assert np.array_equal(qa.cpu().numpy(), qa_o) and np.array_equal(ba.cpu().numpy(), ba_o)
+        assert np.array_equal(qw.cpu().numpy(), qw_o) and np.array_equal(bw.cpu().numpy(), bw_o)
+        assert ta.cpu().numpy()[0] == ta_o and tw.cpu().numpy()[0] == tw_o
+        out = spg.gemm_scaled(qa, ba, qw, bw, epi, residual=res, fmt="nvfp4", tscale_a=ta, tscale_w=tw)
+        D, Da = oracle.gemm_nvfp4_sums(qa_o, ba_o, qw_o, bw_o)
+        y, S, _ = oracle.epilogue(epi, D, Da, ta_o, tw_o, R16)
+    got = host(out)
+    assert got.shape == (M, n_out)
+    ok, excess = oracle.within_tolerance(got, y, S)
+    bad = np.argwhere(~ok)
+    assert ok.all(), f"{len(bad)} of {ok.size} outside the bound; worst excess {excess.max():.3g} at {bad[:5].tolist()}"
