@@ -17,7 +17,7 @@ from synthetic import bf16_normal
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=36, seed=20261203):
+def _cases(n=72, seed=20261203):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
