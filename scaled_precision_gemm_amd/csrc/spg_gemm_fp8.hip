@@ -30,12 +30,14 @@
 //  * SWIGLU pairs weight rows inside one 256-row W tile (128 gate + 128 up).
 //  * XCD-aware tile order; a persistent grid (one workgroup per compute
 //    unit) whose copy pipeline runs on into the next tile; optional split-K
-//    through the workspace; a half-height kernel for a short last round.
+//    through the workspace; a half-height kernel (128-row tiles) for a short
+//    last round and for whole products where the route model prices 128-row
+//    tiles below 256-row ones.
 //  * Epilogue from the accumulators, transposed through a per-wave LDS region
 //    so the output leaves in whole 128-byte row segments (W fragments are the
 //    first MFMA operand, so a lane holds four adjacent output columns).
-//  * Products of at most 32 tokens use an instantiation that leaves out the
-//    MFMAs of the empty A blocks.
+//  * Few-token products split along K (at most 64 tokens) use instantiations
+//    that leave out the MFMAs of the empty A blocks.
 #include "spg_gemm_common.h"
 
 #include <type_traits>
