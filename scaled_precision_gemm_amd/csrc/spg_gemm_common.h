@@ -102,22 +102,25 @@ __device__ __forceinline__ int lane_id()
     return r;
 }
 
-// silu(g) * u = g u / (1 + exp(-g)) with the hardware reciprocal (about 1
-// ulp; the SwiGLU output tolerance is 2^-8 relative), the denominator
-// carried as (1 + exp(-g)) 2^-64 and the 2^-64 given back last.  Unscaled,
-// from g = -87.3 the reciprocal of the denominator is subnormal (the
-// hardware reciprocal flushes it to zero) and from g = -88.7 exp(-g)
-// overflows, while silu(g) u can still be a normal bf16 value (g = -88,
-// u = -46: 1.8e-35).  Scaled, the reciprocal stays normal down to g = -131
-// and exp(-g) 2^-64 is finite down to g = -133; below that
-// |silu(g) u| < |g u| 2^-190, which rounds to zero in bf16 for any |g u|
-// under 2^57.  Against the unscaled form this costs one multiply; the offset
-// in the exponent argument costs 2^-18 of absolute precision in it (a
-// relative 2^-18 in exp, far below bf16's 2^-9).
+// silu(g) * u = g / (1 + exp(-g)) * u with the hardware exp2 and reciprocal
+// (about 1 ulp each; the SwiGLU output tolerance is 2^-8 relative), the
+// denominator carried as d = (1 + exp(-g)) 2^-64 and the 2^-64 given back
+// as 2^-32 on each factor: y = (g / d 2^-32) (u 2^-32).  Unscaled, from
+// g = -87.3 the reciprocal of the denominator is subnormal (the hardware
+// reciprocal flushes it to zero) and from g = -88.7 exp(-g) overflows, so
+// silu(g) u came out 0 where it can still be a normal bf16 value (g = -88,
+// u = -46: 1.8e-35).  Scaled, 1 / d stays normal down to g = -131 (exp(-g)
+// 2^-64 is finite down to -133); g / d 2^-32 = silu(g) 2^32 is normal down
+// to g = -113 and finite for |g| < 2^96, and u 2^-32 is normal for
+// |u| > 2^-94, so the product is right wherever it is a normal number, up
+// to fp32's largest (below g = -113 silu(g) u is under 2^-126 for any
+// |u| < 2^36).  Against the unscaled form this costs two multiplies; the
+// offset in the exponent argument costs 2^-18 of absolute precision in it
+// (a relative 2^-18 in exp).
 __device__ __forceinline__ float swiglu_f32(float g, float u)
 {
     const float d = __builtin_amdgcn_exp2f(__builtin_fmaf(g, -1.44269504f, -64.0f)) + 0x1p-64f;
-    return (g * u) * __builtin_amdgcn_rcpf(d) * 0x1p-64f;
+    return (g * __builtin_amdgcn_rcpf(d) * 0x1p-32f) * (u * 0x1p-32f);
 }
 
 struct Tile {

@@ -100,3 +100,38 @@ def test_random_shape_matches_the_oracle(spg, fmt, epi, M, N, K):
     ok, excess = oracle.within_tolerance(got, y, S)
     bad = np.argwhere(~ok)
     assert ok.all(), f"{len(bad)} of {ok.size} outside the bound; worst excess {excess.max():.3g} at {bad[:5].tolist()}"
+
+
+# Rows of A and W scaled by random powers of ten (A: 1e-30 .. 1e30, W:
+# 1e-20 .. 1e20; SwiGLU, whose epilogue forms gate x up in fp32 first:
+# 1e-10 .. 1e10 and 1e-5 .. 1e5), so the row scales, their products and the
+# outputs span most of the fp32 and bf16 range, subnormal-scale rows included.
+WIDE = [(int(m), int(n) * 2, int(k) * 16, epi) for m, n, k, epi in
+        zip(np.random.default_rng(77).integers(1, 400, 12), np.random.default_rng(78).integers(1, 300, 12),
+            np.random.default_rng(79).integers(1, 80, 12), ["store", "add", "swiglu"] * 4)]
+
+
+@pytest.mark.parametrize("M,N,K,epi", WIDE, ids=lambda v: str(v))
+def test_row_scales_across_the_range_match_the_oracle(spg, M, N, K, epi):
+    rng = np.random.default_rng(M * N + K)
+    from synthetic import f32_to_bf16_bits
+    ea, ew = (10, 5) if epi == "swiglu" else (30, 20)
+    fa = oracle.bf16_to_f64(bf16_normal((M, K), 1.0, M + 5)) * 10.0 ** rng.uniform(-ea, ea, (M, 1))
+    fw = oracle.bf16_to_f64(bf16_normal((N, K), 1.0, N + 6)) * 10.0 ** rng.uniform(-ew, ew, (N, 1))
+    A16 = f32_to_bf16_bits(fa.astype(np.float32))
+    W16 = f32_to_bf16_bits(fw.astype(np.float32))
+    n_out = N // 2 if epi == "swiglu" else N
+    R16 = bf16_normal((M, n_out), 1.0, M + N) if epi == "add" else None
+    qa, sa = spg.quantize_rowwise(dev(A16))
+    qw, sw = spg.quantize_rowwise(dev(W16))
+    qa_o, sa_o = oracle.quantize_rowwise(A16)
+    qw_o, sw_o = oracle.quantize_rowwise(W16)
+    assert np.array_equal(qa.cpu().numpy(), qa_o) and np.array_equal(sa.cpu().numpy(), sa_o)
+    assert np.array_equal(qw.cpu().numpy(), qw_o) and np.array_equal(sw.cpu().numpy(), sw_o)
+    got = host(spg.gemm_scaled(qa, sa, qw, sw, epi, residual=dev(R16) if R16 is not None else None))
+    D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
+    y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, R16)
+    fin = np.isfinite(y) & (np.abs(y) < 3.0e38)      # outputs beyond bf16's range are not compared
+    ok, excess = oracle.within_tolerance(got, y, S)
+    bad = np.argwhere(fin & ~ok)
+    assert len(bad) == 0, f"{len(bad)} outside the bound; worst excess {excess[fin].max():.3g} at {bad[:5].tolist()}"
