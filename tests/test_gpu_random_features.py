@@ -1,5 +1,6 @@
 """Seeded random shapes with the optional features of gemm_scaled: bf16 and
-E4M3 bias rows, outputs split into column segments, K-major operands, padded
+E4M3 bias rows, outputs split into column segments (with a residual matrix
+or a bias row), K-major operands, padded
 leading dimensions, per-tensor batches (own or broadcast weights) and the
 blocked NVFP4 scale planes.  Each case draws its shape and feature from a
 fixed seed, runs quantize + GEMM on the device, and compares the whole output
@@ -14,7 +15,7 @@ from synthetic import bf16_normal
 
 pytestmark = pytest.mark.gpu
 
-FEATURES = ["bias_bf16", "bias_e4m3", "split", "kmajor", "padded", "batch", "nvfp4_blocked"]
+FEATURES = ["bias_bf16", "bias_e4m3", "split", "kmajor", "padded", "batch", "nvfp4_blocked", "split_bias"]
 
 
 def _cases(per_feature=10, seed=4242):
@@ -28,11 +29,11 @@ def _cases(per_feature=10, seed=4242):
             else:
                 fmt = str(rng.choice(["e4m3_row", "e4m3_tensor"])) if feat != "batch" else "e4m3_tensor"
                 K = int(rng.integers(1, 100)) * 16
-            if feat in ("bias_bf16", "bias_e4m3"):
+            if feat in ("bias_bf16", "bias_e4m3", "split_bias"):
                 epi = "add"
             else:
-                epi = str(rng.choice(["store", "add", "swiglu"])) if feat != "split" else str(rng.choice(["store", "swiglu"]))
-            if feat == "split":
+                epi = str(rng.choice(["store", "add", "swiglu"]))
+            if feat in ("split", "split_bias"):
                 n_out = int(rng.integers(2, 12)) * 64 + int(rng.integers(0, 64))
                 N = 2 * n_out if epi == "swiglu" else n_out
             else:
@@ -79,9 +80,9 @@ def test_random_feature_matches_the_oracle(spg, feat, fmt, epi, M, N, K, seed):
     R16 = bias16 = None
     bias_vals = None
     kw = {}
-    if epi == "add" and feat not in ("bias_bf16", "bias_e4m3"):
+    if epi == "add" and feat not in ("bias_bf16", "bias_e4m3", "split_bias"):
         R16 = bf16_normal((M, n_out), 1.0, seed % 1000 + 2)
-    if feat == "bias_bf16":
+    if feat in ("bias_bf16", "split_bias"):
         bias16 = bf16_normal((n_out,), 1.0, seed % 1000 + 3)
         kw["residual"] = dev(bias16)
         bias_vals = oracle.bf16_to_f64(bias16)
@@ -132,12 +133,12 @@ def test_random_feature_matches_the_oracle(spg, feat, fmt, epi, M, N, K, seed):
         ldo = (n_out + 7) // 8 * 8 + 8 * int(rng.integers(1, 4))
         out = torch.zeros((M, ldo), dtype=torch.bfloat16, device="cuda")[:, :n_out]
         kw["out"] = out
-    if feat == "split":
+    if feat in ("split", "split_bias"):
         cuts = sorted(set(int(c) * 64 for c in rng.integers(1, n_out // 64 + 1, size=2) if int(c) * 64 < n_out))
         widths = [b - a for a, b in zip([0] + cuts, cuts + [n_out])]
         kw["out_split"] = widths
     res = spg.gemm_scaled(qa, sa, qw, sw, epi, fmt=fmt, **kw)
-    if feat == "split":
+    if feat in ("split", "split_bias"):
         assert [t.shape[-1] for t in res] == widths
         got = np.concatenate([host(t) for t in res], axis=-1)
     else:
