@@ -7,7 +7,8 @@ decode-width kernel, per-tensor scales with their partial-maximum pass, and
 NVFP4 with its two-pass quantizer).  Each replay runs on new input written
 into the captured buffer, with eager work and synchronizations in between,
 and must equal the eager result for that input bit for bit (the kernels are
-deterministic).
+deterministic).  Products launched on two streams at once must also equal the
+same products run one after another.
 """
 import numpy as np
 import pytest
@@ -97,3 +98,41 @@ def test_captured_step_replays_like_eager(spg, fmt, epi, M, N, K, B, kernel):
         got = host(out_g)
         assert np.array_equal(got, want), f"replay {r}: {np.count_nonzero(got != want)} elements differ"
         torch.cuda.synchronize()
+
+
+def test_two_streams_at_once_match_one_stream(spg):
+    # the library keeps no state between calls (each call's workspace is its
+    # own): products launched on two streams at once give the results they
+    # give one after another on one stream, bit for bit
+    shapes = [("e4m3_row", "add", 128, 5120, 4096), ("e4m3_row", "swiglu", 300, 2048, 1536),
+              ("nvfp4", "store", 256, 1024, 1024), ("e4m3_row", "store", 16, 4096, 2048)]
+    inputs = []
+    for i, (fmt, epi, M, N, K) in enumerate(shapes):
+        A = dev(bf16_normal((M, K), 1.0, 900 + i))
+        W = dev(bf16_normal((N, K), 0.02, 910 + i))
+        n_out = N // 2 if epi == "swiglu" else N
+        R = dev(bf16_normal((M, n_out), 1.0, 920 + i)) if epi == "add" else None
+        inputs.append((fmt, epi, A, W, R))
+
+    def run(fmt, epi, A, W, R):
+        if fmt == "nvfp4":
+            qa, sa, ta = spg.quantize_block16(A)
+            qw, sw, tw = spg.quantize_block16(W)
+            return spg.gemm_scaled(qa, sa, qw, sw, epi, residual=R, fmt="nvfp4", tscale_a=ta, tscale_w=tw)
+        qa, sa = spg.quantize_rowwise(A)
+        qw, sw = spg.quantize_rowwise(W)
+        return spg.gemm_scaled(qa, sa, qw, sw, epi, residual=R)
+
+    want = [host(run(*x)) for x in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    got = [None] * len(inputs)
+    for rep in range(3):
+        for i, x in enumerate(inputs):
+            with torch.cuda.stream(streams[i % 2]):
+                got[i] = run(*x)
+        torch.cuda.synchronize()
+        for i in range(len(inputs)):
+            assert np.array_equal(host(got[i]), want[i]), f"round {rep}, product {i}"
