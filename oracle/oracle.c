@@ -355,6 +355,18 @@ static double silu_prime(double z)
     return sg * (1.0 + z * (1.0 - sg));
 }
 
+/* silu'' vanishes only at +-T0, the root of t tanh(t/2) = 2, so silu' is
+ * monotone on (-inf, -T0], [-T0, T0] and [T0, inf): its largest magnitude on
+ * [lo, hi] is taken at an end or at +-T0 when they lie inside. */
+#define SILU_T0 2.3993572805154675
+static double silu_slope_max(double lo, double hi)
+{
+    double m = fmax(fabs(silu_prime(lo)), fabs(silu_prime(hi)));
+    if (lo <= SILU_T0 && SILU_T0 <= hi) m = fmax(m, fabs(silu_prime(SILU_T0)));
+    if (lo <= -SILU_T0 && -SILU_T0 <= hi) m = fmax(m, fabs(silu_prime(-SILU_T0)));
+    return m;
+}
+
 /* Scale the exact sums and apply the epilogue, all in fp64.
  * D, Dabs: [M, Nw] (row stride Nw); ascale[M], wscale[Nw] are the fp32 scales
  * as doubles (per-tensor and NVFP4 tensor scales are passed replicated).
@@ -367,7 +379,12 @@ static double silu_prime(double z)
  * commit fusing the bias into the GEMM epilogue).
  * y, tol_S: [M, Nout]; out: bf16 bits of y, rounded once from fp64.
  * tol_S is the error scale S of the acceptance bound |gpu - y| <=
- * 2^-8 |y| + 2^-12 S: S = |sa sw| Dabs, first-order propagated for SWIGLU. */
+ * 2^-8 |y| + 2^-12 S: S = |sa sw| Dabs for STORE and ADD.  For SWIGLU the
+ * gate g and up u may each be off by 2^-12 of their own scales Sg, Su; then
+ * |silu(g') u' - silu(g) u| <= L Sg' (|u| + 2^-12 Su) + |silu(g)| Su' with
+ * Sg' = 2^-12 Sg, Su' = 2^-12 Su and L the largest |silu'| within Sg' of g,
+ * so S = L Sg (|u| + 2^-12 Su) + |silu(g)| Su.  Where the gate sum cancels
+ * (|g| far below Sg) the slope at g alone would understate the error. */
 EXPORT void spo_epilogue(int epi, const double *D, const double *Dabs, int64_t M, int64_t Nw,
                          const double *ascale, const double *wscale,
                          const uint16_t *residual, int64_t ldr, const double *bias,
@@ -385,7 +402,8 @@ EXPORT void spo_epilogue(int epi, const double *D, const double *Dabs, int64_t M
                 double Sg = fabs(ascale[i] * wscale[j]) * Dabs[i * Nw + j];
                 double Su = fabs(ascale[i] * wscale[ju]) * Dabs[i * Nw + ju];
                 yv = silu(vg) * vu;
-                S = fabs(silu_prime(vg) * vu) * Sg + fabs(silu(vg)) * Su;
+                double dg = 0x1p-12 * Sg;
+                S = silu_slope_max(vg - dg, vg + dg) * Sg * (fabs(vu) + 0x1p-12 * Su) + fabs(silu(vg)) * Su;
             } else {
                 double v = ascale[i] * wscale[j] * D[i * Nw + j];
                 S = fabs(ascale[i] * wscale[j]) * Dabs[i * Nw + j];

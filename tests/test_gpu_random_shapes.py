@@ -131,7 +131,10 @@ def test_row_scales_across_the_range_match_the_oracle(spg, M, N, K, epi):
     got = host(spg.gemm_scaled(qa, sa, qw, sw, epi, residual=dev(R16) if R16 is not None else None))
     D, Da = oracle.gemm_e4m3_sums(qa_o, qw_o)
     y, S, _ = oracle.epilogue(epi, D, Da, sa_o, sw_o, R16)
-    fin = np.isfinite(y) & (np.abs(y) < 3.0e38)      # outputs beyond bf16's range are not compared
+    # elements whose acceptance interval reaches beyond bf16's finite range
+    # are not compared (there a sum that cancels to zero exactly may come out
+    # as a small fp32 residue times a scale product beyond fp32's range)
+    fin = np.isfinite(y) & (np.abs(y) + 2.0 ** -12 * S < 3.0e38)
     ok, excess = oracle.within_tolerance(got, y, S)
     bad = np.argwhere(fin & ~ok)
     assert len(bad) == 0, f"{len(bad)} outside the bound; worst excess {excess[fin].max():.3g} at {bad[:5].tolist()}"

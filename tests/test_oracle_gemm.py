@@ -199,11 +199,14 @@ def test_swiglu_special_values():
     assert y[0, 0] == 0.0                                   # silu(0) = 0
     assert y[0, 1] == pytest.approx(50.0 * 2.0, rel=1e-20)  # silu(z) ~ z for large z
     assert abs(y[0, 2]) < 1e-19                             # silu(-50) ~ 0
-    # first-order error scale |silu'(g) u| Sg + |silu(g)| Su; silu'(0) = 1/2
-    assert S[0, 0] == pytest.approx(0.5 * 3.0 * 4.0 + 0.0 * 3.0, rel=1e-15)
+    # error scale L Sg (|u| + 2^-12 Su) + |silu(g)| Su, L the largest |silu'|
+    # within 2^-12 Sg of g: silu' rises through 1/2 at 0 and falls towards 1
+    # above 2.4, so L is taken at the interval's upper end, then its lower end
+    dsilu = lambda z: expit(z) * (1 + z * (1 - expit(z)))
+    assert S[0, 0] == pytest.approx(dsilu(4.0 / 4096) * 4.0 * (3.0 + 3.0 / 4096), rel=1e-15)
     z = 50.0
-    dsilu = expit(z) * (1 + z * (1 - expit(z)))
-    assert S[0, 1] == pytest.approx(dsilu * 2.0 * 50.0 + z * expit(z) * 2.0, rel=1e-15)
+    assert S[0, 1] == pytest.approx(dsilu(z - 50.0 / 4096) * 50.0 * (2.0 + 2.0 / 4096) + z * expit(z) * 2.0,
+                                    rel=1e-15)
 
 
 def test_tensor_scale_epilogue_store():
