@@ -223,15 +223,18 @@ __device__ __forceinline__ int wtile_row0(int wn, int x)
 // row (sw); the epilogue forms acc * sa * sw.  Thread i supplies row i:
 //   E4M3 per row:    sa = s_a[row], sw = s_w[W row]
 //   E4M3 per tensor: sa = s_a, sw = s_w (of the batch entry)
-//   NVFP4:           sa = 2^14 * tA * tW (2^14 undoes the two 2^-7
-//                    operand offsets of the kernel's f16 decode), sw = 1
+//   NVFP4:           sa = 2^7 * tA, sw = 2^7 * tW (the two 2^7 undo the
+//                    operand offsets of the kernel's f16 decode).  The
+//                    tensor scales stay separate factors: each is at most
+//                    bf16's maximum / 2688, so 2^7 t < 1.6e37, while their
+//                    product can pass fp32's range for outputs that do not
 template <int EPI, int SMODE>
 __device__ __forceinline__ void scale_values(const GemmArgs &g, const Tile &T, float &va, float &vw)
 {
     const int tid = threadIdx.x;
     if (SMODE == SPG_FMT_NVFP4) {
-        va = 16384.0f * *g.tscale_a * *g.tscale_w;
-        vw = 1.0f;
+        va = 128.0f * *g.tscale_a;
+        vw = 128.0f * *g.tscale_w;
     } else if (SMODE == SPG_FMT_E4M3_ROW) {
         bool wok;
         const int64_t wr = w_row<EPI>(g, T, tid, wok);

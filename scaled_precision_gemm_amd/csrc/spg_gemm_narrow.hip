@@ -364,11 +364,16 @@ __global__ __launch_bounds__(kNarrowThreads) void gemm_narrow_kernel(const GemmA
     if (m < g.M && col < nout) {
         float sa, sw[NH][4];
         if (FP4) {
-            sa = 16384.0f * *g.tscale_a * *g.tscale_w;   // 2^14 undoes the two 2^-7 of the decode
+            // 2^7 per side undoes the decode's 2^-7 offsets; the two tensor
+            // scales stay separate factors (each at most 2^7 * 448^-1 * 6^-1
+            // * bf16's maximum, below 1.6e37), so their product - which can
+            // pass fp32's range when the output does not - is never formed
+            sa = 128.0f * *g.tscale_a;
+            const float sv = 128.0f * *g.tscale_w;
 #pragma unroll
             for (int h = 0; h < NH; ++h)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sw[h][e] = 1.0f;
+                for (int e = 0; e < 4; ++e) sw[h][e] = sv;
         } else if (g.format == SPG_FMT_E4M3_ROW) {
             const float *psa = (const float *)g.sa + (g.stride_a ? b * g.M : 0);
             const float *psw = (const float *)g.sw + (g.stride_w ? b * g.N : 0);

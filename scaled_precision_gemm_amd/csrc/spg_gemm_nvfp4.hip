@@ -12,9 +12,10 @@
 // is decoded once per workgroup tile, on its way into LDS, to the exact f16
 // value  e2m1(code) * S * 2^-7  (6 significant bits, range 2^-17 .. 21),
 // and the tile is multiplied with v_mfma_f32_32x32x16_f16 (fp32
-// accumulation).  The 2^14 of the two operand offsets and the tensor scales
-// are applied in the epilogue.  The dense f16 MFMA rate is half the FP8 rate,
-// so this path is priced against the f16/bf16 roofline.
+// accumulation).  The epilogue undoes each operand's 2^-7 offset together
+// with its tensor scale, as two factors (2^7 tA, 2^7 tW).  The dense f16
+// MFMA rate is half the FP8 rate, so this path is priced against the
+// f16/bf16 roofline.
 //
 // Decode without tables: an E2M1 code c placed as f16 bits
 // ((c & 7) << 9) | ((c & 8) << 12) is exactly e2m1(c) * 2^-14 (normal codes

@@ -144,3 +144,35 @@ def test_row_scales_across_the_range_match_the_oracle(spg, M, N, K, epi):
     ok, excess = oracle.within_tolerance(got, y, S)
     bad = np.argwhere(fin & ~ok)
     assert len(bad) == 0, f"{len(bad)} outside the bound; worst excess {excess[fin].max():.3g} at {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("epi", ["store", "add"])
+def test_nvfp4_tensor_scales_whose_product_passes_fp32_range(spg, epi):
+    # A holds one element of 4e28 (column 0) and W one of 4e12 (column 16,
+    # another K block), the rest ~1e25 and ~1e9: 2^14 tA tW is beyond fp32's
+    # range while every output (~1e38) is finite in bf16, so the tensor
+    # scales must not be folded into one fp32 factor
+    M, N, K = 8, 90, 704
+    fa = oracle.bf16_to_f64(bf16_normal((M, K), 1.0, 31)) * 1e25
+    fw = oracle.bf16_to_f64(bf16_normal((N, K), 1.0, 32)) * 1e9
+    fa[:, 0] = 4e28
+    fw[:, 16] = 4e12
+    from synthetic import f32_to_bf16_bits
+    A16 = f32_to_bf16_bits(fa.astype(np.float32))
+    W16 = f32_to_bf16_bits(fw.astype(np.float32))
+    R16 = bf16_normal((M, N), 1.0, 33) if epi == "add" else None
+    qa, ba, ta = spg.quantize_block16(dev(A16))
+    qw, bw, tw = spg.quantize_block16(dev(W16))
+    qa_o, ba_o, ta_o = oracle.quantize_block16(A16)
+    qw_o, bw_o, tw_o = oracle.quantize_block16(W16)
+    assert np.array_equal(qa.cpu().numpy(), qa_o) and np.array_equal(qw.cpu().numpy(), qw_o)
+    assert ta.cpu().numpy()[0] == ta_o and tw.cpu().numpy()[0] == tw_o
+    assert 16384.0 * float(ta_o) * float(tw_o) > 3.5e38      # the folded factor would be inf in fp32
+    got = host(spg.gemm_scaled(qa, ba, qw, bw, epi, residual=dev(R16) if R16 is not None else None, fmt="nvfp4",
+                               tscale_a=ta, tscale_w=tw))
+    D, Da = oracle.gemm_nvfp4_sums(qa_o, ba_o, qw_o, bw_o)
+    y, S, _ = oracle.epilogue(epi, D, Da, ta_o, tw_o, R16)
+    assert np.all(np.abs(y) + 2.0 ** -12 * S < 3.0e38) and np.abs(y).max() > 1e37
+    ok, excess = oracle.within_tolerance(got, y, S)
+    bad = np.argwhere(~ok)
+    assert ok.all(), f"{len(bad)} outside the bound; worst excess {excess.max():.3g} at {bad[:5].tolist()}"
