@@ -115,6 +115,8 @@ WIDE = [(int(m), int(n) * 2, int(k) * 16, epi) for m, n, k, epi in
 # and a sum that cancels to exactly zero under a row-scale product beyond
 # fp32's range.
 WIDE += [(99, 770, 1408, "swiglu"), (489, 326, 1568, "swiglu"), (329, 208, 1600, "swiglu"), (671, 406, 96, "store")]
+# and shapes the planner splits along K (the reduction applies the epilogue)
+WIDE += [(48, 1024, 4096, "add"), (200, 600, 3072, "swiglu"), (40, 900, 6144, "store")]
 
 
 @pytest.mark.parametrize("M,N,K,epi", WIDE, ids=lambda v: str(v))
