@@ -111,10 +111,11 @@ __device__ __forceinline__ int lane_id()
 // silu(g) u came out 0 where it can still be a normal bf16 value (g = -88,
 // u = -46: 1.8e-35).  Scaled, 1 / d stays normal down to g = -131 (exp(-g)
 // 2^-64 is finite down to -133); g / d 2^-32 = silu(g) 2^32 is normal down
-// to g = -113 and finite for |g| < 2^96, and u 2^-32 is normal for
-// |u| > 2^-94, so the product is right wherever it is a normal number, up
-// to fp32's largest (below g = -113 silu(g) u is under 2^-126 for any
-// |u| < 2^36).  Against the unscaled form this costs two multiplies; the
+// to g = -113, and u 2^-32 is normal for |u| > 2^-94, so the product is
+// right wherever it is a normal number, up to fp32's largest (below
+// g = -113 silu(g) u is under 2^-126 for any |u| < 2^36), for gates below
+// 2^64: g / d, formed first, is g 2^64 for large g and passes fp32's range
+// there.  Against the unscaled form this costs two multiplies; the
 // offset in the exponent argument costs 2^-18 of absolute precision in it
 // (a relative 2^-18 in exp).
 __device__ __forceinline__ float swiglu_f32(float g, float u)
