@@ -97,9 +97,9 @@ def gemm_bytes(wl) -> int:
 
 def quantize_bytes(wl) -> int:
     """Algorithmic bytes of the step's activation quantization: bf16 in, codes
-    and scales out (read once: per-tensor FP8 reads the activations twice, a
-    partial-maximum pass and then the encode pass, but the minimum is one
-    read, and NVFP4 runs as a single launch at this size)."""
+    and scales out (read once: per-tensor FP8 and NVFP4 read the activations
+    twice, a partial-maximum pass and then the encode pass, but the minimum
+    is one read)."""
     elems = wl.batch * wl.M * wl.K
     if wl.fmt == "e4m3_row":
         return 3 * elems + 4 * wl.batch * wl.M
